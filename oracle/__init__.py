@@ -1,0 +1,369 @@
+"""CPU oracle for the quantized-decode hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; never by the product package
+``kv_quantization_amd``.  It shares no code with the HIP library.
+
+The quantizers are encodings, so they live in plain C (``oracle.c``, fp32
+operations one at a time, ``-ffp-contract=off``) and must agree bit for bit.
+The two matrix products are plain definitions, written here as fp64 sums with
+``numpy.matmul`` as the summation primitive:
+
+* W8A8 (metrale_model_layers ``w8a8_decode.rs``, ``w8a8_gemv`` over the
+  ``W8a8Weight`` segments): ``out[m, j] = sum_k (dec(qa[m,k]) * sa) *
+  (dec(qw[j,k]) * sw)`` where the scales are per row, or per 128x128 weight
+  block and per 128-column activation group.
+* INT4 AWQ (boostr ``fused_int4_qkv.rs``, ``fused_int4_qkv_q/k/v``):
+  ``out[m, j] = sum_k x[m,k] * (q[k,j] - z[k/gs, j]) * s[k/gs, j]`` with q
+  unpacked in the ``QKV_AWQ_SHIFTS`` nibble order.
+
+Every function returns, next to the reference value, the bound
+``sum_k |a_k| |w_k|`` of the operands actually multiplied, which the parity
+tests scale by the 1e-3 relative tolerance.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_DIR = Path(__file__).resolve().parent
+_SRC = _DIR / "oracle.c"
+_LIB = _DIR / "liboracle.so"
+
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
+
+
+def build(force: bool = False) -> Path:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no SIMD intrinsics)."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(f".so.tmp{os.getpid()}")
+        subprocess.run(["gcc", *CFLAGS, str(_SRC), "-o", str(tmp), "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(str(build()))
+        i64 = ctypes.c_int64
+        p = ctypes.c_void_p
+        sig = {
+            "oracle_num_threads": ([], ctypes.c_int),
+            "oracle_kv_int8_quant": ([p, p, p, i64, i64], None),
+            "oracle_kv_int8_dequant": ([p, p, p, i64, i64], None),
+            "oracle_kv_fp8_quant": ([p, p, p, i64, i64], None),
+            "oracle_kv_fp8_dequant": ([p, p, p, i64, i64], None),
+            "oracle_kv_int4_quant": ([p, p, p, p, i64, i64, i64], None),
+            "oracle_kv_int4_dequant": ([p, p, p, p, i64, i64, i64], None),
+            "oracle_bf16_to_f32": ([ctypes.c_uint16], ctypes.c_float),
+            "oracle_f32_to_bf16": ([ctypes.c_float], ctypes.c_uint16),
+            "oracle_e4m3_decode": ([ctypes.c_uint8], ctypes.c_float),
+            "oracle_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
+            "oracle_exp": ([ctypes.c_float], ctypes.c_float),
+            "oracle_silu": ([ctypes.c_float], ctypes.c_float),
+            "oracle_act_quant": ([ctypes.c_int, ctypes.c_int, p, p, i64, i64, i64, p, p], None),
+            "oracle_weight_quant": ([ctypes.c_int, p, i64, i64, p, p], None),
+            "oracle_awq_unpack": ([p, p, i64, i64], None),
+            "oracle_awq_pack": ([p, p, i64, i64], None),
+            "oracle_awq_dequant_f64": ([p, p, p, p, i64, i64, i64], None),
+            "oracle_e4m3_dequant_f64": ([ctypes.c_int, p, p, p, i64, i64], None),
+            "oracle_e4m3_encode_array": ([p, p, i64], None),
+            "oracle_f32_to_bf16_array": ([p, p, i64], None),
+            "oracle_exp_array": ([p, p, i64], None),
+            "oracle_silu_array": ([p, p, i64], None),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(_lib, name)
+            fn.argtypes = args
+            fn.restype = res
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_num_threads())
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _p(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _finite(x: np.ndarray) -> None:
+    if not np.all(np.isfinite(x)):
+        raise ValueError("oracle inputs must be finite (NaN/Inf are outside the method's contract)")
+
+
+# --------------------------------------------------------------------------
+# KV cache codecs (boostr kv_cache_quant.wgsl)
+
+def kv_int8_quant(x: np.ndarray):
+    """Per-token symmetric INT8 (section "INT8 Per-Token Quantization").
+
+    x: float32 [T, D] -> (codes int8 [T, D], scales float32 [T])."""
+    x = _c(x, np.float32)
+    _finite(x)
+    t, d = x.shape
+    codes = np.empty((t, d), np.int8)
+    scales = np.empty(t, np.float32)
+    lib().oracle_kv_int8_quant(_p(x), _p(codes), _p(scales), t, d)
+    return codes, scales
+
+
+def kv_int8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Section "INT8 Per-Token Dequantization": float(code) * scale."""
+    codes = _c(codes, np.int8)
+    scales = _c(scales, np.float32)
+    t, d = codes.shape
+    y = np.empty((t, d), np.float32)
+    lib().oracle_kv_int8_dequant(_p(codes), _p(scales), _p(y), t, d)
+    return y
+
+
+def kv_fp8_quant(x: np.ndarray):
+    """Section "FP8 Per-Token Quantization" (an integer /127 code, same bytes as INT8)."""
+    x = _c(x, np.float32)
+    _finite(x)
+    t, d = x.shape
+    codes = np.empty((t, d), np.int8)
+    scales = np.empty(t, np.float32)
+    lib().oracle_kv_fp8_quant(_p(x), _p(codes), _p(scales), t, d)
+    return codes, scales
+
+
+def kv_fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = _c(codes, np.int8)
+    scales = _c(scales, np.float32)
+    t, d = codes.shape
+    y = np.empty((t, d), np.float32)
+    lib().oracle_kv_fp8_dequant(_p(codes), _p(scales), _p(y), t, d)
+    return y
+
+
+def kv_int4_quant(x: np.ndarray, group_size: int):
+    """Per-group asymmetric INT4 (section "INT4 Per-Group Quantization").
+
+    x: float32 [T, D]; groups of ``group_size`` over the flattened array.
+    -> (packed uint8 [T*D/2], scales float32 [G], zeros float32 [G])."""
+    x = _c(x, np.float32)
+    _finite(x)
+    t, d = x.shape
+    if group_size < 2 or group_size % 2 or (t * d) % group_size:
+        raise ValueError("group_size must be even and divide num_tokens*head_dim")
+    g = t * d // group_size
+    packed = np.empty(t * d // 2, np.uint8)
+    scales = np.empty(g, np.float32)
+    zeros = np.empty(g, np.float32)
+    lib().oracle_kv_int4_quant(_p(x), _p(packed), _p(scales), _p(zeros), t, d, group_size)
+    return packed, scales, zeros
+
+
+def kv_int4_dequant(packed, scales, zeros, num_tokens: int, head_dim: int, group_size: int):
+    """Section "INT4 Per-Group Dequantization": code*scale - zero*scale."""
+    packed = _c(packed, np.uint8)
+    scales = _c(scales, np.float32)
+    zeros = _c(zeros, np.float32)
+    y = np.empty((num_tokens, head_dim), np.float32)
+    lib().oracle_kv_int4_dequant(_p(packed), _p(scales), _p(zeros), _p(y), num_tokens, head_dim, group_size)
+    return y
+
+
+# --------------------------------------------------------------------------
+# Number formats
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits (uint16), round to nearest even; element by element in C."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_f32_to_bf16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    """bf16 bits -> fp32 (exact: the bits become the top half)."""
+    return (_c(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """fp32 -> E4M3FN codes (RNE, saturating, sign kept), element by element in C."""
+    x = _c(np.atleast_1d(x), np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().oracle_e4m3_encode_array(_p(x), _p(out), x.size)
+    return out
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """float32 [256]: the value of every E4M3FN code (NaN for 0x7F/0xFF)."""
+    f = lib().oracle_e4m3_decode
+    return np.array([f(c) for c in range(256)], np.float32)
+
+
+def exp_k(y) -> np.ndarray:
+    """The pinned SiLU exponential (Cody-Waite + degree-7 Taylor), fp32."""
+    y = _c(np.atleast_1d(y), np.float32)
+    out = np.empty(y.shape, np.float32)
+    lib().oracle_exp_array(_p(y), _p(out), y.size)
+    return out
+
+
+def silu(v) -> np.ndarray:
+    """v / (1 + exp_k(-v)) in fp32."""
+    v = _c(np.atleast_1d(v), np.float32)
+    out = np.empty(v.shape, np.float32)
+    lib().oracle_silu_array(_p(v), _p(out), v.size)
+    return out
+
+
+# --------------------------------------------------------------------------
+# W8A8 FP8 decode (metrale_model_layers w8a8_decode.rs)
+
+ROWSCALE = 0  # W8a8Scale::PerRow
+BLK128 = 1    # W8a8Scale::Block128
+
+
+def act_quant(kind: int, x_bf16: np.ndarray, k: int, silu: bool = False, up_bf16=None):
+    """Activation quantization (w8a8_act_quant / w8a8_act_quant_silu).
+
+    x_bf16: uint16 [rows, ldx]; up_bf16 the same shape or None.
+    -> (q uint8 [rows, k], scales float32 [rows] or [rows, k/128])."""
+    x = _c(x_bf16, np.uint16)
+    rows, ldx = x.shape
+    _finite(bf16_to_f32(x[:, :k]))
+    if k % 128 or ldx < k:
+        raise ValueError("k must be a multiple of 128 and ldx >= k")
+    up = None if up_bf16 is None else _c(up_bf16, np.uint16)
+    if up is not None and (up.shape != x.shape or not silu):
+        raise ValueError("up must match x and is only used with silu")
+    q = np.empty((rows, k), np.uint8)
+    scales = np.empty((rows,) if kind == ROWSCALE else (rows, k // 128), np.float32)
+    lib().oracle_act_quant(kind, int(silu), _p(x), 0 if up is None else _p(up), ldx, rows, k, _p(q), _p(scales))
+    return q, scales
+
+
+def weight_quant(kind: int, w: np.ndarray):
+    """E4M3 weight quantization with the activation rule, per weight row
+    (ROWSCALE) or per 128x128 block (BLK128).  w: float32 [n, k]."""
+    w = _c(w, np.float32)
+    _finite(w)
+    n, k = w.shape
+    if k % 128:
+        raise ValueError("k must be a multiple of 128")
+    q = np.empty((n, k), np.uint8)
+    scales = np.empty((n,) if kind == ROWSCALE else ((n + 127) // 128, k // 128), np.float32)
+    lib().oracle_weight_quant(kind, _p(w), n, k, _p(q), _p(scales))
+    return q, scales
+
+
+def e4m3_dequant_f64(mode: int, q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """mode 0: per-row scale; 1: 128x128 weight blocks; 2: activation 128-groups."""
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.float32)
+    n, k = q.shape
+    out = np.empty((n, k), np.float64)
+    lib().oracle_e4m3_dequant_f64(mode, _p(q), _p(scales), _p(out), n, k)
+    return out
+
+
+def w8a8_gemv(kind: int, q: np.ndarray, a_scales: np.ndarray, segments):
+    """Reference for ``w8a8_gemv`` over 1..3 concatenated weight segments.
+
+    q: uint8 [M, K] activation codes; a_scales [M] or [M, K/128];
+    segments: list of (codes uint8 [n_i, K], scales [n_i] or [ceil(n_i/128), K/128]).
+    Output column j belongs to the first segment whose running row total
+    exceeds j (the W8a8Weight boundaries).
+    -> (ref float64 [M, N] unrounded, bound float64 [M, N])."""
+    a = e4m3_dequant_f64(0 if kind == ROWSCALE else 2, q, a_scales)
+    ws = [e4m3_dequant_f64(0 if kind == ROWSCALE else 1, wq, ws) for wq, ws in segments]
+    w = np.concatenate(ws, axis=0)            # [N, K]
+    ref = np.matmul(a, w.T)
+    bound = np.matmul(np.abs(a), np.abs(w).T)
+    return ref, bound
+
+
+def w8a8_gemv_sampled(kind: int, q, a_scales, segments, rows_idx, cols_idx):
+    """The same definition evaluated only at the (row, col) pairs given, one
+    dot product per pair, for full-size spot checks."""
+    rows_idx = np.asarray(rows_idx)
+    cols_idx = np.asarray(cols_idx)
+    bounds_n = np.cumsum([0] + [s[0].shape[0] for s in segments])
+    ref = np.empty(rows_idx.size, np.float64)
+    bnd = np.empty(rows_idx.size, np.float64)
+    arow_cache = {}
+    for i, (m, j) in enumerate(zip(rows_idx.tolist(), cols_idx.tolist())):
+        if m not in arow_cache:
+            arow_cache[m] = e4m3_dequant_f64(0 if kind == ROWSCALE else 2, q[m:m + 1],
+                                             a_scales[m:m + 1])[0]
+        a = arow_cache[m]
+        si = int(np.searchsorted(bounds_n, j, side="right") - 1)
+        wq, wsc = segments[si]
+        jj = j - bounds_n[si]
+        if kind == ROWSCALE:
+            w = e4m3_dequant_f64(0, wq[jj:jj + 1], wsc[jj:jj + 1])[0]
+        else:
+            # rebuild the row with its 128-block band of scales
+            band = wsc[jj // 128: jj // 128 + 1]
+            w = e4m3_dequant_f64(1, wq[jj:jj + 1], band)[0]
+        ref[i] = float(np.dot(a, w))
+        bnd[i] = float(np.dot(np.abs(a), np.abs(w)))
+    return ref, bnd
+
+
+# --------------------------------------------------------------------------
+# INT4 AWQ (boostr fused_int4_qkv.rs)
+
+AWQ_SHIFTS = (0, 16, 4, 20, 8, 24, 12, 28)
+
+
+def awq_unpack(qweight: np.ndarray, n: int) -> np.ndarray:
+    """u32 [K, n/8] -> codes uint8 [K, n] (unpack_awq_qkv for every column)."""
+    qw = _c(qweight, np.uint32)
+    k = qw.shape[0]
+    codes = np.empty((k, n), np.uint8)
+    lib().oracle_awq_unpack(_p(qw), _p(codes), k, n)
+    return codes
+
+
+def awq_pack(codes: np.ndarray) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    k, n = c.shape
+    qw = np.empty((k, n // 8), np.uint32)
+    lib().oracle_awq_pack(_p(c), _p(qw), k, n)
+    return qw
+
+
+def awq_dequant_f64(qweight, scales, zeros, group_size: int) -> np.ndarray:
+    """[K, n] fp64 weights (q - z) * s, per the fused_int4_qkv kernels."""
+    qw = _c(qweight, np.uint32)
+    s = _c(scales, np.float32)
+    z = _c(zeros, np.float32)
+    k, n8 = qw.shape
+    n = n8 * 8
+    if k % group_size:
+        raise ValueError("K must be a multiple of group_size")
+    w = np.empty((k, n), np.float64)
+    lib().oracle_awq_dequant_f64(_p(qw), _p(s), _p(z), _p(w), k, n, group_size)
+    return w
+
+
+def int4_awq_gemm(x: np.ndarray, qweight, scales, zeros, group_size: int):
+    """One projection of fused_int4_qkv: x float32 [M, K] -> (ref fp64 [M, n], bound)."""
+    x64 = _c(x, np.float32).astype(np.float64)
+    w = awq_dequant_f64(qweight, scales, zeros, group_size)
+    return np.matmul(x64, w), np.matmul(np.abs(x64), np.abs(w))
+
+
+def int4_awq_qkv(x, projections, group_size: int):
+    """Q, K, V (or a single projection): list of (ref, bound) per projection."""
+    return [int4_awq_gemm(x, qw, s, z, group_size) for (qw, s, z) in projections]
