@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-decode hot path on one MI355X.
+
+One *step* is one pass over every kernel of the path, each at its workload
+shape, on one set of synthetic inputs already resident in HBM:
+
+  KV cache 32768 x 128 fp32: INT8 per-token quant + dequant, INT4 g32 quant + dequant
+  W8A8 per-row fused QKV (K=4096, N=4096+1024+1024): act-quant + GEMV at M = 1, 8, 32
+  W8A8 128x128-block down projection (K=14336, N=4096): SiLU g128 act-quant + GEMM at M = 64, 128, 256
+  INT4 AWQ fused QKV (K=4096, N=4096+1024+1024, g128): GEMV/GEMM at M = 1, 16, 128
+
+The step is captured once per input set in a HIP graph; the timed region
+replays K step graphs, rotating over enough input sets (>= 512 MB in total)
+that no step finds its data in the 256 MB MALL.  value = sum of the
+algorithmic bytes of all kernels / step time.  Each kernel is also timed
+alone (a graph of R launches rotating over the sets, HIP events on the launch
+stream) for the per-kernel breakdown and the roofline of the dominant kernel.
+
+Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # dense E4M3 MFMA
+FP16_PEAK_TFLOPS = 2500.0      # dense fp16 MFMA
+METRIC = "quantized decode GEMV/GEMM GB/s (% HBM peak) and TFLOP/s at M=1..256"
+
+KV_T, KV_D, KV_GS = 32768, 128, 32
+QKV_K, QKV_SEG = 4096, (4096, 1024, 1024)
+DOWN_K, DOWN_N = 14336, 4096
+AWQ_K, AWQ_NS, AWQ_GS = 4096, (4096, 1024, 1024), 128
+QKV_MS, DOWN_MS, AWQ_MS = (1, 8, 32), (64, 128, 256), (1, 16, 128)
+
+
+# ----------------------------------------------------------- work model ---
+
+def kernel_table():
+    """(name, algorithmic bytes, flops, peak kind) per kernel in step order."""
+    rows = []
+    kv_in = KV_T * KV_D * 4
+    rows.append(("kv_int8_quant", kv_in + KV_T * KV_D + KV_T * 4, 0, "hbm"))
+    rows.append(("kv_int8_dequant", kv_in + KV_T * KV_D + KV_T * 4, 0, "hbm"))
+    g = KV_T * KV_D // KV_GS
+    rows.append(("kv_int4_quant", kv_in + KV_T * KV_D // 2 + g * 8, 0, "hbm"))
+    rows.append(("kv_int4_dequant", kv_in + KV_T * KV_D // 2 + g * 8, 0, "hbm"))
+    n = sum(QKV_SEG)
+    for m in QKV_MS:
+        rows.append((f"w8a8_act_quant_row_M{m}", m * QKV_K * 2 + m * QKV_K + m * 4, 0, "hbm"))
+        rows.append((f"w8a8_gemv_rowscale_M{m}", n * QKV_K + n * 4 + m * QKV_K + m * 4 + m * n * 2,
+                     2 * m * n * QKV_K, "fp8"))
+    kb = DOWN_K // 128
+    for m in DOWN_MS:
+        rows.append((f"w8a8_act_quant_silu_g128_M{m}", m * DOWN_K * 2 + m * DOWN_K + m * kb * 4, 0, "hbm"))
+        rows.append((f"w8a8_gemm_blk128_M{m}",
+                     DOWN_N * DOWN_K + (DOWN_N // 128) * kb * 4 + m * DOWN_K + m * kb * 4 + m * DOWN_N * 2,
+                     2 * m * DOWN_N * DOWN_K, "fp8"))
+    na = sum(AWQ_NS)
+    for m in AWQ_MS:
+        rows.append((f"int4_awq_qkv_M{m}",
+                     AWQ_K * na // 2 + 2 * (AWQ_K // AWQ_GS) * na * 4 + m * AWQ_K * 4 + m * na * 4,
+                     2 * m * na * AWQ_K, "fp16"))
+    return rows
+
+
+def roofline_for(name, nbytes, flops, kind, seconds):
+    peak_tf = {"fp8": FP8_PEAK_TFLOPS, "fp16": FP16_PEAK_TFLOPS}.get(kind)
+    gbs = nbytes / seconds / 1e9
+    if peak_tf and flops / nbytes > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9):
+        tf = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(tf / peak_tf, 4)}
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+# -------------------------------------------------------------- inputs ----
+
+def make_inputs(torch, api, synth):
+    """One set of device inputs (numpy draws from the seeded generators)."""
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    s = {}
+    s["kv_x"] = dev(synth.kv_cache(KV_T, KV_D, seed=2))
+    qkv = synth.w8a8_qkv(seed=3)
+    s["qkv_x"] = dev(qkv.x_bf16.view(np.int16)).view(torch.bfloat16)
+    s["qkv_w"] = [api.weight_quant(dev(w), api.ROWSCALE) for w in qkv.weights]
+    down = synth.w8a8_down(seed=4)
+    s["down_x"] = dev(down.x_bf16.view(np.int16)).view(torch.bfloat16)
+    s["down_w"] = [api.weight_quant(dev(w), api.BLK128) for w in down.weights]
+    x5, projs = synth.int4_qkv(seed=5)
+    s["awq_x"] = dev(x5)
+    s["awq_p"] = [(dev(p.qweight.view(np.int32)), dev(p.scales), dev(p.zeros)) for p in projs]
+    torch.cuda.synchronize()
+    return s, (qkv, down, x5, projs)
+
+
+def clone_set(torch, s):
+    c = {}
+    for k, v in s.items():
+        if isinstance(v, list):
+            c[k] = [tuple(t.clone() for t in item) for item in v]
+        else:
+            c[k] = v.clone()
+    return c
+
+
+class StepBuffers:
+    """Outputs and scratch for one input set, allocated before capture."""
+
+    def __init__(self, torch, api, s):
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+        self.s = s
+        self.kv_codes = e((KV_T, KV_D), torch.int8)
+        self.kv_scales = e((KV_T,), torch.float32)
+        self.kv_y8 = e((KV_T, KV_D), torch.float32)
+        g = KV_T * KV_D // KV_GS
+        self.kv_packed = e((KV_T * KV_D // 2,), torch.uint8)
+        self.kv_s4 = e((g,), torch.float32)
+        self.kv_z4 = e((g,), torch.float32)
+        self.kv_y4 = e((KV_T, KV_D), torch.float32)
+        self.qkv_weight = api.W8a8Weight(api.ROWSCALE, s["qkv_w"])
+        self.down_weight = api.W8a8Weight(api.BLK128, s["down_w"])
+        self.qkv_q = {m: e((m, QKV_K), torch.uint8) for m in QKV_MS}
+        self.qkv_sa = {m: e((m,), torch.float32) for m in QKV_MS}
+        self.qkv_out = {m: e((m, sum(QKV_SEG)), torch.bfloat16) for m in QKV_MS}
+        self.down_q = {m: e((m, DOWN_K), torch.uint8) for m in DOWN_MS}
+        self.down_sa = {m: e((m, DOWN_K // 128), torch.float32) for m in DOWN_MS}
+        self.down_out = {m: e((m, DOWN_N), torch.bfloat16) for m in DOWN_MS}
+        self.awq_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_MS}
+
+    # each launcher issues exactly one kernel
+    def launchers(self, api):
+        s = self.s
+        L = []
+        L.append(("kv_int8_quant", lambda: api.quant_int8_token(s["kv_x"], self.kv_codes, self.kv_scales)))
+        L.append(("kv_int8_dequant", lambda: api.dequant_int8_token(self.kv_codes, self.kv_scales, self.kv_y8)))
+        L.append(("kv_int4_quant", lambda: api.quant_int4_group(s["kv_x"], KV_GS, self.kv_packed, self.kv_s4,
+                                                                 self.kv_z4)))
+        L.append(("kv_int4_dequant", lambda: api.dequant_int4_group(self.kv_packed, self.kv_s4, self.kv_z4, KV_T,
+                                                                     KV_D, KV_GS, self.kv_y4)))
+        for m in QKV_MS:
+            L.append((f"w8a8_act_quant_row_M{m}",
+                      lambda m=m: api.act_quant(s["qkv_x"][:m], QKV_K, api.ROWSCALE, False, None, self.qkv_q[m],
+                                                self.qkv_sa[m])))
+            L.append((f"w8a8_gemv_rowscale_M{m}",
+                      lambda m=m: api.gemv(self.qkv_q[m], self.qkv_sa[m], self.qkv_weight, out=self.qkv_out[m])))
+        for m in DOWN_MS:
+            L.append((f"w8a8_act_quant_silu_g128_M{m}",
+                      lambda m=m: api.act_quant(s["down_x"][:m], DOWN_K, api.BLK128, True, None, self.down_q[m],
+                                                self.down_sa[m])))
+            L.append((f"w8a8_gemm_blk128_M{m}",
+                      lambda m=m: api.gemv(self.down_q[m], self.down_sa[m], self.down_weight,
+                                           out=self.down_out[m])))
+        for m in AWQ_MS:
+            L.append((f"int4_awq_qkv_M{m}",
+                      lambda m=m: api.int4_awq_qkv(s["awq_x"][:m], s["awq_p"], AWQ_GS, outs=self.awq_out[m])))
+        return L
+
+
+def capture(torch, fns, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for f in fns:
+                f()
+    return g
+
+
+# ---------------------------------------------------------- cpu baseline --
+
+def cpu_baseline(host_inputs, table):
+    """The oracle, as it stands, over one full step on the same inputs."""
+    import oracle
+    from kv_quantization_amd import synth
+
+    qkv, down, x5, projs = host_inputs
+    kv_x = synth.kv_cache(KV_T, KV_D, seed=2)
+    # offline weight preparation is not part of a step
+    wq = [oracle.weight_quant(oracle.ROWSCALE, w) for w in qkv.weights]
+    wd = [oracle.weight_quant(oracle.BLK128, w) for w in down.weights]
+    awq = [(p.qweight, p.scales, p.zeros) for p in projs]
+    t0 = time.perf_counter()
+    c8, s8 = oracle.kv_int8_quant(kv_x)
+    oracle.kv_int8_dequant(c8, s8)
+    p4, s4, z4 = oracle.kv_int4_quant(kv_x, KV_GS)
+    oracle.kv_int4_dequant(p4, s4, z4, KV_T, KV_D, KV_GS)
+    for m in QKV_MS:
+        q, sa = oracle.act_quant(oracle.ROWSCALE, qkv.x_bf16[:m], QKV_K)
+        oracle.w8a8_gemv(oracle.ROWSCALE, q, sa, wq)
+    for m in DOWN_MS:
+        q, sa = oracle.act_quant(oracle.BLK128, down.x_bf16[:m], DOWN_K, silu=True)
+        oracle.w8a8_gemv(oracle.BLK128, q, sa, wd)
+    for m in AWQ_MS:
+        oracle.int4_awq_qkv(x5[:m], awq, AWQ_GS)
+    seconds = time.perf_counter() - t0
+    total = sum(r[1] for r in table)
+    return {"value": round(total / seconds / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "one full step on the same inputs (every kernel at every M; products as fp64 numpy "
+                      "matmuls), offline weight quantization excluded, %.1f s" % seconds}
+
+
+def tensors_of(s):
+    for v in s.values():
+        for item in (v if isinstance(v, list) else [v]):
+            for t in (item if isinstance(item, tuple) else (item,)):
+                yield t
+
+
+# ------------------------------------------------------------------ main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough for >= 512 MB)")
+    ap.add_argument("--kernel-reps", type=int, default=100, help="launches per isolated kernel timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verbose", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU; every kernel here runs on a single MI355X "
+              "(see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from kv_quantization_amd import api, synth
+
+    log = (lambda *a: print(*a, file=sys.stderr, flush=True)) if args.verbose else (lambda *a: None)
+    table = kernel_table()
+    names = [r[0] for r in table]
+    step_bytes = sum(r[1] for r in table)
+
+    log("generating inputs")
+    base, host_inputs = make_inputs(torch, api, synth)
+    set_bytes = sum(t.numel() * t.element_size() for t in tensors_of(base))
+    nsets = args.sets or max(2, -(-512 * 2 ** 20 // (set_bytes + 64 * 2 ** 20)))
+    sets = [base] + [clone_set(torch, base) for _ in range(nsets - 1)]
+    bufs = [StepBuffers(torch, api, s) for s in sets]
+    launch = [b.launchers(api) for b in bufs]
+    assert [n for n, _ in launch[0]] == names
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for L in launch:                    # eager pass: allocates workspaces, checks launches
+            for _, f in L:
+                f()
+    torch.cuda.synchronize()
+    log(f"{nsets} input sets of {set_bytes / 2**20:.0f} MiB; capturing")
+    step_graphs = [capture(torch, [f for _, f in L], stream) for L in launch]
+
+    # ---- timed region: exactly `steps` steps
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step_graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for i in range(args.steps):
+            step_graphs[i % nsets].replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # ---- per-kernel durations (graphs of R launches rotating over the sets)
+    per_kernel = {}
+    reps = max(nsets, args.kernel_reps // nsets * nsets)
+    for ki, name in enumerate(names):
+        g = capture(torch, [launch[r % nsets][ki][1] for r in range(reps)], stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_kernel[name] = a.elapsed_time(b) / reps / 1e3     # seconds per launch
+        del g
+
+    breakdown = []
+    for name, nbytes, flops, kind in table:
+        sec = per_kernel[name]
+        entry = {"kernel": name, "us": round(sec * 1e6, 2), "GB/s": round(nbytes / sec / 1e9, 1),
+                 "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)}
+        if flops:
+            entry["TFLOP/s"] = round(flops / sec / 1e12, 2)
+        breakdown.append(entry)
+    dom = max(table, key=lambda r: per_kernel[r[0]])
+    roof = roofline_for(*dom, per_kernel[dom[0]])
+    roof["kernel"] = dom[0]
+    roof["traffic"] = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3+f16 MFMA, f32 quantizers",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode hot-path pass: KV cache 32768x128 INT8 + INT4(g32) quant/dequant; W8A8 rowscale "
+                        "fused-QKV act-quant+GEMV K=4096 N=6144 M=1,8,32; W8A8 blk128 SiLU act-quant+GEMM "
+                        "K=14336 N=4096 M=64,128,256; INT4 AWQ fused QKV K=4096 N=6144 g128 M=1,16,128",
+            "input_sets": nsets,
+            "step_bytes": step_bytes,
+            "timing": "HIP graph per step, rotating input sets (no MALL reuse across steps)",
+        },
+        "roofline": roof,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle")
+        result["cpu_baseline"] = cpu_baseline(host_inputs, table)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: quantized-decode kernels for AMD MI355X
+ * (gfx950, CDNA4), written in HIP.
+ *
+ * Conventions for every call below
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees or retains memory.  Base pointers must be 16-byte
+ *     aligned (checked).  bf16 values travel as uint16_t bit patterns and
+ *     E4M3 (OCP E4M3FN) codes as uint8_t.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  No call synchronizes.
+ *   - Return value: KVQ_OK, or a kvq_status_t error.  Arguments are validated
+ *     on the host before any HIP call; on error nothing is launched and
+ *     kvq_last_error() describes the first violated condition.  No exception
+ *     crosses this boundary.
+ *   - Outputs are written in full (no read-modify-write of caller memory),
+ *     except where a call documents a workspace that it leaves zero-filled.
+ *
+ * Sources (web pages; each declaration names the section it implements):
+ *   [KVQ]  boostr, src/ops/wgpu/shaders/cache/kv_cache_quant.wgsl
+ *   [W8A8] metrale_model_layers, layers/ops/w8a8_decode.rs
+ *   [AWQ]  boostr, src/quant/wgpu/shaders/fused_int4_qkv.rs
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_E_INVALID = 1,      /* an argument violates the documented contract   */
+    KVQ_E_UNSUPPORTED = 2,  /* no gfx950 code object for the current device   */
+    KVQ_E_LAUNCH = 3        /* the HIP runtime rejected a kernel launch        */
+} kvq_status_t;
+
+/* Message for the last failing call on this thread ("" if none).  The
+ * pointer stays valid until the next failing call on the same thread. */
+const char *kvq_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int kvq_abi_version(void);
+
+/* ======================================================================== */
+/* KV cache, symmetric per-token INT8                                       */
+/* [KVQ] sections "INT8 Per-Token Quantization" / "Dequantization".  The
+ * page's "FP8 Per-Token" sections compute the same integer code (absmax/127,
+ * not an E4M3 encoding); kvq_quant_fp8_token / kvq_dequant_fp8_token are
+ * aliases of these two calls.
+ *
+ *   scale[t] = max(max_d |x[t][d]| / 127, 1e-8)        (fp32, IEEE division)
+ *   codes[t][d] = clamp(rint_half_even(x[t][d] / scale[t]), -128, 127)
+ *   y[t][d] = (float)codes[t][d] * scale[t]
+ *
+ * x, y: fp32 [num_tokens][head_dim] row-major; codes: int8, same shape;
+ * scales: fp32 [num_tokens].  num_tokens >= 1, head_dim >= 1.  Inputs must be
+ * finite (NaN/Inf are outside the contract). */
+int kvq_quant_int8_token(const float *x, int8_t *codes, float *scales,
+                         uint32_t num_tokens, uint32_t head_dim, void *stream);
+int kvq_dequant_int8_token(const int8_t *codes, const float *scales, float *y,
+                           uint32_t num_tokens, uint32_t head_dim, void *stream);
+int kvq_quant_fp8_token(const float *x, int8_t *codes, float *scales,
+                        uint32_t num_tokens, uint32_t head_dim, void *stream);
+int kvq_dequant_fp8_token(const int8_t *codes, const float *scales, float *y,
+                          uint32_t num_tokens, uint32_t head_dim, void *stream);
+
+/* ======================================================================== */
+/* KV cache, asymmetric per-group INT4                                      */
+/* [KVQ] sections "INT4 Per-Group Quantization" / "Dequantization".  Groups
+ * are group_size consecutive elements of the flattened [num_tokens*head_dim]
+ * array (a group may span tokens when head_dim % group_size != 0).
+ *
+ *   mn, mx = min, max of the group;   scale = (mx - mn) / 15  (stored as is)
+ *   sf = max(scale, 1e-8);   zero = -mn / sf
+ *   code = clamp(rint_half_even((x - mn) / sf), 0, 15)
+ *   packed[e / 2] = code[e even] | code[e odd] << 4      (low nibble first)
+ *   y = (float)code * scale - zero * scale     (two roundings, then subtract)
+ *
+ * x, y: fp32 [num_tokens*head_dim]; packed: uint8 [num_tokens*head_dim/2];
+ * scales, zeros: fp32 [G], G = num_tokens*head_dim/group_size.  The page
+ * stores the zeros after the scales in one buffer; here they are a separate
+ * array.  group_size >= 2, even, and divides num_tokens*head_dim.  A constant
+ * group stores scale 0 and dequantizes to +0 (the page's behaviour). */
+int kvq_quant_int4_group(const float *x, uint8_t *packed, float *scales,
+                         float *zeros, uint32_t num_tokens, uint32_t head_dim,
+                         uint32_t group_size, void *stream);
+int kvq_dequant_int4_group(const uint8_t *packed, const float *scales,
+                           const float *zeros, float *y, uint32_t num_tokens,
+                           uint32_t head_dim, uint32_t group_size, void *stream);
+
+/* ======================================================================== */
+/* W8A8 FP8 decode (OCP E4M3FN activations and weights)                     */
+/* [W8A8] items W8a8Scale, W8a8Weight, W8a8Scratch, w8a8_act_quant,
+ * w8a8_act_quant_silu, w8a8_gemv, w8a8_proj. */
+
+typedef enum {
+    W8A8_ROWSCALE = 0,  /* W8a8Scale::PerRow: one weight scale per output row,
+                           one activation scale per token row               */
+    W8A8_BLK128 = 1     /* W8a8Scale::Block128: one weight scale per 128x128
+                           block, one activation scale per 128 columns       */
+} w8a8_scale_t;
+
+#define W8A8_MAX_ROWS 256u   /* largest token-row count per call            */
+#define W8A8_K_UNIT 128u     /* K must be a positive multiple of this       */
+
+/* Activation quantization (w8a8_act_quant; with silu, w8a8_act_quant_silu).
+ *   v = f32(x)                       silu == 0 (up must be NULL)
+ *   v = silu(f32(x))                 silu != 0, up == NULL
+ *   v = silu(f32(x)) * f32(up)       silu != 0, up != NULL (gate = x)
+ * silu(v) = v / (1 + e^-v) with a fixed fp32 exponential (Cody-Waite
+ * reduction + degree-7 Taylor polynomial), so results are reproducible bits.
+ * Per row (ROWSCALE) or per 128-column group (BLK128):
+ *   s = max(amax / 448, 1e-8);   q = E4M3_rne_satfinite(v / s)
+ * x, up: bf16 [rows][ldx]; q: uint8 [rows][k]; a_scales: fp32 [rows]
+ * (ROWSCALE) or [rows][k/128] (BLK128).  1 <= rows <= 256, k % 128 == 0,
+ * ldx >= k, ldx % 8 == 0.  Inputs must be finite. */
+int w8a8_act_quant(w8a8_scale_t kind, int silu, const uint16_t *x,
+                   const uint16_t *up, uint32_t ldx, uint32_t rows, uint32_t k,
+                   uint8_t *q, float *a_scales, void *stream);
+
+/* Sizes of the two activation buffers w8a8_act_quant writes and w8a8_gemv
+ * reads (W8a8Scratch): q_bytes = rows*k, scale_bytes = rows*max(k/128,1)*4
+ * for BLK128 and rows*4 for ROWSCALE. */
+int w8a8_scratch_bytes(w8a8_scale_t kind, uint32_t rows, uint32_t k,
+                       size_t *q_bytes, size_t *scale_bytes);
+
+/* One weight segment (a Fp8Weight): E4M3 codes [n][k] row-major, and scales
+ * fp32 [n] (ROWSCALE) or [ceil(n/128)][k/128] (BLK128). */
+typedef struct {
+    const uint8_t *w;
+    const float *scale;
+    uint32_t n;
+} w8a8_segment_t;
+
+/* GEMV/GEMM over 1..3 concatenated weight segments (w8a8_gemv):
+ *   out[m][j] = bf16_rne( sum_k dec(q[m][k]) * sa * dec(W[j][k]) * sw )
+ * where W is the concatenation of the segments along n (output column j
+ * belongs to segment 0 below n0, segment 1 below n0+n1, else segment 2) and
+ * the scales are the row scales (ROWSCALE: sa[m] * sw[j]) or the block
+ * scales applied per 128-wide K block (BLK128: sa[m][kb] * sw[j/128][kb]).
+ * Accumulation is fp32.  Every segment but the last must have n % 16 == 0
+ * (ROWSCALE) or n % 128 == 0 (BLK128); all share k.
+ * q, a_scales: as written by w8a8_act_quant; out: bf16 [rows][ldc], ldc >=
+ * sum n; columns >= sum n of each row are not touched.
+ * workspace: NULL, or device memory of at least w8a8_gemv_workspace_bytes(),
+ * zero-filled before its first use; the call leaves it zero-filled again.
+ * Without it the call still works, with less parallelism for large rows.
+ * Concurrent calls must not share a workspace. */
+int w8a8_gemv(w8a8_scale_t kind, const uint8_t *q, const float *a_scales,
+              uint32_t rows, uint32_t k, const w8a8_segment_t *segs,
+              uint32_t nseg, uint16_t *out, uint32_t ldc, void *workspace,
+              size_t workspace_bytes, void *stream);
+
+/* Workspace size that lets w8a8_gemv use its full parallelism (may be 0). */
+int w8a8_gemv_workspace_bytes(w8a8_scale_t kind, uint32_t rows, uint32_t k,
+                              uint32_t n_total, size_t *bytes);
+
+/* w8a8_proj: act_quant into (q, a_scales) then gemv, on one stream. */
+int w8a8_proj(w8a8_scale_t kind, int silu, const uint16_t *x,
+              const uint16_t *up, uint32_t ldx, uint32_t rows, uint32_t k,
+              const w8a8_segment_t *segs, uint32_t nseg, uint16_t *out,
+              uint32_t ldc, uint8_t *q, float *a_scales, void *workspace,
+              size_t workspace_bytes, void *stream);
+
+/* Offline weight preparation with the activation rule: w fp32 [n][k] ->
+ * codes [n][k] and scales [n] (ROWSCALE) or [ceil(n/128)][k/128] (BLK128),
+ * amax taken per weight row or per 128x128 block.  k % 128 == 0.  (The page
+ * receives weights already quantized; this supplies them.) */
+int w8a8_weight_quant(w8a8_scale_t kind, const float *w, uint32_t n,
+                      uint32_t k, uint8_t *q, float *scales, void *stream);
+
+/* Plain conversion fp32 -> E4M3FN (round to nearest even, saturating to
+ * +-448, sign kept), the encoder every W8A8 quantizer above uses. */
+int kvq_f32_to_e4m3(const float *x, uint8_t *q, uint64_t n, void *stream);
+
+/* ======================================================================== */
+/* INT4 AWQ weight-only, fused Q/K/V                                        */
+/* [AWQ] QKV_AWQ_SHIFTS, unpack_awq_qkv, fused_int4_qkv_q / _k / _v.
+ *
+ *   code(k, j) = (qweight[k][j/8] >> SHIFTS[j % 8]) & 0xF,
+ *                SHIFTS = {0, 16, 4, 20, 8, 24, 12, 28}
+ *   out[m][j]  = sum_k x[m][k] * (code(k, j) - zeros[k/gs][j]) * scales[k/gs][j]
+ *
+ * One projection: qweight uint32 [k][n/8]; scales, zeros fp32 [k/gs][n];
+ * out fp32 [m][n].  n % 8 == 0. */
+typedef struct {
+    const uint32_t *qweight;
+    const float *scales;
+    const float *zeros;
+    float *out;
+    uint32_t n;
+} int4_awq_proj_t;
+
+/* Q, K and V in one launch (the page dispatches three kernels).  k_proj and
+ * v_proj are both NULL (a single projection) or both set with equal n.
+ * x: fp32 [m][k], m >= 1, k % group_size == 0, group_size % 32 == 0.
+ * Activations are rounded to fp16 (round to nearest even) for the matrix
+ * cores; codes are exact; accumulation is fp32; |x| must stay below 65504.
+ * workspace: NULL, or at least int4_awq_workspace_bytes(), zero-filled before
+ * its first use and left zero-filled; concurrent calls must not share it. */
+int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k,
+                      uint32_t group_size, const int4_awq_proj_t *q_proj,
+                      const int4_awq_proj_t *k_proj,
+                      const int4_awq_proj_t *v_proj, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_size,
+                             uint32_t n_total, size_t *bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

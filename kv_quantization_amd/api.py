@@ -1,0 +1,244 @@
+"""PyTorch-facing wrappers over the libkvq.so C ABI.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind include/kvq.h.  torch provides device memory and the current
+stream; tensors must live on a ROCm device, be contiguous and have the dtype
+each function states.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import W8A8_BLK128, W8A8_ROWSCALE, Int4AwqProj, W8a8Segment
+
+ROWSCALE = W8A8_ROWSCALE
+BLK128 = W8A8_BLK128
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _empty(shape, dtype, like: torch.Tensor):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ------------------------------------------------------------ workspace ----
+
+_workspaces: dict = {}
+
+
+def workspace(device: torch.device, nbytes: int, stream: int) -> torch.Tensor:
+    """A zero-filled device buffer of at least nbytes, cached per (device,
+    stream).  The kernels leave their workspace zero-filled, so reuse by calls
+    ordered on one stream is safe."""
+    key = (torch.device(device), stream)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
+# ----------------------------------------------------------- KV cache ------
+
+def quant_int8_token(x: torch.Tensor, codes=None, scales=None):
+    """x fp32 [T, D] -> (codes int8 [T, D], scales fp32 [T])."""
+    t, d = x.shape
+    codes = _empty((t, d), torch.int8, x) if codes is None else codes
+    scales = _empty((t,), torch.float32, x) if scales is None else scales
+    _lib.call("kvq_quant_int8_token", _dev(x, torch.float32, "x"), _dev(codes, torch.int8, "codes"),
+              _dev(scales, torch.float32, "scales"), t, d, _stream(x))
+    return codes, scales
+
+
+def dequant_int8_token(codes: torch.Tensor, scales: torch.Tensor, out=None):
+    t, d = codes.shape
+    out = _empty((t, d), torch.float32, codes) if out is None else out
+    _lib.call("kvq_dequant_int8_token", _dev(codes, torch.int8, "codes"), _dev(scales, torch.float32, "scales"),
+              _dev(out, torch.float32, "out"), t, d, _stream(codes))
+    return out
+
+
+def quant_int4_group(x: torch.Tensor, group_size: int, packed=None, scales=None, zeros=None):
+    """x fp32 [T, D] -> (packed uint8 [T*D/2], scales fp32 [G], zeros fp32 [G])."""
+    t, d = x.shape
+    total = t * d
+    g = total // group_size if group_size else 0
+    packed = _empty((total // 2,), torch.uint8, x) if packed is None else packed
+    scales = _empty((g,), torch.float32, x) if scales is None else scales
+    zeros = _empty((g,), torch.float32, x) if zeros is None else zeros
+    _lib.call("kvq_quant_int4_group", _dev(x, torch.float32, "x"), _dev(packed, torch.uint8, "packed"),
+              _dev(scales, torch.float32, "scales"), _dev(zeros, torch.float32, "zeros"), t, d, group_size,
+              _stream(x))
+    return packed, scales, zeros
+
+
+def dequant_int4_group(packed, scales, zeros, num_tokens: int, head_dim: int, group_size: int, out=None):
+    out = _empty((num_tokens, head_dim), torch.float32, packed) if out is None else out
+    _lib.call("kvq_dequant_int4_group", _dev(packed, torch.uint8, "packed"), _dev(scales, torch.float32, "scales"),
+              _dev(zeros, torch.float32, "zeros"), _dev(out, torch.float32, "out"), num_tokens, head_dim,
+              group_size, _stream(packed))
+    return out
+
+
+# --------------------------------------------------------------- W8A8 ------
+
+def scratch_bytes(kind: int, rows: int, k: int):
+    qb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _lib.call("w8a8_scratch_bytes", kind, rows, k, ctypes.byref(qb), ctypes.byref(sb))
+    return qb.value, sb.value
+
+
+def act_quant(x: torch.Tensor, k: int | None = None, kind: int = ROWSCALE, silu: bool = False,
+              up: torch.Tensor | None = None, q=None, scales=None):
+    """x bf16 [rows, ldx] (gate when silu) -> (q uint8 [rows, k], scales fp32)."""
+    rows, ldx = x.shape
+    k = ldx if k is None else k
+    q = _empty((rows, k), torch.uint8, x) if q is None else q
+    if scales is None:
+        scales = _empty((rows,) if kind == ROWSCALE else (rows, k // 128), torch.float32, x)
+    up_ptr = 0 if up is None else _dev(up, torch.bfloat16, "up")
+    if up is not None and up.shape != x.shape:
+        raise ValueError("up must have the shape of x")
+    _lib.call("w8a8_act_quant", kind, int(silu), _dev(x, torch.bfloat16, "x"), up_ptr, ldx, rows, k,
+              _dev(q, torch.uint8, "q"), _dev(scales, torch.float32, "scales"), _stream(x))
+    return q, scales
+
+
+def weight_quant(w: torch.Tensor, kind: int = ROWSCALE):
+    """w fp32 [n, k] -> (codes uint8 [n, k], scales fp32 [n] or [ceil(n/128), k/128])."""
+    n, k = w.shape
+    q = _empty((n, k), torch.uint8, w)
+    s = _empty((n,) if kind == ROWSCALE else ((n + 127) // 128, k // 128), torch.float32, w)
+    _lib.call("w8a8_weight_quant", kind, _dev(w, torch.float32, "w"), n, k, _dev(q, torch.uint8, "q"),
+              _dev(s, torch.float32, "scales"), _stream(w))
+    return q, s
+
+
+def f32_to_e4m3(x: torch.Tensor, out=None):
+    out = _empty(x.shape, torch.uint8, x) if out is None else out
+    _lib.call("kvq_f32_to_e4m3", _dev(x, torch.float32, "x"), _dev(out, torch.uint8, "out"), x.numel(), _stream(x))
+    return out
+
+
+@dataclass
+class W8a8Weight:
+    """1..3 E4M3 weight segments sharing K (metrale W8a8Weight)."""
+    kind: int
+    segments: list  # [(codes uint8 [n_i, k], scales fp32), ...]
+
+    @property
+    def k(self) -> int:
+        return int(self.segments[0][0].shape[1])
+
+    @property
+    def n(self) -> int:
+        return int(sum(int(c.shape[0]) for c, _ in self.segments))
+
+    def c_segments(self):
+        arr = (W8a8Segment * 3)()
+        for i, (c, s) in enumerate(self.segments):
+            arr[i].w = _dev(c, torch.uint8, f"segment {i} codes")
+            arr[i].scale = _dev(s, torch.float32, f"segment {i} scales")
+            arr[i].n = int(c.shape[0])
+        return arr
+
+
+def gemv_workspace_bytes(kind: int, rows: int, k: int, n_total: int) -> int:
+    b = ctypes.c_size_t()
+    _lib.call("w8a8_gemv_workspace_bytes", kind, rows, k, n_total, ctypes.byref(b))
+    return b.value
+
+
+def gemv(q: torch.Tensor, a_scales: torch.Tensor, weight: W8a8Weight, out=None, ldc: int | None = None,
+         use_workspace: bool = True):
+    """(q, a_scales) from act_quant, W8a8Weight -> out bf16 [rows, ldc]."""
+    rows, k = q.shape
+    n = weight.n
+    ldc = n if ldc is None else ldc
+    out = _empty((rows, ldc), torch.bfloat16, q) if out is None else out
+    stream = _stream(q)
+    ws_ptr, ws_bytes = 0, 0
+    if use_workspace:
+        ws_bytes = gemv_workspace_bytes(weight.kind, rows, k, n)
+        if ws_bytes:
+            ws_ptr = workspace(q.device, ws_bytes, stream).data_ptr()
+    _lib.call("w8a8_gemv", weight.kind, _dev(q, torch.uint8, "q"), _dev(a_scales, torch.float32, "a_scales"), rows,
+              k, weight.c_segments(), len(weight.segments), _dev(out, torch.bfloat16, "out"), ldc, ws_ptr, ws_bytes,
+              stream)
+    return out
+
+
+def proj(x: torch.Tensor, weight: W8a8Weight, silu: bool = False, up=None, out=None):
+    """act_quant + gemv in one call (metrale w8a8_proj)."""
+    rows, ldx = x.shape
+    k = weight.k
+    q = _empty((rows, k), torch.uint8, x)
+    sa = _empty((rows,) if weight.kind == ROWSCALE else (rows, k // 128), torch.float32, x)
+    n = weight.n
+    out = _empty((rows, n), torch.bfloat16, x) if out is None else out
+    stream = _stream(x)
+    ws_bytes = gemv_workspace_bytes(weight.kind, rows, k, n)
+    ws_ptr = workspace(x.device, ws_bytes, stream).data_ptr() if ws_bytes else 0
+    up_ptr = 0 if up is None else _dev(up, torch.bfloat16, "up")
+    _lib.call("w8a8_proj", weight.kind, int(silu), _dev(x, torch.bfloat16, "x"), up_ptr, ldx, rows, k,
+              weight.c_segments(), len(weight.segments), _dev(out, torch.bfloat16, "out"), out.shape[1],
+              q.data_ptr(), sa.data_ptr(), ws_ptr, ws_bytes, stream)
+    return out
+
+
+# ------------------------------------------------------------ INT4 AWQ -----
+
+def int4_workspace_bytes(m: int, k: int, group_size: int, n_total: int) -> int:
+    b = ctypes.c_size_t()
+    _lib.call("int4_awq_workspace_bytes", m, k, group_size, n_total, ctypes.byref(b))
+    return b.value
+
+
+def int4_awq_qkv(x: torch.Tensor, projections, group_size: int, outs=None, use_workspace: bool = True):
+    """x fp32 [m, k]; projections: 1 or 3 of (qweight int32/uint32 [k, n/8],
+    scales fp32 [k/gs, n], zeros fp32 [k/gs, n]) -> list of fp32 [m, n]."""
+    m, k = x.shape
+    if len(projections) not in (1, 3):
+        raise ValueError("need 1 (single) or 3 (Q, K, V) projections")
+    structs, res = [], []
+    for i, (qw, sc, zr) in enumerate(projections):
+        n = int(qw.shape[1]) * 8
+        o = _empty((m, n), torch.float32, x) if outs is None else outs[i]
+        p = Int4AwqProj()
+        if qw.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("qweight must be int32/uint32")
+        p.qweight = _dev(qw, qw.dtype, "qweight")
+        p.scales = _dev(sc, torch.float32, "scales")
+        p.zeros = _dev(zr, torch.float32, "zeros")
+        p.out = _dev(o, torch.float32, "out")
+        p.n = n
+        structs.append(p)
+        res.append(o)
+    stream = _stream(x)
+    n_total = sum(s.n for s in structs)
+    ws_ptr, ws_bytes = 0, 0
+    if use_workspace:
+        ws_bytes = int4_workspace_bytes(m, k, group_size, n_total)
+        if ws_bytes:
+            ws_ptr = workspace(x.device, ws_bytes, stream).data_ptr()
+    kp = ctypes.byref(structs[1]) if len(structs) == 3 else None
+    vp = ctypes.byref(structs[2]) if len(structs) == 3 else None
+    _lib.call("int4_awq_qkv_gemm", _dev(x, torch.float32, "x"), m, k, group_size, ctypes.byref(structs[0]), kp, vp,
+              ws_ptr, ws_bytes, stream)
+    return res

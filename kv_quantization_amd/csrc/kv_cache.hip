@@ -1,0 +1,387 @@
+// KV-cache quantization for gfx950: symmetric per-token INT8 and asymmetric
+// per-group INT4, quantize and dequantize.
+//
+// Follows boostr kv_cache_quant.wgsl, sections "INT8 Per-Token
+// Quantization/Dequantization" (the "FP8 Per-Token" sections compute the same
+// code) and "INT4 Per-Group Quantization/Dequantization".  The page runs one
+// thread per token or group with strided, uncoalesced loops; here a team of
+// lanes owns a token (INT8) or group (INT4): each lane holds 4 consecutive
+// fp32 values from one 16-byte load, so a wave64 load instruction reads 1 KiB
+// of contiguous memory, the absmax/min/max is a butterfly over the team, and
+// each lane writes its packed codes with one 4-byte (INT8) or 2-byte (INT4)
+// store.  Shapes the teams cannot tile fall back to one wave per unit.
+//
+// Numerics match the page operation for operation in fp32: IEEE division
+// (v_div_scale/fmas/fixup, never a reciprocal multiply), round-half-to-even
+// via v_rndne_f32, and no fused multiply-add (the library is built with
+// -ffp-contract=off).
+#include "kvq_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kBlock = 256;           // 4 waves
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kUnroll = 4;            // 16-byte loads in flight per lane
+
+__device__ __forceinline__ uint32_t int8_code(float v, float s) {
+    int c = (int)__builtin_rintf(v / s);
+    c = c < -128 ? -128 : (c > 127 ? 127 : c);
+    return (uint32_t)c & 0xFFu;
+}
+
+__device__ __forceinline__ float int8_scale(float amax) { return fmaxf(amax / 127.0f, 1e-8f); }
+
+__device__ __forceinline__ uint32_t int4_code(float v, float mn, float sf) {
+    float d = v - mn;
+    int c = (int)__builtin_rintf(d / sf);
+    c = c < 0 ? 0 : (c > 15 ? 15 : c);
+    return (uint32_t)c;
+}
+
+__device__ __forceinline__ float abs_max4(f32x4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__device__ __forceinline__ uint64_t global_wave() {
+    return (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+}
+
+// ------------------------------------------------------------ INT8 ------
+
+// L lanes per token (head_dim = 4L); a wave covers U*(64/L) tokens.
+template <int L, int U>
+__global__ __launch_bounds__(kBlock) void int8_quant_team(const f32x4 *__restrict__ x,
+                                                          uint32_t *__restrict__ codes,
+                                                          float *__restrict__ scales,
+                                                          uint64_t num_tokens) {
+    constexpr int TPI = kWave / L;
+    const int lane = lane_id();
+    const int sub = lane / L, li = lane % L;
+    const uint64_t t0 = global_wave() * (U * TPI) + sub;
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t t = t0 + (uint64_t)u * TPI;
+        v[u] = t < num_tokens ? __builtin_nontemporal_load(&x[t * L + li]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t t = t0 + (uint64_t)u * TPI;
+        const float s = int8_scale(team_max<L>(abs_max4(v[u])));
+        const uint32_t packed = int8_code(v[u].x, s) | (int8_code(v[u].y, s) << 8) |
+                                (int8_code(v[u].z, s) << 16) | (int8_code(v[u].w, s) << 24);
+        if (t < num_tokens) {
+            codes[t * L + li] = packed;
+            if (li == 0) scales[t] = s;
+        }
+    }
+}
+
+// Any head_dim: one wave per token.
+__global__ __launch_bounds__(kBlock) void int8_quant_wave(const float *__restrict__ x,
+                                                          int8_t *__restrict__ codes,
+                                                          float *__restrict__ scales,
+                                                          uint64_t num_tokens, uint32_t head_dim) {
+    const uint64_t t = global_wave();
+    if (t >= num_tokens) return;
+    const float *row = x + t * head_dim;
+    float m = 0.0f;
+    for (uint32_t d = lane_id(); d < head_dim; d += kWave) m = fmaxf(m, fabsf(row[d]));
+    const float s = int8_scale(team_max<kWave>(m));
+    if (lane_id() == 0) scales[t] = s;
+    for (uint32_t d = lane_id(); d < head_dim; d += kWave)
+        codes[t * head_dim + d] = (int8_t)(uint8_t)int8_code(row[d], s);
+}
+
+template <int L, int U>
+__global__ __launch_bounds__(kBlock) void int8_dequant_team(const uint32_t *__restrict__ codes,
+                                                            const float *__restrict__ scales,
+                                                            f32x4 *__restrict__ y,
+                                                            uint64_t num_tokens) {
+    constexpr int TPI = kWave / L;
+    const int lane = lane_id();
+    const int sub = lane / L, li = lane % L;
+    const uint64_t t0 = global_wave() * (U * TPI) + sub;
+    uint32_t w[U];
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t t = t0 + (uint64_t)u * TPI;
+        const bool ok = t < num_tokens;
+        w[u] = ok ? __builtin_nontemporal_load(&codes[t * L + li]) : 0u;
+        s[u] = ok ? scales[t] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t t = t0 + (uint64_t)u * TPI;
+        f32x4 o;
+        o.x = (float)(int8_t)(w[u]) * s[u];
+        o.y = (float)(int8_t)(w[u] >> 8) * s[u];
+        o.z = (float)(int8_t)(w[u] >> 16) * s[u];
+        o.w = (float)(int8_t)(w[u] >> 24) * s[u];
+        if (t < num_tokens) __builtin_nontemporal_store(o, &y[t * L + li]);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void int8_dequant_wave(const int8_t *__restrict__ codes,
+                                                            const float *__restrict__ scales,
+                                                            float *__restrict__ y,
+                                                            uint64_t num_tokens, uint32_t head_dim) {
+    const uint64_t t = global_wave();
+    if (t >= num_tokens) return;
+    const float s = scales[t];
+    for (uint32_t d = lane_id(); d < head_dim; d += kWave)
+        y[t * head_dim + d] = (float)codes[t * head_dim + d] * s;
+}
+
+// ------------------------------------------------------------ INT4 ------
+
+// L lanes per group (group_size = 4L); a wave covers U*(64/L) groups.
+template <int L, int U>
+__global__ __launch_bounds__(kBlock) void int4_quant_team(const f32x4 *__restrict__ x,
+                                                          uint16_t *__restrict__ packed,
+                                                          float *__restrict__ scales,
+                                                          float *__restrict__ zeros,
+                                                          uint64_t num_groups) {
+    constexpr int GPI = kWave / L;
+    const int lane = lane_id();
+    const int sub = lane / L, li = lane % L;
+    const uint64_t g0 = global_wave() * (U * GPI) + sub;
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t g = g0 + (uint64_t)u * GPI;
+        v[u] = g < num_groups ? __builtin_nontemporal_load(&x[g * L + li]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t g = g0 + (uint64_t)u * GPI;
+        const float mn = team_min<L>(fminf(fminf(v[u].x, v[u].y), fminf(v[u].z, v[u].w)));
+        const float mx = team_max<L>(fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+        const float s = (mx - mn) / 15.0f;
+        const float sf = fmaxf(s, 1e-8f);
+        const float z = -mn / sf;
+        const uint32_t p = int4_code(v[u].x, mn, sf) | (int4_code(v[u].y, mn, sf) << 4) |
+                           (int4_code(v[u].z, mn, sf) << 8) | (int4_code(v[u].w, mn, sf) << 12);
+        if (g < num_groups) {
+            packed[g * L + li] = (uint16_t)p;
+            if (li == 0) {
+                scales[g] = s;
+                zeros[g] = z;
+            }
+        }
+    }
+}
+
+// Any even group_size: one wave per group, one byte (two codes) per step.
+__global__ __launch_bounds__(kBlock) void int4_quant_wave(const float *__restrict__ x,
+                                                          uint8_t *__restrict__ packed,
+                                                          float *__restrict__ scales,
+                                                          float *__restrict__ zeros,
+                                                          uint64_t num_groups, uint32_t group_size) {
+    const uint64_t g = global_wave();
+    if (g >= num_groups) return;
+    const float *grp = x + g * group_size;
+    float mn = grp[0], mx = grp[0];
+    for (uint32_t i = lane_id(); i < group_size; i += kWave) {
+        mn = fminf(mn, grp[i]);
+        mx = fmaxf(mx, grp[i]);
+    }
+    mn = team_min<kWave>(mn);
+    mx = team_max<kWave>(mx);
+    const float s = (mx - mn) / 15.0f;
+    const float sf = fmaxf(s, 1e-8f);
+    const float z = -mn / sf;
+    if (lane_id() == 0) {
+        scales[g] = s;
+        zeros[g] = z;
+    }
+    uint8_t *out = packed + g * (group_size / 2);
+    for (uint32_t p = lane_id(); p < group_size / 2; p += kWave)
+        out[p] = (uint8_t)(int4_code(grp[2 * p], mn, sf) | (int4_code(grp[2 * p + 1], mn, sf) << 4));
+}
+
+template <int L, int U>
+__global__ __launch_bounds__(kBlock) void int4_dequant_team(const uint16_t *__restrict__ packed,
+                                                            const float *__restrict__ scales,
+                                                            const float *__restrict__ zeros,
+                                                            f32x4 *__restrict__ y,
+                                                            uint64_t num_groups) {
+    constexpr int GPI = kWave / L;
+    const int lane = lane_id();
+    const int sub = lane / L, li = lane % L;
+    const uint64_t g0 = global_wave() * (U * GPI) + sub;
+    uint32_t w[U];
+    float s[U], z[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t g = g0 + (uint64_t)u * GPI;
+        const bool ok = g < num_groups;
+        w[u] = ok ? packed[g * L + li] : 0u;
+        s[u] = ok ? scales[g] : 0.0f;
+        z[u] = ok ? zeros[g] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t g = g0 + (uint64_t)u * GPI;
+        const float zs = z[u] * s[u];
+        f32x4 o;
+        o.x = (float)(w[u] & 15u) * s[u] - zs;
+        o.y = (float)((w[u] >> 4) & 15u) * s[u] - zs;
+        o.z = (float)((w[u] >> 8) & 15u) * s[u] - zs;
+        o.w = (float)((w[u] >> 12) & 15u) * s[u] - zs;
+        if (g < num_groups) __builtin_nontemporal_store(o, &y[g * L + li]);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void int4_dequant_wave(const uint8_t *__restrict__ packed,
+                                                            const float *__restrict__ scales,
+                                                            const float *__restrict__ zeros,
+                                                            float *__restrict__ y,
+                                                            uint64_t num_groups, uint32_t group_size) {
+    const uint64_t g = global_wave();
+    if (g >= num_groups) return;
+    const float s = scales[g];
+    const float zs = zeros[g] * s;
+    const uint8_t *in = packed + g * (group_size / 2);
+    float *out = y + g * group_size;
+    for (uint32_t p = lane_id(); p < group_size / 2; p += kWave) {
+        const uint32_t b = in[p];
+        out[2 * p] = (float)(b & 15u) * s - zs;
+        out[2 * p + 1] = (float)(b >> 4) * s - zs;
+    }
+}
+
+// ------------------------------------------------------------ host ------
+
+inline unsigned blocks_for(uint64_t units, uint64_t units_per_block) {
+    return (unsigned)((units + units_per_block - 1) / units_per_block);
+}
+
+// Team width for a row of `elems` fp32 values split 4 per lane, or 0.
+inline int team_lanes(uint64_t elems) {
+    if (elems % 4) return 0;
+    const uint64_t l = elems / 4;
+    return (l >= 1 && l <= 64 && (l & (l - 1)) == 0) ? (int)l : 0;
+}
+
+#define KVQ_TEAM_SWITCH(L, CALL)              \
+    switch (L) {                              \
+        case 1: { constexpr int LL = 1; CALL; } break;   \
+        case 2: { constexpr int LL = 2; CALL; } break;   \
+        case 4: { constexpr int LL = 4; CALL; } break;   \
+        case 8: { constexpr int LL = 8; CALL; } break;   \
+        case 16: { constexpr int LL = 16; CALL; } break; \
+        case 32: { constexpr int LL = 32; CALL; } break; \
+        default: { constexpr int LL = 64; CALL; } break; \
+    }
+
+int check_kv_common(const char *fn, const void *a, const void *b, const void *c,
+                    uint32_t num_tokens, uint32_t head_dim) {
+    if (!a || !b || !c) return fail(KVQ_E_INVALID, "%s: null pointer argument", fn);
+    if (!aligned16(a) || !aligned16(b) || !aligned16(c))
+        return fail(KVQ_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    if (num_tokens == 0 || head_dim == 0)
+        return fail(KVQ_E_INVALID, "%s: num_tokens=%u head_dim=%u (want both >= 1)", fn, num_tokens, head_dim);
+    return KVQ_OK;
+}
+
+int check_int4(const char *fn, const void *a, const void *b, const void *c, const void *d,
+               uint32_t num_tokens, uint32_t head_dim, uint32_t group_size) {
+    int st = check_kv_common(fn, a, b, c, num_tokens, head_dim);
+    if (st) return st;
+    if (!d) return fail(KVQ_E_INVALID, "%s: null pointer argument", fn);
+    if (!aligned16(d)) return fail(KVQ_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    const uint64_t total = (uint64_t)num_tokens * head_dim;
+    if (group_size < 2 || group_size % 2 || total % group_size)
+        return fail(KVQ_E_INVALID,
+                    "%s: group_size=%u must be even, >= 2 and divide num_tokens*head_dim=%llu", fn,
+                    group_size, (unsigned long long)total);
+    return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" int kvq_quant_int8_token(const float *x, int8_t *codes, float *scales, uint32_t num_tokens,
+                                    uint32_t head_dim, void *stream) {
+    int st = check_kv_common("kvq_quant_int8_token", x, codes, scales, num_tokens, head_dim);
+    if (st) return st;
+    const int L = team_lanes(head_dim);
+    hipStream_t s = as_stream(stream);
+    if (L) {
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int8_quant_team<LL, kUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
+                               (const f32x4 *)x, (uint32_t *)codes, scales, num_tokens)));
+    } else {
+        int8_quant_wave<<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(x, codes, scales, num_tokens,
+                                                                                  head_dim);
+    }
+    return launch_status("kvq_quant_int8_token");
+}
+
+extern "C" int kvq_dequant_int8_token(const int8_t *codes, const float *scales, float *y, uint32_t num_tokens,
+                                      uint32_t head_dim, void *stream) {
+    int st = check_kv_common("kvq_dequant_int8_token", codes, scales, y, num_tokens, head_dim);
+    if (st) return st;
+    const int L = team_lanes(head_dim);
+    hipStream_t s = as_stream(stream);
+    if (L) {
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int8_dequant_team<LL, kUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
+                               (const uint32_t *)codes, scales, (f32x4 *)y, num_tokens)));
+    } else {
+        int8_dequant_wave<<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(codes, scales, y, num_tokens,
+                                                                                    head_dim);
+    }
+    return launch_status("kvq_dequant_int8_token");
+}
+
+extern "C" int kvq_quant_fp8_token(const float *x, int8_t *codes, float *scales, uint32_t num_tokens,
+                                   uint32_t head_dim, void *stream) {
+    return kvq_quant_int8_token(x, codes, scales, num_tokens, head_dim, stream);
+}
+
+extern "C" int kvq_dequant_fp8_token(const int8_t *codes, const float *scales, float *y, uint32_t num_tokens,
+                                     uint32_t head_dim, void *stream) {
+    return kvq_dequant_int8_token(codes, scales, y, num_tokens, head_dim, stream);
+}
+
+extern "C" int kvq_quant_int4_group(const float *x, uint8_t *packed, float *scales, float *zeros,
+                                    uint32_t num_tokens, uint32_t head_dim, uint32_t group_size, void *stream) {
+    int st = check_int4("kvq_quant_int4_group", x, packed, scales, zeros, num_tokens, head_dim, group_size);
+    if (st) return st;
+    const uint64_t groups = (uint64_t)num_tokens * head_dim / group_size;
+    const int L = team_lanes(group_size);
+    hipStream_t s = as_stream(stream);
+    if (L) {
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int4_quant_team<LL, kUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
+                               (const f32x4 *)x, (uint16_t *)packed, scales, zeros, groups)));
+    } else {
+        int4_quant_wave<<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(x, packed, scales, zeros, groups,
+                                                                              group_size);
+    }
+    return launch_status("kvq_quant_int4_group");
+}
+
+extern "C" int kvq_dequant_int4_group(const uint8_t *packed, const float *scales, const float *zeros, float *y,
+                                      uint32_t num_tokens, uint32_t head_dim, uint32_t group_size, void *stream) {
+    int st = check_int4("kvq_dequant_int4_group", packed, scales, zeros, y, num_tokens, head_dim, group_size);
+    if (st) return st;
+    const uint64_t groups = (uint64_t)num_tokens * head_dim / group_size;
+    const int L = team_lanes(group_size);
+    hipStream_t s = as_stream(stream);
+    if (L) {
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int4_dequant_team<LL, kUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
+                               (const uint16_t *)packed, scales, zeros, (f32x4 *)y, groups)));
+    } else {
+        int4_dequant_wave<<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(packed, scales, zeros, y, groups,
+                                                                                group_size);
+    }
+    return launch_status("kvq_dequant_int4_group");
+}

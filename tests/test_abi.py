@@ -1,0 +1,152 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects every contract violation on the host before any
+HIP call (so these run without a GPU)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from kv_quantization_amd import _lib
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "kvq.h"
+
+# Every call below breaks the contract, so it returns before any HIP call and
+# the fake addresses are never used on a device.
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+MISALIGNED = 0x10004
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_parses_and_library_exports_every_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 17, names
+    for n in names:
+        assert hasattr(lib, n), f"libkvq.so does not export {n}"
+    assert set(names) == set(_lib.SIGNATURES) | {"kvq_last_error", "kvq_abi_version"}
+    assert lib.kvq_abi_version() == 100
+
+
+def _err(lib, name, *args):
+    st = getattr(lib, name)(*args)
+    return st, lib.kvq_last_error().decode()
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((0, FAKE, FAKE, 4, 8, None), "null"),
+    ((MISALIGNED, FAKE, FAKE, 4, 8, None), "aligned"),
+    ((FAKE, FAKE, FAKE, 0, 8, None), "num_tokens=0"),
+    ((FAKE, FAKE, FAKE, 4, 0, None), "head_dim=0"),
+])
+def test_kv_int8_validation(lib, args, frag):
+    for fn in ("kvq_quant_int8_token", "kvq_dequant_int8_token", "kvq_quant_fp8_token", "kvq_dequant_fp8_token"):
+        st, msg = _err(lib, fn, *args)
+        assert st == _lib.KVQ_E_INVALID and frag in msg, (fn, msg)
+
+
+# Only invalid argument sets here: a valid one would launch on fake pointers.
+@pytest.mark.parametrize("t,d,gs", [(4, 8, 3), (4, 8, 0), (3, 5, 4), (3, 6, 4), (1, 1, 2)])
+def test_kv_int4_group_validation(lib, t, d, gs):
+    st, msg = _err(lib, "kvq_quant_int4_group", FAKE, FAKE, FAKE, FAKE, t, d, gs, None)
+    assert st == _lib.KVQ_E_INVALID and "group_size" in msg
+
+
+def test_kv_int4_null_and_alignment(lib):
+    assert _err(lib, "kvq_dequant_int4_group", FAKE, FAKE, 0, FAKE, 4, 8, 4, None)[0] == _lib.KVQ_E_INVALID
+    assert _err(lib, "kvq_dequant_int4_group", FAKE, FAKE, MISALIGNED, FAKE, 4, 8, 4, None)[0] == _lib.KVQ_E_INVALID
+
+
+@pytest.mark.parametrize("kind,silu,up,ldx,rows,k,frag", [
+    (0, 0, 0, 128, 0, 128, "rows"),
+    (0, 0, 0, 128, 257, 128, "rows"),
+    (1, 0, 0, 256, 4, 200, "K=200"),
+    (0, 0, 0, 120, 4, 128, "ldx=120"),
+    (0, 0, 0, 132, 4, 128, "ldx=132"),
+    (0, 0, FAKE, 128, 4, 128, "up is only used with silu"),
+    (2, 0, 0, 128, 4, 128, "scale kind"),
+])
+def test_act_quant_validation(lib, kind, silu, up, ldx, rows, k, frag):
+    st, msg = _err(lib, "w8a8_act_quant", kind, silu, FAKE, up or None, ldx, rows, k, FAKE, FAKE, None)
+    assert st == _lib.KVQ_E_INVALID and frag in msg, msg
+
+
+def test_scratch_bytes_follow_the_scratch_rule(lib):
+    qb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.w8a8_scratch_bytes(0, 256, 4096, ctypes.byref(qb), ctypes.byref(sb)) == 0
+    assert (qb.value, sb.value) == (256 * 4096, 256 * 4)
+    assert lib.w8a8_scratch_bytes(1, 64, 14336, ctypes.byref(qb), ctypes.byref(sb)) == 0
+    assert (qb.value, sb.value) == (64 * 14336, 64 * 112 * 4)
+
+
+def test_weight_quant_and_cast_validation(lib):
+    assert _err(lib, "w8a8_weight_quant", 0, FAKE, 16, 100, FAKE, FAKE, None)[0] == _lib.KVQ_E_INVALID
+    assert _err(lib, "w8a8_weight_quant", 1, FAKE, 0, 128, FAKE, FAKE, None)[0] == _lib.KVQ_E_INVALID
+    assert _err(lib, "kvq_f32_to_e4m3", FAKE, FAKE, 0, None)[0] == _lib.KVQ_E_INVALID
+    assert _err(lib, "kvq_f32_to_e4m3", MISALIGNED, FAKE, 8, None)[0] == _lib.KVQ_E_INVALID
+
+
+def _segs(*specs):
+    arr = (_lib.W8a8Segment * 3)()
+    for i, (w, s, n) in enumerate(specs):
+        arr[i].w, arr[i].scale, arr[i].n = w, s, n
+    return arr
+
+
+@pytest.mark.parametrize("kind,rows,k,specs,nseg,ldc,frag", [
+    (0, 0, 128, [(FAKE, FAKE, 16)], 1, 16, "rows"),
+    (0, 257, 128, [(FAKE, FAKE, 16)], 1, 16, "rows"),
+    (0, 4, 100, [(FAKE, FAKE, 16)], 1, 16, "K=100"),
+    (0, 4, 128, [(FAKE, FAKE, 16)], 0, 16, "segments"),
+    (0, 4, 128, [(FAKE, FAKE, 16)] * 3, 4, 64, "segments"),
+    (0, 4, 128, [(FAKE, FAKE, 0)], 1, 16, "empty"),
+    (0, 4, 128, [(0, FAKE, 16)], 1, 16, "empty"),
+    (0, 4, 128, [(FAKE, FAKE, 24), (FAKE, FAKE, 16)], 2, 64, "not a multiple of 16"),
+    (1, 4, 128, [(FAKE, FAKE, 64), (FAKE, FAKE, 128)], 2, 256, "not a multiple of 128"),
+    (0, 4, 128, [(FAKE, FAKE, 32), (FAKE, FAKE, 16)], 2, 40, "ldc=40"),
+    (0, 4, 128, [(MISALIGNED, FAKE, 16)], 1, 16, "aligned"),
+])
+def test_gemv_validation(lib, kind, rows, k, specs, nseg, ldc, frag):
+    st, msg = _err(lib, "w8a8_gemv", kind, FAKE, FAKE, rows, k, _segs(*specs), nseg, FAKE, ldc, None, 0, None)
+    assert st == _lib.KVQ_E_INVALID and frag in msg, msg
+
+
+def _proj(qw=FAKE, s=FAKE, z=FAKE, o=FAKE, n=64):
+    p = _lib.Int4AwqProj()
+    p.qweight, p.scales, p.zeros, p.out, p.n = qw, s, z, o, n
+    return p
+
+
+@pytest.mark.parametrize("m,k,gs,q,kv,frag", [
+    (0, 256, 128, _proj(), None, "m == 0"),
+    (1, 256, 96, _proj(), None, "group_size"),
+    (1, 200, 128, _proj(), None, "K=200"),
+    (1, 256, 128, _proj(n=60), None, "n=60"),
+    (1, 256, 128, _proj(qw=0), None, "null"),
+    (1, 256, 128, _proj(o=MISALIGNED), None, "aligned"),
+    (1, 256, 128, _proj(), (_proj(n=32), _proj(n=64)), "differ"),
+    (1, 256, 128, _proj(), (_proj(), None), "both"),
+])
+def test_int4_validation(lib, m, k, gs, q, kv, frag):
+    kp = ctypes.byref(kv[0]) if kv and kv[0] is not None else None
+    vp = ctypes.byref(kv[1]) if kv and kv[1] is not None else None
+    st, msg = _err(lib, "int4_awq_qkv_gemm", FAKE, m, k, gs, ctypes.byref(q), kp, vp, None, 0, None)
+    assert st == _lib.KVQ_E_INVALID and frag in msg, msg
+
+
+def test_workspace_sizes(lib):
+    b = ctypes.c_size_t()
+    assert lib.int4_awq_workspace_bytes(1, 4096, 128, 6144, ctypes.byref(b)) == 0
+    assert b.value > 0          # small M slices K across workgroups
+    assert lib.int4_awq_workspace_bytes(1, 512, 128, 512, ctypes.byref(b)) == 0
+    assert b.value == 0         # tiny problem: one workgroup per tile
+    assert lib.w8a8_gemv_workspace_bytes(0, 8, 4096, 6144, ctypes.byref(b)) == 0

@@ -1,0 +1,117 @@
+"""GPU parity: INT4 AWQ fused Q/K/V GEMV/GEMM vs the oracle's fp64 definition,
+|gpu - ref| <= 1e-3 * sum|x||w| per output, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import print_case
+from gpu_util import assert_canary, dev, host, poisoned
+from kv_quantization_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-3
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _bind_oracle(oracle_mod):
+    global _oracle
+    _oracle = oracle_mod
+
+
+def _run(x, projs, gs, use_workspace=True):
+    m = x.shape[0]
+    outs, raws = [], []
+    for p in projs:
+        n = p.qweight.shape[1] * 8
+        o, raw = poisoned((m, n), torch.float32)
+        outs.append(o)
+        raws.append((raw, m * n * 4))
+    api.int4_awq_qkv(dev(x), [(dev(p.qweight), dev(p.scales), dev(p.zeros)) for p in projs], gs, outs=outs,
+                     use_workspace=use_workspace)
+    torch.cuda.synchronize()
+    for raw, nb in raws:
+        assert_canary(raw, nb)
+    return [host(o) for o in outs]
+
+
+def _check(x, projs, gs, got, what):
+    refs = _oracle.int4_awq_qkv(x, [(p.qweight, p.scales, p.zeros) for p in projs], gs)
+    worst = 0.0
+    for (ref, bound), g in zip(refs, got):
+        ratio = np.abs(g.astype(np.float64) - ref) / np.maximum(bound, 1e-300)
+        worst = max(worst, float(ratio.max()))
+    print(f"{what}: max |err|/sum|x||w| = {worst:.3e}", flush=True)
+    assert worst <= RTOL, what
+
+
+def test_single_projection_512():
+    print_case("int4 single 512")
+    x, projs = synth.int4_gemv_512()
+    _check(x, projs, 128, _run(x, projs, 128), "C1")
+
+
+@pytest.mark.parametrize("m", [1, 16, 128])
+def test_fused_qkv_8b(m):
+    print_case("int4 qkv 8b", m)
+    x, projs = synth.int4_qkv()
+    _check(x[:m], projs, 128, _run(x[:m], projs, 128), f"qkv M={m}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 16, 17, 31, 32, 33, 64, 100, 256])
+@pytest.mark.parametrize("gs", [32, 64, 128, 256])
+def test_shapes(m, gs):
+    print_case("int4 shapes", m, gs)
+    k = 512
+    x, projs = synth.int4_awq(m, k, (136, 24, 24), gs, seed=700 + m + gs)
+    _check(x, projs, gs, _run(x, projs, gs), f"m={m} gs={gs}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 40])
+def test_without_workspace_same_bits_order_independent(m):
+    print_case("int4 workspace vs none", m)
+    x, projs = synth.int4_awq(m, 2048, (1024, 256, 256), 128, seed=800 + m)
+    a = _run(x, projs, 128, use_workspace=True)
+    b = _run(x, projs, 128, use_workspace=False)
+    _check(x, projs, 128, a, f"ws m={m}")
+    _check(x, projs, 128, b, f"nows m={m}")
+    # repeated calls reuse the workspace (left zero-filled): same bits again
+    c = _run(x, projs, 128, use_workspace=True)
+    for u, v in zip(a, c):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_single_is_q_part_of_fused():
+    print_case("int4 single vs fused")
+    x, projs = synth.int4_awq(3, 256, (64, 16, 16), 128, seed=900)
+    fused = _run(x, projs, 128)
+    single = _run(x, projs[:1], 128)
+    np.testing.assert_array_equal(fused[0], single[0])
+
+
+def test_degenerate_scales_zeros():
+    print_case("int4 degenerate")
+    rng = np.random.default_rng(901)
+    x, projs = synth.int4_awq(4, 256, (64,), 64, seed=902)
+    p = projs[0]
+    codes = _oracle.awq_unpack(p.qweight, 64)
+    # zero == code within each group -> exactly zero output
+    z = codes.reshape(4, 64, 64)[:, 0, :].astype(np.float32)
+    codes[:] = np.repeat(z.astype(np.uint8), 64, axis=0)
+    p.qweight = _oracle.awq_pack(codes)
+    p.zeros = z
+    got = _run(x, [p], 64)
+    # The kernel sums s * (P - z*X) with P = sum x~ q and X = sum x~ in fp32, so
+    # a cancellation leaves a residual bounded by a few ulps of
+    # s * (sum |x~| q + |z| sum |x~|) per group (not by sum |x||w|, which is 0).
+    xa = np.abs(x.astype(np.float16).astype(np.float64))
+    per_group = [(xa[:, g * 64:(g + 1) * 64] @ codes[g * 64:(g + 1) * 64].astype(np.float64)
+                  + xa[:, g * 64:(g + 1) * 64].sum(axis=1, keepdims=True) * np.abs(z[g]))
+                 * p.scales[g].astype(np.float64) for g in range(4)]
+    cancel_bound = 2.0 ** -24 * 70 * np.sum(per_group, axis=0)
+    assert np.all(np.abs(got[0]) <= cancel_bound)
+    # unit scales, zero offsets, small-integer x: exact integer results
+    xi = rng.integers(-8, 8, (4, 256)).astype(np.float32)
+    p.scales = np.ones_like(p.scales)
+    p.zeros = np.zeros_like(p.zeros)
+    got = _run(xi, [p], 64)
+    np.testing.assert_array_equal(got[0], (xi.astype(np.int64) @ codes.astype(np.int64)).astype(np.float32))

@@ -1,0 +1,144 @@
+"""GPU parity: W8A8 FP8 GEMV/GEMM (w8a8_gemv, w8a8_proj) vs the oracle's fp64
+definition, |gpu - ref| <= 1e-3 * sum|a||w| per output, through the C ABI.
+
+The activations and weights given to both sides are the oracle's quantized
+codes (their bit-exact parity with the HIP quantizers is tested separately)."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import print_case
+from gpu_util import assert_canary, dev, host, poisoned
+from kv_quantization_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-3
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _bind_oracle(oracle_mod):
+    global _oracle
+    _oracle = oracle_mod
+
+
+def _weights(kind, ws):
+    segs = [_oracle.weight_quant(kind, w) for w in ws]
+    return segs, api.W8a8Weight(kind, [(dev(q), dev(s)) for q, s in segs])
+
+
+def _half_ulp_bf16(v):
+    """Half a bf16 ulp at |v| (8 significant bits): the rounding any bf16 output carries."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 8)
+
+
+def _check(out_bf16, ref, bound, what, strict=False):
+    """|gpu - ref| <= 1e-3 * sum|a||w| + half a bf16 ulp of the result (the output
+    format's own rounding).  strict: also without the bf16 allowance, which holds
+    at the workload shapes (large K, |y| << sum|a||w|)."""
+    got = _oracle.bf16_to_f32(out_bf16).astype(np.float64)
+    err = np.abs(got - ref)
+    ratio = err / np.maximum(bound, 1e-300)
+    worst = float(ratio.max())
+    print(f"{what}: max |err|/sum|a||w| = {worst:.3e}", flush=True)
+    over = err > RTOL * bound + _half_ulp_bf16(ref)
+    assert not over.any(), f"{what}: {int(over.sum())} outputs beyond tolerance, worst ratio {worst:.3e}"
+    if strict:
+        assert worst <= RTOL, f"{what}: {int((ratio > RTOL).sum())} outputs beyond 1e-3, worst {worst:.3e}"
+
+
+def _case(kind, x_bf16, k, ws, rows, silu=False, up=None, ldc_pad=0, what="", strict=False):
+    segs, weight = _weights(kind, ws)
+    q, sa = _oracle.act_quant(kind, x_bf16[:rows], k, silu=silu, up_bf16=None if up is None else up[:rows])
+    ref, bound = _oracle.w8a8_gemv(kind, q, sa, segs)
+    n = ref.shape[1]
+    ldc = n + ldc_pad
+    out, raw = poisoned((rows, ldc), torch.bfloat16)
+    api.gemv(dev(q), dev(sa), weight, out=out, ldc=ldc)
+    torch.cuda.synchronize()
+    o = host(out)
+    _check(o[:, :n], ref, bound, what, strict)
+    if ldc_pad:
+        assert np.all(o[:, n:].view(np.uint8) == 0xAA), "columns past N were written"
+    assert_canary(raw, rows * ldc * 2)
+    return o[:, :n]
+
+
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_rowscale_fused_qkv(m):
+    print_case("w8a8 rowscale qkv", m)
+    inp = synth.w8a8_qkv()
+    _case(0, inp.x_bf16, 4096, inp.weights, m, what=f"qkv M={m}", strict=True)
+
+
+_down = {}
+
+
+def _down_inputs():
+    if not _down:
+        inp = synth.w8a8_down()
+        segs, weight = _weights(1, inp.weights)
+        _down.update(inp=inp, segs=segs, weight=weight)
+    return _down
+
+
+@pytest.mark.parametrize("m", [64, 128, 256])
+def test_blk128_down_proj(m):
+    print_case("w8a8 blk128 down", m)
+    d = _down_inputs()
+    q, sa = _oracle.act_quant(1, d["inp"].x_bf16[:m], 14336, silu=True)
+    ref, bound = _oracle.w8a8_gemv(1, q, sa, d["segs"])
+    out = api.gemv(dev(q), dev(sa), d["weight"])
+    torch.cuda.synchronize()
+    _check(host(out), ref, bound, f"down M={m}", strict=True)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("rows", [1, 3, 16, 17, 33, 63, 64, 65, 100, 255, 256])
+def test_row_counts(kind, rows):
+    print_case("w8a8 rows", kind, rows)
+    seg_n = (48, 32, 21) if kind == 0 else (128, 256, 77)
+    inp = synth.w8a8(256, 384, seg_n, seed=300 + rows)
+    _case(kind, inp.x_bf16, 384, inp.weights, rows, ldc_pad=8, what=f"kind={kind} rows={rows}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("seg_n,k", [((1,), 128), ((7,), 256), ((16, 1), 128), ((128,), 128), ((64, 64, 64), 512),
+                                     ((2048,), 1024)])
+def test_segment_shapes(kind, seg_n, k):
+    if kind == 1 and any(n % 128 for n in seg_n[:-1]):
+        pytest.skip("BLK128 needs 128-aligned non-last segments")
+    print_case("w8a8 segments", kind, seg_n, k)
+    inp = synth.w8a8(70, k, seg_n, seed=400 + k + sum(seg_n))
+    for rows in (1, 9, 70):
+        _case(kind, inp.x_bf16, k, inp.weights, rows, what=f"kind={kind} segs={seg_n} rows={rows}")
+
+
+def test_segment_invariance_rowscale():
+    """Three segments give the same bits as one concatenated segment."""
+    print_case("w8a8 segment invariance")
+    inp = synth.w8a8(8, 512, (256, 128, 64), seed=500)
+    q, sa = _oracle.act_quant(0, inp.x_bf16, 512)
+    segs3, w3 = _weights(0, inp.weights)
+    w1 = api.W8a8Weight(0, [(dev(np.concatenate([s[0] for s in segs3])), dev(np.concatenate([s[1] for s in segs3])))])
+    a = host(api.gemv(dev(q), dev(sa), w3))
+    b = host(api.gemv(dev(q), dev(sa), w1))
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("kind,silu,with_up", [(0, False, False), (1, True, False), (1, True, True), (0, True, True)])
+def test_proj_equals_act_quant_then_gemv(kind, silu, with_up):
+    print_case("w8a8 proj", kind, silu, with_up)
+    inp = synth.w8a8(40, 1024, (256, 128), seed=600, with_up=with_up)
+    _, weight = _weights(kind, inp.weights)
+    x = dev(inp.x_bf16)
+    up = None if inp.up_bf16 is None else dev(inp.up_bf16)
+    q, sa = api.act_quant(x, 1024, kind, silu, up)
+    a = host(api.gemv(q, sa, weight))
+    b = host(api.proj(x, weight, silu=silu, up=up))
+    np.testing.assert_array_equal(a, b)
+    # and the proj output against the oracle chain
+    qo, so = _oracle.act_quant(kind, inp.x_bf16, 1024, silu=silu, up_bf16=inp.up_bf16)
+    np.testing.assert_array_equal(host(q), qo)
+    ref, bound = _oracle.w8a8_gemv(kind, qo, so, [_oracle.weight_quant(kind, w) for w in inp.weights])
+    _check(b, ref, bound, "proj")
