@@ -59,6 +59,15 @@ __device__ __forceinline__ int proj_of(const Projs &P, uint32_t gw) {
     return (P.count > 1 && gw >= P.wstart[1]) ? ((P.count > 2 && gw >= P.wstart[2]) ? 2 : 1) : 0;
 }
 
+// Agent-coherent (sc1) accesses for the partial tiles exchanged between
+// workgroups that may run on different XCDs (whose L2s are not coherent).
+__device__ __forceinline__ void store_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ f16x2 h2_bits(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ uint32_t h2_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 
@@ -242,36 +251,46 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
                 const uint32_t col = 8 * (gwo - P.wstart[po]) + (col4 & 1) * 4;
                 *reinterpret_cast<f32x4 *>(P.out[po] + (size_t)m * P.n[po] + col) = v;
             } else {
-                *reinterpret_cast<f32x4 *>(part + (size_t)s * (MR * 128) + (mt * 16 + row) * 128 + col4 * 4) = v;
+                float *dst = part + (size_t)s * (MR * 128) + (mt * 16 + row) * 128 + col4 * 4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) store_agent(dst + j, v[j]);
             }
         }
         __syncthreads();
     }
     if (ks_b == 1) return;
 
-    // cross-workgroup K reduction: the last workgroup of this tile finishes it
-    __threadfence();
+    // Cross-workgroup K reduction.  The partial tiles were written with
+    // agent-coherent stores (sc1, below); once every thread's stores have
+    // completed, one atomic per workgroup counts arrivals, and the last
+    // workgroup of the tile reads all partials with agent-coherent loads,
+    // adds them in split order (so the result does not depend on arrival
+    // order) and resets the counter for the next call.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(&counters[tile_id], 1u);
+        const uint32_t prev = __hip_atomic_fetch_add(&counters[tile_id], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == ks_b - 1;
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     for (int e = threadIdx.x; e < MR * 32; e += kBlock) {
         const int row = e >> 5, col4 = e & 31;
         const uint32_t m = c * MR + row;
         const uint32_t gwo = t * 16 + (col4 >> 1);
         if (m >= M || gwo >= P.wtotal) continue;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        for (uint32_t q = 0; q < ks_b; ++q)
-            v += *reinterpret_cast<const f32x4 *>(part + (size_t)q * (MR * 128) + row * 128 + col4 * 4);
+        for (uint32_t q = 0; q < ks_b; ++q) {
+            const float *src = part + (size_t)q * (MR * 128) + row * 128 + col4 * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] += load_agent(src + j);
+        }
         const int po = proj_of(P, gwo);
         const uint32_t col = 8 * (gwo - P.wstart[po]) + (col4 & 1) * 4;
         *reinterpret_cast<f32x4 *>(P.out[po] + (size_t)m * P.n[po] + col) = v;
     }
-    if (threadIdx.x == 0) counters[tile_id] = 0u;
+    if (threadIdx.x == 0) __hip_atomic_store(&counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ host --

@@ -8,14 +8,14 @@
 // threads over <=128-row chunks, re-streaming the weights per chunk.  Here
 // every call is one launch over all (<=256) rows:
 //
-//   * rows <= 64  "skinny": a workgroup owns 16 output columns; its 4 waves
+//   * rows <= 32  "skinny": a workgroup owns 16 output columns; its 4 waves
 //     split K, each streaming 16 weight rows with 16-byte loads straight into
 //     MFMA operands (v_mfma_scale_f32_16x16x128_f8f6f4, unit E8M0 scales, so
 //     one instruction is one 128-wide scale block) and the activation rows
 //     as the other operand; partial sums meet in LDS.
-//   * rows > 64   "tiled": 64x64 output tiles, activation and weight tiles
-//     staged through padded LDS rows (conflict-free 16-byte reads), double
-//     buffered so the next K block's global loads overlap the MFMAs.
+//   * rows > 32   "wide": all rows x 128 columns per workgroup over a slice
+//     of K, both tiles staged through a 3-stage LDS ring with direct
+//     global->LDS loads; split-K partials are added by a second kernel.
 //
 // Operand layout: for a 16x16x128 fp8 MFMA, lane l supplies row (l % 16) of
 // A (or column (l % 16) of B) and 32 bytes of K.  Lane l carries K bytes
@@ -186,144 +186,239 @@ __global__ __launch_bounds__(kBlock) void w8a8_skinny(const uint8_t *__restrict_
     }
 }
 
-// -------------------------------------------------------------- tiled ---
+// --------------------------------------------------------------- wide ---
+//
+// rows > 32: one workgroup owns all (<= 256) activation rows and 128 output
+// columns over one slice of K (split-K), so the weight tile is read from HBM
+// once per call and the activation tile (re-read by every column tile) comes
+// from L2.  2x2 waves, each (rows/2) x 64.  Each 128-wide K step of both
+// tiles (and the 128-column activation block scales) travels global -> LDS
+// with gfx950's direct loads (global_load_lds_dwordx4: lane i's 16 bytes land
+// at LDS base + 16*i), through a 3-stage ring so two K steps are in flight
+// while the third is multiplied.  Rows are stored with their eight 16-byte
+// chunks XOR-swizzled by (row & 7), which keeps both the load pattern and the
+// MFMA operand reads (ds_read_b128) free of bank conflicts.  With split-K the
+// fp32 partial tiles go to the workspace and w8a8_reduce adds them in split
+// order (deterministic), applies per-row scales and writes bf16.
 
-constexpr int kTile = 64;                 // output tile 64 x 64
-constexpr int kLdsRow = 144;              // 128 bytes of K + 16 bytes pad
+constexpr int kWideN = 128;
+constexpr int kStages = 3;
 
-// KIND 0 per-row, 1 block scales.  grid (ceil(N/64), ceil(rows/64)).
-template <int KIND>
-__global__ __launch_bounds__(kBlock) void w8a8_tiled(const uint8_t *__restrict__ q, const float *__restrict__ sa,
-                                                     uint32_t rows, uint32_t K, Segs S, uint16_t *__restrict__ out,
-                                                     uint32_t ldc) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTile * kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTile * kLdsRow];
+// LDS byte offset of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Direct global->LDS loads, written as inline assembly so that the compiler
+// does not add its conservative "all LDS DMA complete" wait before every LDS
+// read; the ring below waits explicitly (wait_vm) for exactly the stage it
+// is about to read.  lds_wave_base must be wave-uniform (it goes to M0); lane
+// i's data lands at lds_wave_base + i * size.
+__device__ __forceinline__ void lds_load16(const void *g, uint32_t lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void *g, uint32_t lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int MTW, int KIND>
+struct WideCfg {
+    static constexpr int BM = 32 * MTW;
+    static constexpr int A_BYTES = BM * 128;
+    static constexpr int B_BYTES = kWideN * 128;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_INSTR = BM / 32;      // 1 KiB loads per wave for A
+    static constexpr int B_INSTR = 4;            // and for B (128 rows x 128 B / 4 waves)
+    static constexpr int N_INSTR = A_INSTR + B_INSTR + (KIND == 1 ? 2 : 0);
+};
+
+template <int MTW, int KIND>
+__global__ __launch_bounds__(kBlock) void w8a8_wide(const uint8_t *__restrict__ q, const float *__restrict__ sa,
+                                                    uint32_t rows, uint32_t K, Segs S, uint16_t *__restrict__ out,
+                                                    uint32_t ldc, uint32_t splits, uint32_t ntiles,
+                                                    float *__restrict__ partials) {
+    using C = WideCfg<MTW, KIND>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * C::STAGE];
+    __shared__ __attribute__((aligned(16))) float lds_sa[kStages][4][64];
+    __shared__ __attribute__((aligned(16))) float lds_sw[kStages][4][64];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;            // wave's 32x32 sub-tile
+    const int wm = wv >> 1, wn = wv & 1;
     const int r16 = lane & 15, g = lane >> 4;
-    const uint32_t n0 = blockIdx.x * kTile, m0 = blockIdx.y * kTile;
+    const uint32_t tile = blockIdx.x % ntiles, split = blockIdx.x / ntiles;
+    const uint32_t n0 = tile * kWideN;
     const uint32_t nkb = K / 128;
+    const uint32_t kb0 = (uint32_t)((uint64_t)split * nkb / splits);
+    const uint32_t kb1 = (uint32_t)((uint64_t)(split + 1) * nkb / splits);
+    const int nks = (int)(kb1 - kb0);
 
-    // global -> LDS assignment: thread t moves 16-byte chunks c = t and t+256
-    // of each 64 x 128-byte tile: row c/8, column chunk c%8.
-    const uint8_t *ga[2];
-    const uint8_t *gb[2];
-    bool oka[2], okb[2];
-    int ldsoff[2];
+    // -- per-lane global sources for the direct loads (one row chunk each) --
+    // A: instruction j of wave w fills rows 8*(w*A_INSTR + j) .. +8; lane i
+    // holds LDS chunk slot i%8 of row 8*(...) + i/8, i.e. logical chunk
+    // (i%8) ^ (row & 7).
+    const uint8_t *asrc[C::A_INSTR];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = tid + h * kBlock;
-        const int row = c >> 3, col = (c & 7) * 16;
-        ldsoff[h] = row * kLdsRow + col;
-        const uint32_t m = m0 + row;
-        oka[h] = m < rows;
-        ga[h] = q + (size_t)(oka[h] ? m : 0) * K + col;
-        const uint32_t j = n0 + row;
-        okb[h] = j < S.ntotal;
-        const int sg = seg_of(S, okb[h] ? j : 0);
-        const uint32_t jl = (okb[h] ? j : 0) - S.start[sg];
-        okb[h] = okb[h] && jl < S.n[sg];
-        gb[h] = S.w[sg] + (size_t)(okb[h] ? jl : 0) * K + col;
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int row = 8 * (wv * C::A_INSTR + j) + (lane >> 3);
+        const int chunk = (lane & 7) ^ (row & 7);
+        const uint32_t m = (uint32_t)row < rows ? row : 0;      // rows past the end: any valid row
+        asrc[j] = q + (size_t)m * K + chunk * 16;
     }
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
-    u32x4 ra[2], rb[2];
-    auto gload = [&](uint32_t kb) {
+    const uint8_t *bsrc[C::B_INSTR];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            ra[h] = oka[h] ? *reinterpret_cast<const u32x4 *>(ga[h] + (size_t)kb * 128) : z4;
-            rb[h] = okb[h] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(gb[h] + (size_t)kb * 128))
-                           : z4;
+    for (int j = 0; j < C::B_INSTR; ++j) {
+        const int row = 8 * (wv * C::B_INSTR + j) + (lane >> 3);
+        const int chunk = (lane & 7) ^ (row & 7);
+        uint32_t jg = n0 + row;
+        int sg = seg_of(S, jg < S.ntotal ? jg : 0);
+        uint32_t jl = (jg < S.ntotal ? jg : 0) - S.start[sg];
+        if (jl >= S.n[sg]) { sg = 0; jl = 0; }               // past the end: any valid row
+        bsrc[j] = S.w[sg] + (size_t)jl * K + chunk * 16;
+    }
+    // activation block scales for K block kb: wave w loads rows w*BM/4 + lane
+    const float *ssrc = sa;
+    if (KIND == 1) {
+        const uint32_t m = (uint32_t)(wv * (C::BM / 4) + lane);
+        ssrc = sa + (size_t)(m < rows && lane < C::BM / 4 ? m : 0) * nkb;
+    }
+
+    const float *swp = sa;
+    if (KIND == 1) {
+        const int sgb = seg_of(S, n0);
+        swp = S.s[sgb] + (size_t)((n0 - S.start[sgb]) / 128) * nkb;
+    }
+
+    // wave-uniform LDS byte offsets (they go to M0)
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+    const uint32_t sa0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sa[0][0][0]));
+    const uint32_t sw0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sw[0][0][0]));
+    const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
+    auto issue = [&](int it) {
+        const uint32_t st = (uint32_t)(it % kStages);
+        const uint32_t kb = kb0 + it;
+        const uint32_t abase = lds0 + st * C::STAGE;
+        const uint32_t bbase = abase + C::A_BYTES;
+#pragma unroll
+        for (int j = 0; j < C::A_INSTR; ++j)
+            lds_load16(asrc[j] + (size_t)kb * 128, abase + (wvu * C::A_INSTR + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < C::B_INSTR; ++j)
+            lds_load16(bsrc[j] + (size_t)kb * 128, bbase + (wvu * C::B_INSTR + j) * 1024);
+        if (KIND == 1) {
+            lds_load4(ssrc + kb, sa0 + (st * 4 + wvu) * 256);
+            lds_load4(swp + kb, sw0 + (st * 4 + wvu) * 256);   // every lane: the tile's weight block scale
         }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            *reinterpret_cast<u32x4 *>(&lds_a[buf][ldsoff[h]]) = ra[h];
-            *reinterpret_cast<u32x4 *>(&lds_b[buf][ldsoff[h]]) = rb[h];
-        }
-    };
 
-    f32x4 acc[2][2];
+    f32x4 acc[MTW][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // block-scale bookkeeping: the 64-column tile lies in one 128-row band
-    // of one segment (BLK128 segments start at multiples of 128)
-    const int sg_blk = seg_of(S, n0);
-    const float *swp = S.s[sg_blk] + (size_t)((n0 - S.start[sg_blk]) / 128) * nkb;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (uint32_t kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nkb) gload(kb + 1);
-        i32x8 a[2], b[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint8_t *pa = &lds_a[buf][(wm * 32 + i * 16 + r16) * kLdsRow + g * 16];
-            const uint8_t *pb = &lds_b[buf][(wn * 32 + i * 16 + r16) * kLdsRow + g * 16];
-            const u32x4 alo = *reinterpret_cast<const u32x4 *>(pa), ahi = *reinterpret_cast<const u32x4 *>(pa + 64);
-            const u32x4 blo = *reinterpret_cast<const u32x4 *>(pb), bhi = *reinterpret_cast<const u32x4 *>(pb + 64);
-            a[i] = i32x8{(int)alo[0], (int)alo[1], (int)alo[2], (int)alo[3], (int)ahi[0], (int)ahi[1], (int)ahi[2],
-                         (int)ahi[3]};
-            b[i] = i32x8{(int)blo[0], (int)blo[1], (int)blo[2], (int)blo[3], (int)bhi[0], (int)bhi[1], (int)bhi[2],
-                         (int)bhi[3]};
-        }
-        if (KIND == 0) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma_fp8(a[i], b[j], acc[i][j]);
+    if (nks > 0) issue(0);
+    if (nks > 1) issue(1);
+    for (int it = 0; it < nks; ++it) {
+        if (it + 2 < nks) {
+            issue(it + 2);
+            wait_vm<2 * C::N_INSTR>();
+        } else if (it + 1 < nks) {
+            wait_vm<C::N_INSTR>();
         } else {
-            const float swb = swp[kb];
+            wait_vm<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        const int st = it % kStages;
+        const uint8_t *abase = lds + st * C::STAGE;
+        const uint8_t *bbase = abase + C::A_BYTES;
+        i32x8 b[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                float sab[4];
+        for (int nt = 0; nt < 4; ++nt) {
+            const int row = wn * 64 + nt * 16 + r16;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(bbase + row * 128 + ((g ^ (row & 7)) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(bbase + row * 128 + (((g + 4) ^ (row & 7)) << 4));
+            b[nt] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+        const float swk = KIND == 1 ? lds_sw[st][wv][0] : 1.0f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t m = m0 + wm * 32 + i * 16 + 4 * g + e;
-                    sab[e] = (m < rows ? sa[(size_t)m * nkb + kb] : 0.0f) * swb;
-                }
+        for (int mt = 0; mt < MTW; ++mt) {
+            const int row = wm * 16 * MTW + mt * 16 + r16;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(abase + row * 128 + ((g ^ (row & 7)) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(abase + row * 128 + (((g + 4) ^ (row & 7)) << 4));
+            const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            if (KIND == 0) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const f32x4 p = mfma_fp8(a[i], b[j], f32x4{0.f, 0.f, 0.f, 0.f});
+                for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_fp8(a, b[nt], acc[mt][nt]);
+            } else {
+                // rows 4g..4g+3 of this M tile: one 16-byte read of the staged scales
+                const int r0 = wm * 16 * MTW + mt * 16 + 4 * g;
+                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&lds_sa[st][r0 / (C::BM / 4)][r0 % (C::BM / 4)]);
+                const f32x4 sc = s4 * swk;
+                f32x4 p[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[e], sab[e], acc[i][j][e]);
-                }
+                for (int nt = 0; nt < 4; ++nt) p[nt] = mfma_fp8(a, b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[mt][nt][e] = __builtin_fmaf(p[nt][e], sc[e], acc[mt][nt][e]);
             }
         }
-        if (kb + 1 < nkb) {
-            lstore(buf ^ 1);
-            __syncthreads();
-        }
+        __builtin_amdgcn_s_barrier();   // this stage is refilled by the issue() two iterations on
     }
 
-    // epilogue
+    // ---- epilogue: bf16 output (no split) or fp32 partial tile
+    float *part = partials + (size_t)split * rows * S.ntotal;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint32_t col = n0 + wn * 32 + j * 16 + r16;
+    for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t col = n0 + wn * 64 + nt * 16 + r16;
         if (col >= S.ntotal) continue;
         const int sg = seg_of(S, col);
         const uint32_t jl = col - S.start[sg];
         if (jl >= S.n[sg]) continue;
-        const float sw = KIND == 0 ? S.s[sg][jl] : 1.0f;
+        const float sw = (KIND == 0 && splits == 1) ? S.s[sg][jl] : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t m = m0 + wm * 32 + i * 16 + 4 * g + e;
-                if (m < rows) {
-                    const float y = KIND == 0 ? acc[i][j][e] * sa[m] * sw : acc[i][j][e];
+                const uint32_t m = wm * 16 * MTW + mt * 16 + 4 * g + e;
+                if (m >= rows) continue;
+                if (splits == 1) {
+                    const float y = KIND == 0 ? acc[mt][nt][e] * sa[m] * sw : acc[mt][nt][e];
                     out[(size_t)m * ldc + col] = bf16_rne(y);
+                } else {
+                    part[(size_t)m * S.ntotal + col] = acc[mt][nt][e];
                 }
             }
         }
     }
+}
+
+// Sum the split-K partials [splits][rows][N] in split order, scale (per-row
+// kind), round to bf16.  One thread per output element.
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void w8a8_reduce(const float *__restrict__ partials, uint32_t splits,
+                                                      const float *__restrict__ sa, uint32_t rows, Segs S,
+                                                      uint16_t *__restrict__ out, uint32_t ldc) {
+    const uint64_t idx = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t total = (uint64_t)rows * S.ntotal;
+    if (idx >= total) return;
+    const uint32_t m = (uint32_t)(idx / S.ntotal), col = (uint32_t)(idx % S.ntotal);
+    float v = 0.0f;
+    for (uint32_t s = 0; s < splits; ++s) v += partials[(size_t)s * total + idx];
+    if (KIND == 0) {
+        const int sg = seg_of(S, col);
+        v = v * sa[m] * S.s[sg][col - S.start[sg]];
+    }
+    out[(size_t)m * ldc + col] = bf16_rne(v);
 }
 
 // --------------------------------------------------------------- host ---
@@ -368,29 +463,72 @@ int check_gemv(const char *fn, w8a8_scale_t kind, const uint8_t *q, const float 
     return KVQ_OK;
 }
 
+struct WidePlan {
+    uint32_t mtw, ntiles, splits;
+    size_t ws_bytes;
+};
+
+// rows > 32: all rows per workgroup (MTW = ceil(rows/32) 16-row tiles per
+// wave), 128-column tiles, and enough K slices to give ~256 workgroups.
+WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
+    WidePlan p;
+    p.mtw = (rows + 31) / 32;
+    p.ntiles = (ntotal + kWideN - 1) / kWideN;
+    const uint32_t nkb = k / 128;
+    uint32_t sp = 256 / (p.ntiles ? p.ntiles : 1);
+    if (sp > nkb) sp = nkb;
+    if (sp < 1) sp = 1;
+    p.splits = sp;
+    p.ws_bytes = sp > 1 ? (size_t)sp * rows * ntotal * sizeof(float) : 0;
+    return p;
+}
+
 int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint32_t rows, uint32_t k, const Segs &S,
-                uint16_t *out, uint32_t ldc, hipStream_t s) {
-    if (rows <= 64) {
+                uint16_t *out, uint32_t ldc, void *workspace, size_t workspace_bytes, hipStream_t s) {
+    if (rows <= 32) {
         const unsigned grid = (S.ntotal + 15) / 16;
-        const int mt = (rows + 15) / 16;
-#define KVQ_SKINNY(MT)                                                                                        \
-    do {                                                                                                      \
-        if (kind == W8A8_ROWSCALE) w8a8_skinny<MT, 0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc); \
-        else w8a8_skinny<MT, 1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);                  \
-    } while (0)
-        switch (mt) {
-            case 1: KVQ_SKINNY(1); break;
-            case 2: KVQ_SKINNY(2); break;
-            case 3: KVQ_SKINNY(3); break;
-            default: KVQ_SKINNY(4); break;
+        if (rows <= 16) {
+            if (kind == W8A8_ROWSCALE) w8a8_skinny<1, 0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+            else w8a8_skinny<1, 1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+        } else {
+            if (kind == W8A8_ROWSCALE) w8a8_skinny<2, 0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+            else w8a8_skinny<2, 1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
         }
-#undef KVQ_SKINNY
-    } else {
-        const dim3 grid((S.ntotal + kTile - 1) / kTile, (rows + kTile - 1) / kTile);
-        if (kind == W8A8_ROWSCALE) w8a8_tiled<0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
-        else w8a8_tiled<1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+        return launch_status("w8a8_gemv");
     }
-    return launch_status("w8a8_gemv");
+    WidePlan pl = wide_plan(rows, k, S.ntotal);
+    float *partials = nullptr;
+    if (pl.splits > 1) {
+        if (workspace && workspace_bytes >= pl.ws_bytes && aligned16(workspace)) partials = static_cast<float *>(workspace);
+        else pl.splits = 1;
+    }
+    const unsigned grid = pl.ntiles * pl.splits;
+#define KVQ_WIDE(MTW)                                                                                           \
+    do {                                                                                                        \
+        if (kind == W8A8_ROWSCALE)                                                                              \
+            w8a8_wide<MTW, 0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles,  \
+                                                      partials);                                                \
+        else                                                                                                    \
+            w8a8_wide<MTW, 1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles,  \
+                                                      partials);                                                \
+    } while (0)
+    switch (pl.mtw) {
+        case 2: KVQ_WIDE(2); break;
+        case 3: KVQ_WIDE(3); break;
+        case 4: KVQ_WIDE(4); break;
+        case 5: KVQ_WIDE(5); break;
+        case 6: KVQ_WIDE(6); break;
+        case 7: KVQ_WIDE(7); break;
+        default: KVQ_WIDE(8); break;
+    }
+#undef KVQ_WIDE
+    int st = launch_status("w8a8_gemv");
+    if (st || pl.splits == 1) return st;
+    const uint64_t total = (uint64_t)rows * S.ntotal;
+    const unsigned rgrid = (unsigned)((total + kBlock - 1) / kBlock);
+    if (kind == W8A8_ROWSCALE) w8a8_reduce<0><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+    else w8a8_reduce<1><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+    return launch_status("w8a8_gemv (split-K reduction)");
 }
 
 }  // namespace
@@ -407,19 +545,17 @@ using namespace kvq;
 extern "C" int w8a8_gemv(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint32_t rows, uint32_t k,
                          const w8a8_segment_t *segs, uint32_t nseg, uint16_t *out, uint32_t ldc, void *workspace,
                          size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     Segs S;
     int st = check_gemv("w8a8_gemv", kind, q, a_scales, rows, k, segs, nseg, out, ldc, &S);
     if (st) return st;
-    return gemv_launch(kind, q, a_scales, rows, k, S, out, ldc, as_stream(stream));
+    return gemv_launch(kind, q, a_scales, rows, k, S, out, ldc, workspace, workspace_bytes, as_stream(stream));
 }
 
 extern "C" int w8a8_gemv_workspace_bytes(w8a8_scale_t kind, uint32_t rows, uint32_t k, uint32_t n_total,
                                          size_t *bytes) {
-    (void)kind; (void)rows; (void)k; (void)n_total;
+    (void)kind;
     if (!bytes) return fail(KVQ_E_INVALID, "w8a8_gemv_workspace_bytes: null output pointer");
-    *bytes = 0;
+    *bytes = (rows > 32 && rows <= W8A8_MAX_ROWS && k >= 128) ? wide_plan(rows, k, n_total).ws_bytes : 0;
     return KVQ_OK;
 }
 
@@ -434,7 +570,5 @@ extern "C" int w8a8_proj(w8a8_scale_t kind, int silu, const uint16_t *x, const u
     if (st) return st;
     st = act_quant_launch(kind, silu, x, up, ldx, rows, k, q, a_scales, as_stream(stream));
     if (st) return st;
-    (void)workspace;
-    (void)workspace_bytes;
-    return gemv_launch(kind, q, a_scales, rows, k, S, out, ldc, as_stream(stream));
+    return gemv_launch(kind, q, a_scales, rows, k, S, out, ldc, workspace, workspace_bytes, as_stream(stream));
 }
