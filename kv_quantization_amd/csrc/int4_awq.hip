@@ -5,105 +5,102 @@
 // 20, 8, 24, 12, 28) and fused_int4_qkv_q / _k / _v (out[m][j] = sum_k
 // x[m][k] * (q - zero[k/gs][j]) * scale[k/gs][j], weights [K][n/8], fp32
 // scales and zeros [K/gs][n]).  The page runs three dispatches of one thread
-// per output with a serial K loop; here Q, K and V are one launch over the
-// concatenated word columns, and the sum runs on the matrix cores:
+// per output with a serial K loop; here Q, K and V are one launch, and the
+// sums run on the matrix cores:
 //
 //   out = sum_g s_g * (P_g - z_g * X_g),  P_g = sum_{k in g} x~_k * q_k,
 //                                          X_g = sum_{k in g} x~_k
 //
-// with x~ = fp16(x) (round to nearest even) and the integer codes q exact in
-// fp16, so P_g and X_g come from v_mfma_f32_16x16x32_f16 (X_g with an all-ones
-// B operand) and the only rounding of the inputs is the activation's.  s and z
-// are applied per group in fp32.
+// with x~ = fp16(x) (round to nearest even) and the codes q exact, so P_g and
+// X_g come from v_mfma_f32_16x16x32_f16 (X_g with an all-ones B operand) and
+// the only rounding of the inputs is the activation's.  s and z are applied
+// per group in fp32.
 //
-// Operand construction: one wave owns 16 word columns (128 output columns).
-// Lane (wc = l % 16, kg = l / 16) loads the words of 8 consecutive K rows of
-// word column wc; v_perm_b32 pairs the bytes of rows k and k+1 so that each
-// 16-bit half holds the same column's nibbles from the two rows, and the
-// "1024 + q" half-precision magic (OR with 0x6400, then subtract 1024, or
-// scale by 1/16 for a nibble sitting 4 bits higher) yields the exact codes.
-// The 8 column positions of a word become 8 MFMA B operands; MFMA number c
-// computes output columns 8*wc + c.  A operands are the activation rows: lane
-// (m, kg) holds x~[m][8*kg .. 8*kg+7] of the 32-wide K step, the same K order
-// as the weights.
+// Code unpacking costs one AND per two codes: the fp16 bit pattern q (0..15)
+// is the subnormal q * 2^-24, exact, and the matrix cores multiply fp16
+// subnormals exactly; a nibble sitting 4 bits higher reads as q * 2^-20.  The
+// powers of two go into the per-group epilogue: s * (P - z X) =
+// (s * 2^24) * (P' - (z * 2^-24) X) with P' the MFMA sum of x~ * q * 2^-24.
+// v_perm_b32 first pairs the bytes of K rows k and k+1 of one word column so
+// that each 16-bit half holds the same column's nibble from the two rows: the
+// even columns of a word live in its bytes 0-1, the odd ones in bytes 2-3.
 //
-// Work split: a workgroup of 4 waves covers one 128-column tile, one chunk of
-// 16 or 32 activation rows and 4 consecutive slices of the K groups; the waves
-// meet in LDS.  When K is sliced across workgroups (small M needs it to fill
-// 256 CUs), each workgroup writes its partial tile to the caller's workspace
-// and the last one to arrive (a per-tile counter) adds the partials in a fixed
-// order, writes the output and resets the counter.
+// Layout of the work: one wave owns 16 word columns (128 output columns) of
+// one projection, a chunk of 16 or 32 activation rows, and a slice of the
+// 32-wide K steps.  Lane (wc = l % 16, kg = l / 16) supplies word column wc
+// and K rows 8*kg .. 8*kg+7 of each step; MFMA number c computes output
+// columns 8*wc + c.  The activation operand holds x~[m][8*kg .. 8*kg+7] in the
+// same K order.  Loads go through buffer resources (SGPR base + per-lane
+// offset + uniform row offset), so the hot loop does no 64-bit address math,
+// and out-of-range lanes read zeros.  A workgroup's 4 waves take 4 K slices of
+// the same tile and meet in LDS; when more K slices are needed to fill the
+// GPU, workgroups exchange fp32 partial tiles through the caller's workspace
+// with agent-coherent (sc1) stores and loads, and the last workgroup of a tile
+// (a relaxed agent-scope counter) adds them in slice order and resets the
+// counter.
 #include "kvq_common.h"
 
 namespace kvq {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kBlock = 256;
 constexpr int kTargetWaves = 2048;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 family
 
 struct Projs {
     const uint32_t *qw[3];
     const float *sc[3];
     const float *zr[3];
     float *out[3];
-    uint32_t wstart[3];   // first global word column of each projection
     uint32_t n[3];        // output columns of each projection
+    uint32_t tstart[3];   // first 16-word-column tile of each projection
     uint32_t count;
-    uint32_t wtotal;      // total word columns
+    uint32_t ntiles;
 };
 
-__device__ __forceinline__ int proj_of(const Projs &P, uint32_t gw) {
-    return (P.count > 1 && gw >= P.wstart[1]) ? ((P.count > 2 && gw >= P.wstart[2]) ? 2 : 1) : 0;
+// Uniform selection among the three projections (explicit selects keep the
+// values in SGPRs; indexing the kernel-argument arrays would load them into
+// VGPRs and force per-lane buffer-resource loops).
+template <typename T>
+__device__ __forceinline__ T pick(int p, T a0, T a1, T a2) {
+    return p == 0 ? a0 : (p == 1 ? a1 : a2);
 }
 
-// Agent-coherent (sc1) accesses for the partial tiles exchanged between
-// workgroups that may run on different XCDs (whose L2s are not coherent).
-__device__ __forceinline__ void store_agent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
 
-__device__ __forceinline__ f16x2 h2_bits(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
-__device__ __forceinline__ uint32_t h2_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+// Cache-policy operand of the buffer intrinsics: sc1 makes a load or store
+// coherent at agent scope (the encoding an agent-scope relaxed atomic load or
+// store uses on this family), which the partial tiles exchanged between
+// workgroups on different XCDs (whose L2s are not coherent) need.
+constexpr int kAuxSc1 = 16;
 
-// Exact codes of a nibble at bits 0-3 of each half: (1024 + q) - 1024.
-__device__ __forceinline__ uint32_t nib_lo(uint32_t t) {
-    const f16x2 h = h2_bits((t & 0x000F000Fu) | 0x64006400u);
-    return h2_u32(h - f16x2{(_Float16)1024.0f, (_Float16)1024.0f});
-}
-// Exact codes of a nibble at bits 4-7 of each half: (1024 + 16q) / 16 - 64.
-__device__ __forceinline__ uint32_t nib_hi(uint32_t t) {
-    const f16x2 h = h2_bits((t & 0x00F000F0u) | 0x64006400u);
-    return h2_u32(__builtin_elementwise_fma(h, f16x2{(_Float16)0.0625f, (_Float16)0.0625f},
-                                            f16x2{(_Float16)-64.0f, (_Float16)-64.0f}));
-}
-
-// 8 words (K rows 0..7 of one word column) -> 8 B operands, operand c holding
-// column c's codes for K rows 0..7 (row 2i in the low half of register i).
+// 8 words (K rows 0..7 of one word column) -> 8 B operands; operand c holds
+// column c's codes (as fp16 subnormals, scaled 2^-24 or 2^-20) for rows 0..7,
+// row 2i in the low half of register i.
 __device__ __forceinline__ void awq_operands(const uint32_t w[8], f16x8 B[8]) {
     uint32_t r[8][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // even columns live in bytes 0-1 of a word, odd columns in bytes 2-3
         const uint32_t ev = __builtin_amdgcn_perm(w[2 * i + 1], w[2 * i], 0x05040100u);
         const uint32_t od = __builtin_amdgcn_perm(w[2 * i + 1], w[2 * i], 0x07060302u);
-        r[0][i] = nib_lo(ev);
-        r[2][i] = nib_hi(ev);
-        r[4][i] = nib_lo(ev >> 8);
-        r[6][i] = nib_hi(ev >> 8);
-        r[1][i] = nib_lo(od);
-        r[3][i] = nib_hi(od);
-        r[5][i] = nib_lo(od >> 8);
-        r[7][i] = nib_hi(od >> 8);
+        const uint32_t ev8 = ev >> 8, od8 = od >> 8;
+        r[0][i] = ev & 0x000F000Fu;    // column 0, scale 2^-24
+        r[2][i] = ev & 0x00F000F0u;    // column 2, scale 2^-20
+        r[4][i] = ev8 & 0x000F000Fu;   // column 4
+        r[6][i] = ev8 & 0x00F000F0u;   // column 6
+        r[1][i] = od & 0x000F000Fu;    // column 1
+        r[3][i] = od & 0x00F000F0u;    // column 3
+        r[5][i] = od8 & 0x000F000Fu;   // column 5
+        r[7][i] = od8 & 0x00F000F0u;   // column 7
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        u32x4 v = {r[c][0], r[c][1], r[c][2], r[c][3]};
+        const u32x4 v = {r[c][0], r[c][1], r[c][2], r[c][3]};
         B[c] = __builtin_bit_cast(f16x8, v);
     }
 }
@@ -119,10 +116,13 @@ __device__ __forceinline__ f32x4 mfma16(const f16x8 &a, const f16x8 &b, const f3
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 as_f32x4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
+
 // MT: 16-row activation tiles per chunk (1 or 2).  R: accumulator rows per
 // lane that can hold real outputs (1 when m == 1, else 4).  KSG: 32-wide K
-// steps per quantization group (group_size / 32).
-template <int MT, int R, int KSG>
+// steps per quantization group.  U: K steps loaded together (a "piece"; U
+// divides KSG).  PF: prefetch the next piece while computing this one.
+template <int MT, int R, int KSG, int U, bool PF>
 __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, uint32_t M, uint32_t K, Projs P,
                                                    uint32_t nchunks, uint32_t ks_b, uint32_t *__restrict__ counters,
                                                    float *__restrict__ partials) {
@@ -131,99 +131,135 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
     __shared__ f32x4 red[4][16][32];
     __shared__ int s_last;
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
     const int wc = lane & 15, kg = lane >> 4;
 
     uint32_t b = blockIdx.x;
-    const uint32_t s = b % ks_b;
+    const uint32_t bs = b % ks_b;
     b /= ks_b;
     const uint32_t c = b % nchunks, t = b / nchunks;
-    const uint32_t G = K / GS;
-    const uint32_t nsplit = ks_b * 4, split = s * 4 + wv;
-    const uint32_t g0 = (uint32_t)((uint64_t)split * G / nsplit);
-    const uint32_t g1 = (uint32_t)((uint64_t)(split + 1) * G / nsplit);
+    const int p = (P.count > 1 && t >= P.tstart[1]) ? ((P.count > 2 && t >= P.tstart[2]) ? 2 : 1) : 0;
+    const uint32_t np = pick(p, P.n[0], P.n[1], P.n[2]), wp = np / 8;
+    const uint32_t tp = t - pick(p, P.tstart[0], P.tstart[1], P.tstart[2]);   // tile within the projection
+    const uint32_t lw = tp * 16 + wc;     // lane's word column in its projection
+    const bool wok = lw < wp;
 
-    const uint32_t gw = t * 16 + wc;
-    const bool wok = gw < P.wtotal;
-    const int p = proj_of(P, wok ? gw : 0);
-    const uint32_t lw = (wok ? gw : 0) - P.wstart[p];
-    const uint32_t np = P.n[p], wp = np / 8;
-    const uint32_t *qcol = P.qw[p] + lw + (size_t)(kg * 8) * wp;
-    const float *scol = P.sc[p] + 8 * lw;
-    const float *zcol = P.zr[p] + 8 * lw;
+    // K slice of this wave, in pieces of U steps
+    const uint32_t npieces = K / (32 * U);
+    const uint32_t nsplit = ks_b * 4, split = bs * 4 + wv;
+    const uint32_t pc0 = (uint32_t)((uint64_t)split * npieces / nsplit);
+    const uint32_t pc1 = (uint32_t)((uint64_t)(split + 1) * npieces / nsplit);
 
-    const float *xrow[MT];
-    bool xok[MT];
+    // buffer resources and per-lane offsets (out-of-range lanes point past the end: reads give 0)
+    const uint32_t wbytes = K * wp * 4;
+    const rsrc_t rw = make_rsrc(pick(p, P.qw[0], P.qw[1], P.qw[2]), wbytes);
+    const uint32_t voff_w = wok ? ((uint32_t)(kg * 8) * wp + lw) * 4 : wbytes;
+    const uint32_t xbytes = M * K * 4;
+    const rsrc_t rx = make_rsrc(x, xbytes);
+    uint32_t voff_x[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const uint32_t m = c * MR + mt * 16 + wc;
-        xok[mt] = m < M;
-        xrow[mt] = x + (size_t)(xok[mt] ? m : 0) * K + kg * 8;
+        voff_x[mt] = m < M ? (m * K + kg * 8) * 4 : xbytes;
     }
+    const uint32_t szbytes = (K / GS) * np * 4;
+    const rsrc_t rs = make_rsrc(pick(p, P.sc[0], P.sc[1], P.sc[2]), szbytes);
+    const rsrc_t rz = make_rsrc(pick(p, P.zr[0], P.zr[1], P.zr[2]), szbytes);
+    const uint32_t voff_sz = wok ? lw * 32 : szbytes;
 
     f32x4 acc[MT][8];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) acc[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f16x8 ones;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
-    const f16x8 zero8 = ones - ones;
-
-    for (uint32_t g = g0; g < g1; ++g) {
-        uint32_t w[KSG][8];
-#pragma unroll
-        for (int ks = 0; ks < KSG; ++ks)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                w[ks][i] = wok ? __builtin_nontemporal_load(qcol + (size_t)(g * GS + ks * 32 + i) * wp) : 0u;
-        f16x8 a[KSG][MT];
-#pragma unroll
-        for (int ks = 0; ks < KSG; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (xok[mt]) {
-                    const f32x4 *xp = reinterpret_cast<const f32x4 *>(xrow[mt] + g * GS + ks * 32);
-                    a[ks][mt] = to_f16x8(xp[0], xp[1]);
-                } else {
-                    a[ks][mt] = zero8;
-                }
-            }
-        f32x4 pg[MT][8], xg[MT];
+    f32x4 pg[MT][8], xg[MT];
+    auto reset = [&]() {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             xg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+    };
+    reset();
+    f16x8 ones;
 #pragma unroll
-        for (int ks = 0; ks < KSG; ++ks) {
-            f16x8 B[8];
-            awq_operands(w[ks], B);
+    for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+
+    struct Piece {
+        uint32_t w[U][8];
+        u32x4 xv[U][MT][2];
+    };
+    auto load = [&](uint32_t pc, Piece &pz) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t k0 = (pc * U + u) * 32;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                pz.w[u][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, (k0 + i) * wp * 4, 0);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                xg[mt] = mfma16(a[ks][mt], ones, xg[mt]);
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = mfma16(a[ks][mt], B[cc], pg[mt][cc]);
+                pz.xv[u][mt][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * 4, 0);
+                pz.xv[u][mt][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * 4 + 16, 0);
             }
         }
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, z0 = s0, z1 = s0;
-        if (wok) {
-            const f32x4 *sp = reinterpret_cast<const f32x4 *>(scol + (size_t)g * np);
-            const f32x4 *zp = reinterpret_cast<const f32x4 *>(zcol + (size_t)g * np);
-            s0 = sp[0]; s1 = sp[1]; z0 = zp[0]; z1 = zp[1];
+    };
+    auto compute = [&](uint32_t pc, const Piece &pz) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            f16x8 B[8];
+            awq_operands(pz.w[u], B);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f16x8 a = to_f16x8(as_f32x4(pz.xv[u][mt][0]), as_f32x4(pz.xv[u][mt][1]));
+                xg[mt] = mfma16(a, ones, xg[mt]);
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = mfma16(a, B[cc], pg[mt][cc]);
+            }
         }
-        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        // group epilogue at the end of a group or of this wave's slice
+        const uint32_t kstep_end = (pc + 1) * U;
+        if (kstep_end % KSG == 0 || pc + 1 == pc1) {
+            const uint32_t g = (pc * U) / KSG;
+            const f32x4 s0 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff_sz, g * np * 4, 0));
+            const f32x4 s1 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff_sz, g * np * 4 + 16, 0));
+            const f32x4 z0 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rz, voff_sz, g * np * 4, 0));
+            const f32x4 z1 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rz, voff_sz, g * np * 4 + 16, 0));
+            // columns 0,1,4,5 were unpacked as q*2^-24, columns 2,3,6,7 as q*2^-20
+            const float f[8] = {0x1p24f, 0x1p24f, 0x1p20f, 0x1p20f, 0x1p24f, 0x1p24f, 0x1p20f, 0x1p20f};
+            const float sv[8] = {s0.x * f[0], s0.y * f[1], s0.z * f[2], s0.w * f[3],
+                                 s1.x * f[4], s1.y * f[5], s1.z * f[6], s1.w * f[7]};
+            const float zv[8] = {z0.x / f[0], z0.y / f[1], z0.z / f[2], z0.w / f[3],
+                                 z1.x / f[4], z1.y / f[5], z1.z / f[6], z1.w / f[7]};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc)
+                for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
-                for (int i = 0; i < R; ++i)
-                    acc[mt][cc][i] = __builtin_fmaf(sv[cc], __builtin_fmaf(-zv[cc], xg[mt][i], pg[mt][cc][i]),
-                                                    acc[mt][cc][i]);
+                    for (int i = 0; i < R; ++i)
+                        acc[mt][cc][i] = __builtin_fmaf(sv[cc], __builtin_fmaf(-zv[cc], xg[mt][i], pg[mt][cc][i]),
+                                                        acc[mt][cc][i]);
+            reset();
+        }
+    };
+
+    if (PF) {
+        Piece b0, b1;
+        if (pc0 < pc1) load(pc0, b0);
+        for (uint32_t pc = pc0; pc < pc1; pc += 2) {
+            if (pc + 1 < pc1) load(pc + 1, b1);
+            compute(pc, b0);
+            if (pc + 1 < pc1) {
+                if (pc + 2 < pc1) load(pc + 2, b0);
+                compute(pc + 1, b1);
+            }
+        }
+    } else {
+        for (uint32_t pc = pc0; pc < pc1; ++pc) {
+            Piece b0;
+            load(pc, b0);
+            compute(pc, b0);
+        }
     }
 
     // Waves -> LDS, one 16-row tile at a time, as [row][column] with
@@ -231,6 +267,8 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
     // waves' values and write 16-byte pieces of the output (or partial) rows.
     const uint32_t tile_id = t * nchunks + c;
     float *part = partials + (size_t)tile_id * ks_b * (MR * 128);
+    const rsrc_t rp = make_rsrc(part, ks_b * (MR * 128) * 4);
+    float *outp = pick(p, P.out[0], P.out[1], P.out[2]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -243,29 +281,21 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
         for (int e = threadIdx.x; e < 16 * 32; e += kBlock) {
             const int row = e >> 5, col4 = e & 31;
             const uint32_t m = c * MR + mt * 16 + row;
-            const uint32_t gwo = t * 16 + (col4 >> 1);
-            if (m >= M || gwo >= P.wtotal) continue;
+            const uint32_t lwo = tp * 16 + (col4 >> 1);
+            if (m >= M || lwo >= wp) continue;
             const f32x4 v = red[0][row][col4] + red[1][row][col4] + red[2][row][col4] + red[3][row][col4];
             if (ks_b == 1) {
-                const int po = proj_of(P, gwo);
-                const uint32_t col = 8 * (gwo - P.wstart[po]) + (col4 & 1) * 4;
-                *reinterpret_cast<f32x4 *>(P.out[po] + (size_t)m * P.n[po] + col) = v;
+                *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + 8 * lwo + (col4 & 1) * 4) = v;
             } else {
-                float *dst = part + (size_t)s * (MR * 128) + (mt * 16 + row) * 128 + col4 * 4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) store_agent(dst + j, v[j]);
+                const uint32_t off = ((bs * MR + mt * 16 + row) * 128 + col4 * 4) * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, off, 0, kAuxSc1);
             }
         }
         __syncthreads();
     }
     if (ks_b == 1) return;
 
-    // Cross-workgroup K reduction.  The partial tiles were written with
-    // agent-coherent stores (sc1, below); once every thread's stores have
-    // completed, one atomic per workgroup counts arrivals, and the last
-    // workgroup of the tile reads all partials with agent-coherent loads,
-    // adds them in split order (so the result does not depend on arrival
-    // order) and resets the counter for the next call.
+    // Cross-workgroup K reduction (see the header comment).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -278,17 +308,12 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
     for (int e = threadIdx.x; e < MR * 32; e += kBlock) {
         const int row = e >> 5, col4 = e & 31;
         const uint32_t m = c * MR + row;
-        const uint32_t gwo = t * 16 + (col4 >> 1);
-        if (m >= M || gwo >= P.wtotal) continue;
+        const uint32_t lwo = tp * 16 + (col4 >> 1);
+        if (m >= M || lwo >= wp) continue;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        for (uint32_t q = 0; q < ks_b; ++q) {
-            const float *src = part + (size_t)q * (MR * 128) + row * 128 + col4 * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] += load_agent(src + j);
-        }
-        const int po = proj_of(P, gwo);
-        const uint32_t col = 8 * (gwo - P.wstart[po]) + (col4 & 1) * 4;
-        *reinterpret_cast<f32x4 *>(P.out[po] + (size_t)m * P.n[po] + col) = v;
+        for (uint32_t q = 0; q < ks_b; ++q)
+            v += as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rp, ((q * MR + row) * 128 + col4 * 4) * 4, 0, kAuxSc1));
+        *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + 8 * lwo + (col4 & 1) * 4) = v;
     }
     if (threadIdx.x == 0) __hip_atomic_store(&counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -296,40 +321,45 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
 // ------------------------------------------------------------------ host --
 
 struct Plan {
-    uint32_t mt, mr, nchunks, ntiles, ks_b;
+    uint32_t mt, mr, nchunks, ks_b, u;
     size_t counter_bytes, partial_bytes;
 };
 
-Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t wtotal) {
+uint32_t piece_steps(uint32_t mt, uint32_t ksg) {
+    const uint32_t cap = mt == 1 ? 4 : 2;
+    return ksg < cap ? ksg : cap;
+}
+
+Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles) {
     Plan pl;
     pl.mt = m <= 16 ? 1 : 2;
     pl.mr = 16 * pl.mt;
     pl.nchunks = (m + pl.mr - 1) / pl.mr;
-    pl.ntiles = (wtotal + 15) / 16;
-    const uint32_t groups = k / gs;
-    const uint64_t units = (uint64_t)pl.ntiles * pl.nchunks;
+    pl.u = piece_steps(pl.mt, gs / 32);
+    const uint32_t npieces = k / (32 * pl.u);
+    const uint64_t units = (uint64_t)ntiles * pl.nchunks;
     uint64_t waves = kTargetWaves / (units ? units : 1);
-    if (waves > groups) waves = groups;
-    if (waves < 1) waves = 1;
+    if (waves > npieces) waves = npieces;
     pl.ks_b = (uint32_t)(waves / 4 ? waves / 4 : 1);
-    const size_t tiles = (size_t)pl.ntiles * pl.nchunks;
+    const size_t tiles = (size_t)ntiles * pl.nchunks;
     pl.counter_bytes = pl.ks_b > 1 ? ((tiles * 4 + 255) / 256) * 256 : 0;
     pl.partial_bytes = pl.ks_b > 1 ? tiles * pl.ks_b * pl.mr * 128 * 4 : 0;
     return pl;
 }
 
-int check_proj(const char *fn, const int4_awq_proj_t *p, const char *which, uint32_t m, uint32_t k, uint32_t gs) {
-    (void)m;
-    (void)gs;
+int check_proj(const char *fn, const int4_awq_proj_t *p, const char *which, uint32_t k, uint32_t gs) {
     if (!p->qweight || !p->scales || !p->zeros || !p->out)
         return fail(KVQ_E_INVALID, "%s: %s projection has a null pointer", fn, which);
     if (!aligned16(p->qweight) || !aligned16(p->scales) || !aligned16(p->zeros) || !aligned16(p->out))
         return fail(KVQ_E_INVALID, "%s: %s projection pointers must be 16-byte aligned", fn, which);
     if (p->n == 0 || p->n % 8)
         return fail(KVQ_E_INVALID, "%s: %s projection n=%u (want a positive multiple of 8)", fn, which, p->n);
-    (void)k;
+    if ((uint64_t)k * p->n / 2 >= 0x80000000ull || (uint64_t)(k / gs) * p->n * 4 >= 0x80000000ull)
+        return fail(KVQ_E_INVALID, "%s: %s projection larger than 2 GiB", fn, which);
     return KVQ_OK;
 }
+
+uint32_t tiles_of(uint32_t n) { return (n / 8 + 15) / 16; }
 
 }  // namespace
 }  // namespace kvq
@@ -339,12 +369,14 @@ using namespace kvq;
 extern "C" int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_size, uint32_t n_total,
                                         size_t *bytes) {
     if (!bytes) return fail(KVQ_E_INVALID, "int4_awq_workspace_bytes: null output pointer");
-    if (m == 0 || group_size == 0 || k % group_size || n_total % 8) {
-        *bytes = 0;
-        return KVQ_OK;
+    *bytes = 0;
+    if (m == 0 || group_size < 32 || group_size % 32 || k % group_size || n_total % 8) return KVQ_OK;
+    // splitting n_total into up to three projections adds at most two tiles
+    for (uint32_t extra = 0; extra <= 2; ++extra) {
+        const Plan pl = make_plan(m, k, group_size, tiles_of(n_total) + extra);
+        const size_t b = pl.counter_bytes + pl.partial_bytes;
+        if (b > *bytes) *bytes = b;
     }
-    const Plan pl = make_plan(m, k, group_size, n_total / 8);
-    *bytes = pl.counter_bytes + pl.partial_bytes;
     return KVQ_OK;
 }
 
@@ -360,41 +392,33 @@ extern "C" int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k, uint32_
         return fail(KVQ_E_INVALID, "%s: group_size=%u (supported: 32, 64, 128, 256)", fn, group_size);
     if (k == 0 || k % group_size)
         return fail(KVQ_E_INVALID, "%s: K=%u is not a positive multiple of group_size=%u", fn, k, group_size);
+    if ((uint64_t)m * k * 4 >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: x larger than 2 GiB", fn);
     if ((k_proj == nullptr) != (v_proj == nullptr))
         return fail(KVQ_E_INVALID, "%s: k and v projections must be both set or both NULL", fn);
-    int st = check_proj(fn, q_proj, "q", m, k, group_size);
+    int st = check_proj(fn, q_proj, "q", k, group_size);
     if (st) return st;
-    Projs P;
-    P.count = 1;
-    P.qw[0] = q_proj->qweight; P.sc[0] = q_proj->scales; P.zr[0] = q_proj->zeros; P.out[0] = q_proj->out;
-    P.n[0] = q_proj->n;
-    P.wstart[0] = 0;
-    uint64_t wtotal = q_proj->n / 8;
+    const int4_awq_proj_t *list[3] = {q_proj, k_proj, v_proj};
     if (k_proj) {
-        st = check_proj(fn, k_proj, "k", m, k, group_size);
+        st = check_proj(fn, k_proj, "k", k, group_size);
         if (st) return st;
-        st = check_proj(fn, v_proj, "v", m, k, group_size);
+        st = check_proj(fn, v_proj, "v", k, group_size);
         if (st) return st;
         if (k_proj->n != v_proj->n)
             return fail(KVQ_E_INVALID, "%s: k and v projections differ in n (%u vs %u)", fn, k_proj->n, v_proj->n);
-        const int4_awq_proj_t *kv[2] = {k_proj, v_proj};
-        for (int i = 0; i < 2; ++i) {
-            P.qw[i + 1] = kv[i]->qweight; P.sc[i + 1] = kv[i]->scales; P.zr[i + 1] = kv[i]->zeros;
-            P.out[i + 1] = kv[i]->out; P.n[i + 1] = kv[i]->n;
-            P.wstart[i + 1] = (uint32_t)wtotal;
-            wtotal += kv[i]->n / 8;
-        }
-        P.count = 3;
-    } else {
-        for (int i = 1; i < 3; ++i) {
-            P.qw[i] = P.qw[0]; P.sc[i] = P.sc[0]; P.zr[i] = P.zr[0]; P.out[i] = P.out[0];
-            P.n[i] = 0; P.wstart[i] = (uint32_t)wtotal;
-        }
     }
-    if (wtotal > 0x0FFFFFFFull) return fail(KVQ_E_INVALID, "%s: total n too large", fn);
-    P.wtotal = (uint32_t)wtotal;
+    Projs P;
+    P.count = k_proj ? 3 : 1;
+    uint32_t tiles = 0;
+    for (uint32_t i = 0; i < 3; ++i) {
+        const int4_awq_proj_t *pr = i < P.count ? list[i] : q_proj;
+        P.qw[i] = pr->qweight; P.sc[i] = pr->scales; P.zr[i] = pr->zeros; P.out[i] = pr->out;
+        P.n[i] = i < P.count ? pr->n : 0;
+        P.tstart[i] = tiles;
+        if (i < P.count) tiles += tiles_of(pr->n);
+    }
+    P.ntiles = tiles;
 
-    Plan pl = make_plan(m, k, group_size, P.wtotal);
+    Plan pl = make_plan(m, k, group_size, P.ntiles);
     uint32_t *counters = nullptr;
     float *partials = nullptr;
     if (pl.ks_b > 1) {
@@ -405,24 +429,25 @@ extern "C" int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k, uint32_
             partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.counter_bytes);
         }
     }
-    const uint64_t blocks = (uint64_t)pl.ntiles * pl.nchunks * pl.ks_b;
+    const uint64_t blocks = (uint64_t)P.ntiles * pl.nchunks * pl.ks_b;
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
     hipStream_t s = as_stream(stream);
     const uint32_t ksg = group_size / 32;
-#define KVQ_AWQ(MT, R, KSG) \
-    awq_gemm<MT, R, KSG><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b, counters, partials)
-#define KVQ_AWQ_K(MT, R)                     \
-    switch (ksg) {                           \
-        case 1: KVQ_AWQ(MT, R, 1); break;    \
-        case 2: KVQ_AWQ(MT, R, 2); break;    \
-        case 4: KVQ_AWQ(MT, R, 4); break;    \
-        default: KVQ_AWQ(MT, R, 8); break;   \
+#define KVQ_AWQ(MT, R, KSG, U, PF)                                                                            \
+    awq_gemm<MT, R, KSG, U, PF><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b, counters, \
+                                                                    partials)
+#define KVQ_AWQ_K(MT, R, CAP, PF)                                   \
+    switch (ksg) {                                                  \
+        case 1: KVQ_AWQ(MT, R, 1, 1, PF); break;                    \
+        case 2: KVQ_AWQ(MT, R, 2, 2, PF); break;                    \
+        case 4: KVQ_AWQ(MT, R, 4, (CAP < 4 ? CAP : 4), PF); break;  \
+        default: KVQ_AWQ(MT, R, 8, (CAP < 4 ? CAP : 4), PF); break; \
     }
     if (pl.mt == 1) {
-        if (m == 1) KVQ_AWQ_K(1, 1)
-        else KVQ_AWQ_K(1, 4)
+        if (m == 1) KVQ_AWQ_K(1, 1, 4, true)
+        else KVQ_AWQ_K(1, 4, 4, true)
     } else {
-        KVQ_AWQ_K(2, 4)
+        KVQ_AWQ_K(2, 4, 2, false)
     }
 #undef KVQ_AWQ_K
 #undef KVQ_AWQ

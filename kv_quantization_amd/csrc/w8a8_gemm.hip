@@ -214,12 +214,18 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
 // read; the ring below waits explicitly (wait_vm) for exactly the stage it
 // is about to read.  lds_wave_base must be wave-uniform (it goes to M0); lane
 // i's data lands at lds_wave_base + i * size.
+// M0 is named as clobbered; nothing else in these kernels keeps a value in
+// M0 (gfx9 LDS instructions do not use it), so the "reserved register"
+// warning does not apply.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_load16(const void *g, uint32_t lds_wave_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_load4(const void *g, uint32_t lds_wave_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
