@@ -191,38 +191,64 @@ __global__ __launch_bounds__(kBlock) void w8a8_skinny(const uint8_t *__restrict_
 // rows > 32: one workgroup owns all (<= 256) activation rows and 128 output
 // columns over one slice of K (split-K), so the weight tile is read from HBM
 // once per call and the activation tile (re-read by every column tile) comes
-// from L2.  2x2 waves, each (rows/2) x 64.  Each 128-wide K step of both
-// tiles (and the 128-column activation block scales) travels global -> LDS
-// with gfx950's direct loads (global_load_lds_dwordx4: lane i's 16 bytes land
-// at LDS base + 16*i), through a 3-stage ring so two K steps are in flight
-// while the third is multiplied.  Rows are stored with their eight 16-byte
-// chunks XOR-swizzled by (row & 7), which keeps both the load pattern and the
-// MFMA operand reads (ds_read_b128) free of bank conflicts.  With split-K the
-// fp32 partial tiles go to the workspace and w8a8_reduce adds them in split
-// order (deterministic), applies per-row scales and writes bf16.
+// from L2.  8 waves in a 4 (rows) x 2 (64 columns) grid, two per SIMD, so one
+// wave's scaling arithmetic overlaps the other's matrix instructions.  Each
+// 128-wide K step of both tiles (and the activation block scales) travels
+// global -> LDS with direct DMA loads (lane i's 16 bytes land at LDS base +
+// 16*i) through a 3-stage ring, two K steps in flight while the third is
+// multiplied.  Rows are stored with their eight 16-byte chunks XOR-swizzled
+// by (row & 7), which keeps both the load pattern and the MFMA operand reads
+// (ds_read_b128) free of bank conflicts.  The loads are buffer loads from
+// wave-uniform bases (the per-lane offsets never change; rows past the end
+// of the activations or of a weight segment read as zero); a 128-column tile
+// that straddles two weight segments (possible only with per-row scales)
+// uses per-lane global addresses instead.  With split-K the fp32 partial
+// tiles go to the workspace and w8a8_reduce adds them in split order
+// (deterministic), applies per-row scales and writes bf16.
 
 constexpr int kWideN = 128;
 constexpr int kStages = 3;
+constexpr int kWideWaves = 8;
+constexpr int kWideThreads = kWideWaves * kWave;
 
 // LDS byte offset of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// Direct global->LDS loads, written as inline assembly so that the compiler
-// does not add its conservative "all LDS DMA complete" wait before every LDS
-// read; the ring below waits explicitly (wait_vm) for exactly the stage it
-// is about to read.  lds_wave_base must be wave-uniform (it goes to M0); lane
-// i's data lands at lds_wave_base + i * size.
-// M0 is named as clobbered; nothing else in these kernels keeps a value in
-// M0 (gfx9 LDS instructions do not use it), so the "reserved register"
-// warning does not apply.
+// Raw buffer resource (4 SGPRs): base, stride 0, size in bytes (reads past
+// it return zero), untyped dword format of the gfx9 family.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// Direct loads into LDS, written as inline assembly so that the compiler does
+// not add its conservative "all LDS DMA complete" wait before every LDS read;
+// the ring waits explicitly (wait_vm) for exactly the stage it is about to
+// read.  lds_wave_base must be wave-uniform (it goes to M0).  M0 is named as
+// clobbered; nothing else in these kernels keeps a value in M0 (gfx9 LDS
+// instructions do not use it), so the "reserved register" warning does not
+// apply.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_load16(const void *g, uint32_t lds_wave_base) {
+__device__ __forceinline__ void lds_buf16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 ::"v"(voff), "s"(rsrc), "s"(soff), "s"(lds_wave_base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_buf4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 ::"v"(voff), "s"(rsrc), "s"(soff), "s"(lds_wave_base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_glb16(const void *g, uint32_t lds_wave_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_load4(const void *g, uint32_t lds_wave_base) {
+__device__ __forceinline__ void lds_glb4(const void *g, uint32_t lds_wave_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -237,27 +263,28 @@ __device__ __forceinline__ void wait_vm() {
 
 template <int MTW, int KIND>
 struct WideCfg {
-    static constexpr int BM = 32 * MTW;
+    static constexpr int WM = 4;                         // waves along rows
+    static constexpr int BM = 16 * MTW * WM;             // rows per workgroup
     static constexpr int A_BYTES = BM * 128;
     static constexpr int B_BYTES = kWideN * 128;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_INSTR = BM / 32;      // 1 KiB loads per wave for A
-    static constexpr int B_INSTR = 4;            // and for B (128 rows x 128 B / 4 waves)
-    static constexpr int N_INSTR = A_INSTR + B_INSTR + (KIND == 1 ? 2 : 0);
+    static constexpr int A_INSTR = A_BYTES / 1024 / kWideWaves;   // 1 KiB loads per wave
+    static constexpr int B_INSTR = B_BYTES / 1024 / kWideWaves;
+    static constexpr int SA_ROWS = BM / kWideWaves;               // activation scales per wave
+    static constexpr int N_INSTR = A_INSTR + B_INSTR + (KIND == 1 ? 1 : 0);
+    static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SA_ROWS <= 64, "tile shape");
 };
 
-template <int MTW, int KIND>
-__global__ __launch_bounds__(kBlock) void w8a8_wide(const uint8_t *__restrict__ q, const float *__restrict__ sa,
-                                                    uint32_t rows, uint32_t K, Segs S, uint16_t *__restrict__ out,
-                                                    uint32_t ldc, uint32_t splits, uint32_t ntiles,
-                                                    float *__restrict__ partials) {
+template <int MTW, int KIND, bool UNI>
+__global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restrict__ q, const float *__restrict__ sa,
+                                                          uint32_t rows, uint32_t K, Segs S,
+                                                          uint16_t *__restrict__ out, uint32_t ldc, uint32_t splits,
+                                                          uint32_t ntiles, float *__restrict__ partials) {
     using C = WideCfg<MTW, KIND>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * C::STAGE];
-    __shared__ __attribute__((aligned(16))) float lds_sa[kStages][4][64];
-    __shared__ __attribute__((aligned(16))) float lds_sw[kStages][4][64];
-    const int tid = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) float lds_sa[kStages][kWideWaves][64];
     const int lane = lane_id();
-    const int wv = tid >> 6;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wv >> 1, wn = wv & 1;
     const int r16 = lane & 15, g = lane >> 4;
     const uint32_t tile = blockIdx.x % ntiles, split = blockIdx.x / ntiles;
@@ -267,62 +294,64 @@ __global__ __launch_bounds__(kBlock) void w8a8_wide(const uint8_t *__restrict__ 
     const uint32_t kb1 = (uint32_t)((uint64_t)(split + 1) * nkb / splits);
     const int nks = (int)(kb1 - kb0);
 
-    // -- per-lane global sources for the direct loads (one row chunk each) --
-    // A: instruction j of wave w fills rows 8*(w*A_INSTR + j) .. +8; lane i
-    // holds LDS chunk slot i%8 of row 8*(...) + i/8, i.e. logical chunk
-    // (i%8) ^ (row & 7).
-    const uint8_t *asrc[C::A_INSTR];
+    // -- sources of the direct loads.  Load j of wave w fills 1 KiB of the
+    // tile: rows 8*(w*INSTR + j) .. +8; lane i writes LDS chunk slot i%8 of
+    // row (that + i/8), which holds logical chunk (i%8) ^ (row & 7).
+    const u32x4 ra = buffer_rsrc(q, rows * K);
+    uint32_t aoff[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
-        const int row = 8 * (wv * C::A_INSTR + j) + (lane >> 3);
-        const int chunk = (lane & 7) ^ (row & 7);
-        const uint32_t m = (uint32_t)row < rows ? row : 0;      // rows past the end: any valid row
-        asrc[j] = q + (size_t)m * K + chunk * 16;
+        const uint32_t row = 8 * (wv * C::A_INSTR + j) + (lane >> 3);
+        aoff[j] = row * K + (((lane & 7) ^ (row & 7)) << 4);   // rows >= `rows` read zeros
     }
+    const int sg0 = seg_of(S, n0);
+    const uint8_t *wseg = sg0 == 0 ? S.w[0] : (sg0 == 1 ? S.w[1] : S.w[2]);
+    const uint32_t seg_start = sg0 == 0 ? S.start[0] : (sg0 == 1 ? S.start[1] : S.start[2]);
+    const uint32_t seg_n = sg0 == 0 ? S.n[0] : (sg0 == 1 ? S.n[1] : S.n[2]);
+    const u32x4 rb = buffer_rsrc(wseg, seg_n * K);
+    uint32_t boff[C::B_INSTR];
     const uint8_t *bsrc[C::B_INSTR];
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
-        const int row = 8 * (wv * C::B_INSTR + j) + (lane >> 3);
-        const int chunk = (lane & 7) ^ (row & 7);
-        uint32_t jg = n0 + row;
-        int sg = seg_of(S, jg < S.ntotal ? jg : 0);
-        uint32_t jl = (jg < S.ntotal ? jg : 0) - S.start[sg];
-        if (jl >= S.n[sg]) { sg = 0; jl = 0; }               // past the end: any valid row
-        bsrc[j] = S.w[sg] + (size_t)jl * K + chunk * 16;
+        const uint32_t row = 8 * (wv * C::B_INSTR + j) + (lane >> 3);
+        const uint32_t chunk = ((lane & 7) ^ (row & 7)) << 4;
+        boff[j] = (n0 - seg_start + row) * K + chunk;          // past the segment: zeros
+        if (!UNI) {
+            uint32_t jg = n0 + row;
+            int sg = seg_of(S, jg < S.ntotal ? jg : 0);
+            uint32_t jl = (jg < S.ntotal ? jg : 0) - S.start[sg];
+            if (jl >= S.n[sg]) { sg = 0; jl = 0; }           // past the end: any valid row
+            bsrc[j] = S.w[sg] + (size_t)jl * K + chunk;
+        }
     }
-    // activation block scales for K block kb: wave w loads rows w*BM/4 + lane
-    const float *ssrc = sa;
+    // Block scales of K block kb, one 4-byte load per wave: lanes below
+    // SA_ROWS stage the activation scales of rows w*SA_ROWS + lane (rows past
+    // the end take row 0's: their products are zero), the other lanes the
+    // weight scale of this 128-column band.
+    const float *sasrc = sa;
     if (KIND == 1) {
-        const uint32_t m = (uint32_t)(wv * (C::BM / 4) + lane);
-        ssrc = sa + (size_t)(m < rows && lane < C::BM / 4 ? m : 0) * nkb;
+        const float *sseg = sg0 == 0 ? S.s[0] : (sg0 == 1 ? S.s[1] : S.s[2]);
+        const float *swp = sseg + (size_t)((n0 - seg_start) / 128) * nkb;
+        const uint32_t m = wv * C::SA_ROWS + lane;
+        sasrc = lane < C::SA_ROWS ? sa + (size_t)(m < rows ? m : 0) * nkb : swp;
     }
 
-    const float *swp = sa;
-    if (KIND == 1) {
-        const int sgb = seg_of(S, n0);
-        swp = S.s[sgb] + (size_t)((n0 - S.start[sgb]) / 128) * nkb;
-    }
-
-    // wave-uniform LDS byte offsets (they go to M0)
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
     const uint32_t sa0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sa[0][0][0]));
-    const uint32_t sw0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sw[0][0][0]));
-    const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
     auto issue = [&](int it) {
         const uint32_t st = (uint32_t)(it % kStages);
         const uint32_t kb = kb0 + it;
         const uint32_t abase = lds0 + st * C::STAGE;
         const uint32_t bbase = abase + C::A_BYTES;
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(kb * 128);
 #pragma unroll
-        for (int j = 0; j < C::A_INSTR; ++j)
-            lds_load16(asrc[j] + (size_t)kb * 128, abase + (wvu * C::A_INSTR + j) * 1024);
+        for (int j = 0; j < C::A_INSTR; ++j) lds_buf16(ra, aoff[j], soff, abase + (wv * C::A_INSTR + j) * 1024);
 #pragma unroll
-        for (int j = 0; j < C::B_INSTR; ++j)
-            lds_load16(bsrc[j] + (size_t)kb * 128, bbase + (wvu * C::B_INSTR + j) * 1024);
-        if (KIND == 1) {
-            lds_load4(ssrc + kb, sa0 + (st * 4 + wvu) * 256);
-            lds_load4(swp + kb, sw0 + (st * 4 + wvu) * 256);   // every lane: the tile's weight block scale
+        for (int j = 0; j < C::B_INSTR; ++j) {
+            if (UNI) lds_buf16(rb, boff[j], soff, bbase + (wv * C::B_INSTR + j) * 1024);
+            else lds_glb16(bsrc[j] + (size_t)kb * 128, bbase + (wv * C::B_INSTR + j) * 1024);
         }
+        if (KIND == 1) lds_glb4(sasrc + kb, sa0 + (st * kWideWaves + wv) * 256);
     };
 
     f32x4 acc[MTW][4];
@@ -344,6 +373,7 @@ __global__ __launch_bounds__(kBlock) void w8a8_wide(const uint8_t *__restrict__ 
         }
         __builtin_amdgcn_s_barrier();
         const int st = it % kStages;
+        const float swk = KIND == 1 ? lds_sa[st][0][63] : 1.0f;
         const uint8_t *abase = lds + st * C::STAGE;
         const uint8_t *bbase = abase + C::A_BYTES;
         i32x8 b[4];
@@ -354,7 +384,6 @@ __global__ __launch_bounds__(kBlock) void w8a8_wide(const uint8_t *__restrict__ 
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(bbase + row * 128 + (((g + 4) ^ (row & 7)) << 4));
             b[nt] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }
-        const float swk = KIND == 1 ? lds_sw[st][wv][0] : 1.0f;
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) {
             const int row = wm * 16 * MTW + mt * 16 + r16;
@@ -367,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void w8a8_wide(const uint8_t *__restrict__ 
             } else {
                 // rows 4g..4g+3 of this M tile: one 16-byte read of the staged scales
                 const int r0 = wm * 16 * MTW + mt * 16 + 4 * g;
-                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&lds_sa[st][r0 / (C::BM / 4)][r0 % (C::BM / 4)]);
+                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&lds_sa[st][r0 / C::SA_ROWS][r0 % C::SA_ROWS]);
                 const f32x4 sc = s4 * swk;
                 f32x4 p[4];
 #pragma unroll
@@ -447,6 +476,8 @@ int check_gemv(const char *fn, w8a8_scale_t kind, const uint8_t *q, const float 
             return fail(KVQ_E_INVALID, "%s: segment %u pointers must be 16-byte aligned", fn, i);
         if (i + 1 < nseg && segs[i].n % align)
             return fail(KVQ_E_INVALID, "%s: segment %u has %u rows, not a multiple of %u", fn, i, segs[i].n, align);
+        if ((uint64_t)segs[i].n * k >= 0x80000000ull)
+            return fail(KVQ_E_INVALID, "%s: segment %u is larger than 2 GiB", fn, i);
         S->w[i] = segs[i].w;
         S->s[i] = segs[i].scale;
         S->start[i] = (uint32_t)total;
@@ -463,6 +494,7 @@ int check_gemv(const char *fn, w8a8_scale_t kind, const uint8_t *q, const float 
     S->count = nseg;
     S->ntotal = (uint32_t)total;
     if (ldc < total) return fail(KVQ_E_INVALID, "%s: ldc=%u < N=%u", fn, ldc, (uint32_t)total);
+    if ((uint64_t)rows * k >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: activation block is larger than 2 GiB", fn);
     if (!q || !a_scales || !out) return fail(KVQ_E_INVALID, "%s: null pointer argument", fn);
     if (!aligned16(q) || !aligned16(a_scales) || !aligned16(out))
         return fail(KVQ_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
@@ -474,11 +506,12 @@ struct WidePlan {
     size_t ws_bytes;
 };
 
-// rows > 32: all rows per workgroup (MTW = ceil(rows/32) 16-row tiles per
-// wave), 128-column tiles, and enough K slices to give ~256 workgroups.
+// rows > 32: all rows per workgroup (MTW = ceil(rows/64) 16-row tiles per
+// wave, 4 waves along rows), 128-column tiles, and enough K slices to give
+// ~256 workgroups.
 WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
     WidePlan p;
-    p.mtw = (rows + 31) / 32;
+    p.mtw = (rows + 63) / 64;
     p.ntiles = (ntotal + kWideN - 1) / kWideN;
     const uint32_t nkb = k / 128;
     uint32_t sp = 256 / (p.ntiles ? p.ntiles : 1);
@@ -509,24 +542,24 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
         else pl.splits = 1;
     }
     const unsigned grid = pl.ntiles * pl.splits;
-#define KVQ_WIDE(MTW)                                                                                           \
-    do {                                                                                                        \
-        if (kind == W8A8_ROWSCALE)                                                                              \
-            w8a8_wide<MTW, 0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles,  \
-                                                      partials);                                                \
-        else                                                                                                    \
-            w8a8_wide<MTW, 1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles,  \
-                                                      partials);                                                \
+    // tiles never straddle segments when every non-last segment is a multiple of 128 rows
+    bool uni = true;
+    for (uint32_t i = 0; i + 1 < S.count; ++i) uni = uni && (S.n[i] % kWideN == 0);
+#define KVQ_WIDE3(MTW, KIND, UNI) \
+    w8a8_wide<MTW, KIND, UNI><<<grid, kWideThreads, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles, partials)
+#define KVQ_WIDE(MTW)                                        \
+    do {                                                     \
+        if (kind == W8A8_BLK128) KVQ_WIDE3(MTW, 1, true);    \
+        else if (uni) KVQ_WIDE3(MTW, 0, true);               \
+        else KVQ_WIDE3(MTW, 0, false);                       \
     } while (0)
     switch (pl.mtw) {
+        case 1: KVQ_WIDE(1); break;
         case 2: KVQ_WIDE(2); break;
         case 3: KVQ_WIDE(3); break;
-        case 4: KVQ_WIDE(4); break;
-        case 5: KVQ_WIDE(5); break;
-        case 6: KVQ_WIDE(6); break;
-        case 7: KVQ_WIDE(7); break;
-        default: KVQ_WIDE(8); break;
+        default: KVQ_WIDE(4); break;
     }
+#undef KVQ_WIDE3
 #undef KVQ_WIDE
     int st = launch_status("w8a8_gemv");
     if (st || pl.splits == 1) return st;
