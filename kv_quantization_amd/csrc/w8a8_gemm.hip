@@ -270,10 +270,23 @@ struct WideCfg {
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_INSTR = A_BYTES / 1024 / kWideWaves;   // 1 KiB loads per wave
     static constexpr int B_INSTR = B_BYTES / 1024 / kWideWaves;
-    static constexpr int SA_ROWS = BM / kWideWaves;               // activation scales per wave
-    static constexpr int N_INSTR = A_INSTR + B_INSTR + (KIND == 1 ? 1 : 0);
-    static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SA_ROWS <= 64, "tile shape");
+    static constexpr int SA_ROWS = BM / kWideWaves;               // activation-scale rows per wave
+    static constexpr int SC_INSTR = (SA_ROWS * 4 + 63) / 64;        // dword loads per wave per chunk
+    static constexpr int SC_BYTES = (BM + 1) * 16;                  // one chunk: [BM rows + sw][4 K blocks]
+    static constexpr int N_INSTR = A_INSTR + B_INSTR;
+    static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SA_ROWS % 8 == 0, "tile shape");
 };
+
+// s_waitcnt vmcnt(base + extra) for a run-time extra in [0, 3]
+template <int BASE>
+__device__ __forceinline__ void wait_vm_plus(uint32_t extra) {
+    switch (extra) {
+        case 0: wait_vm<BASE>(); break;
+        case 1: wait_vm<BASE + 1>(); break;
+        case 2: wait_vm<BASE + 2>(); break;
+        default: wait_vm<BASE + 3>(); break;
+    }
+}
 
 template <int MTW, int KIND, bool UNI>
 __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restrict__ q, const float *__restrict__ sa,
@@ -282,7 +295,8 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
                                                           uint32_t ntiles, float *__restrict__ partials) {
     using C = WideCfg<MTW, KIND>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * C::STAGE];
-    __shared__ __attribute__((aligned(16))) float lds_sa[kStages][kWideWaves][64];
+    // block scales (KIND 1), double-buffered in chunks of 4 K blocks
+    __shared__ __attribute__((aligned(16))) float lds_sc[KIND == 1 ? 2 : 1][KIND == 1 ? C::SC_BYTES / 4 : 4];
     const int lane = lane_id();
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wv >> 1, wn = wv & 1;
@@ -324,20 +338,31 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
             bsrc[j] = S.w[sg] + (size_t)jl * K + chunk;
         }
     }
-    // Block scales of K block kb, one 4-byte load per wave: lanes below
-    // SA_ROWS stage the activation scales of rows w*SA_ROWS + lane (rows past
-    // the end take row 0's: their products are zero), the other lanes the
-    // weight scale of this 128-column band.
-    const float *sasrc = sa;
+    // Block scales travel in chunks of 4 K blocks (kb = 4c .. 4c+3), loaded
+    // with the first stage that needs them: lane i of load j of wave w takes
+    // sa[row][4c + i%4] for row w*SA_ROWS + 16j + i/4 (rows past the end and
+    // K blocks past the array read zero), so a chunk holds [row][4] floats;
+    // wave 0 also loads sw[band][4c .. 4c+3] of this 128-column band behind
+    // the rows.  Scales are re-read from HBM once per 4 K blocks, not per
+    // stage: a per-row 4-byte read touches a whole cache line.
+    const u32x4 rsa = buffer_rsrc(sa, KIND == 1 ? rows * nkb * 4 : 4);
+    u32x4 rsw = rsa;
     if (KIND == 1) {
         const float *sseg = sg0 == 0 ? S.s[0] : (sg0 == 1 ? S.s[1] : S.s[2]);
-        const float *swp = sseg + (size_t)((n0 - seg_start) / 128) * nkb;
-        const uint32_t m = wv * C::SA_ROWS + lane;
-        sasrc = lane < C::SA_ROWS ? sa + (size_t)(m < rows ? m : 0) * nkb : swp;
+        rsw = buffer_rsrc(sseg + (size_t)((n0 - seg_start) / 128) * nkb, nkb * 4);
     }
+    uint32_t scoff[C::SC_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::SC_INSTR; ++j)
+        scoff[j] = ((wv * C::SA_ROWS + 16 * j + (lane >> 2)) * nkb + (lane & 3)) * 4;
 
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
-    const uint32_t sa0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sa[0][0][0]));
+    const uint32_t sc0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sc[0][0]));
+    // number of scale loads this wave adds to stage it
+    auto sc_count = [&](int it) -> uint32_t {
+        if (KIND != 1 || it >= nks || (it != 0 && ((kb0 + it) & 3) != 0)) return 0;
+        return C::SC_INSTR + (wv == 0 ? 1 : 0);
+    };
     auto issue = [&](int it) {
         const uint32_t st = (uint32_t)(it % kStages);
         const uint32_t kb = kb0 + it;
@@ -351,7 +376,18 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
             if (UNI) lds_buf16(rb, boff[j], soff, bbase + (wv * C::B_INSTR + j) * 1024);
             else lds_glb16(bsrc[j] + (size_t)kb * 128, bbase + (wv * C::B_INSTR + j) * 1024);
         }
-        if (KIND == 1) lds_glb4(sasrc + kb, sa0 + (st * kWideWaves + wv) * 256);
+        if (sc_count(it)) {
+            // the chunk offset goes into the per-lane offset, which the
+            // buffer range check covers
+            const uint32_t c4 = (kb & ~3u) * 4;
+            const uint32_t slot = sc0 + ((kb >> 2) & 1) * C::SC_BYTES;
+#pragma unroll
+            for (int j = 0; j < C::SC_INSTR; ++j) {
+                const uint32_t dst = slot + (wv * C::SA_ROWS + 16 * j) * 16;
+                if (16 * j + (lane >> 2) < C::SA_ROWS) lds_buf4(rsa, scoff[j] + c4, 0, dst);
+            }
+            if (wv == 0 && lane < 4) lds_buf4(rsw, lane * 4 + c4, 0, slot + C::BM * 16);
+        }
     };
 
     f32x4 acc[MTW][4];
@@ -363,17 +399,20 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
     if (nks > 0) issue(0);
     if (nks > 1) issue(1);
     for (int it = 0; it < nks; ++it) {
+        // wait for stage it: the loads of later stages may stay in flight
         if (it + 2 < nks) {
             issue(it + 2);
-            wait_vm<2 * C::N_INSTR>();
+            wait_vm_plus<2 * C::N_INSTR>(sc_count(it + 1) + sc_count(it + 2));
         } else if (it + 1 < nks) {
-            wait_vm<C::N_INSTR>();
+            wait_vm_plus<C::N_INSTR>(sc_count(it + 1));
         } else {
             wait_vm<0>();
         }
         __builtin_amdgcn_s_barrier();
         const int st = it % kStages;
-        const float swk = KIND == 1 ? lds_sa[st][0][63] : 1.0f;
+        const uint32_t kbi = kb0 + it;
+        const float *scs = &lds_sc[KIND == 1 ? (kbi >> 2) & 1 : 0][kbi & 3];   // [row * 4] of this K block
+        const float swk = KIND == 1 ? scs[C::BM * 4] : 1.0f;
         const uint8_t *abase = lds + st * C::STAGE;
         const uint8_t *bbase = abase + C::A_BYTES;
         i32x8 b[4];
@@ -394,10 +433,9 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_fp8(a, b[nt], acc[mt][nt]);
             } else {
-                // rows 4g..4g+3 of this M tile: one 16-byte read of the staged scales
+                // rows 4g..4g+3 of this M tile
                 const int r0 = wm * 16 * MTW + mt * 16 + 4 * g;
-                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&lds_sa[st][r0 / C::SA_ROWS][r0 % C::SA_ROWS]);
-                const f32x4 sc = s4 * swk;
+                const f32x4 sc = f32x4{scs[r0 * 4], scs[r0 * 4 + 4], scs[r0 * 4 + 8], scs[r0 * 4 + 12]} * swk;
                 f32x4 p[4];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) p[nt] = mfma_fp8(a, b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -438,22 +476,38 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
 }
 
 // Sum the split-K partials [splits][rows][N] in split order, scale (per-row
-// kind), round to bf16.  One thread per output element.
-template <int KIND>
+// kind), round to bf16.  One thread per 4 consecutive output columns of a row
+// (16-byte partial loads; needs N % 4 == 0, so no 4-column group leaves its
+// row, and per-row segments are multiples of 16 columns, so none straddles a
+// segment), or per column otherwise.
+template <int KIND, int V>
 __global__ __launch_bounds__(kBlock) void w8a8_reduce(const float *__restrict__ partials, uint32_t splits,
                                                       const float *__restrict__ sa, uint32_t rows, Segs S,
                                                       uint16_t *__restrict__ out, uint32_t ldc) {
-    const uint64_t idx = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t idx = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * V;
     const uint64_t total = (uint64_t)rows * S.ntotal;
     if (idx >= total) return;
     const uint32_t m = (uint32_t)(idx / S.ntotal), col = (uint32_t)(idx % S.ntotal);
-    float v = 0.0f;
-    for (uint32_t s = 0; s < splits; ++s) v += partials[(size_t)s * total + idx];
+    float v[V];
+    if (V == 4) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (uint32_t s = 0; s < splits; ++s)
+            a += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(partials + (size_t)s * total + idx));
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = a[e];
+    } else {
+        v[0] = 0.0f;
+        for (uint32_t s = 0; s < splits; ++s) v[0] += partials[(size_t)s * total + idx];
+    }
     if (KIND == 0) {
         const int sg = seg_of(S, col);
-        v = v * sa[m] * S.s[sg][col - S.start[sg]];
+        const float *sw = S.s[sg] + (col - S.start[sg]);
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = v[e] * sa[m] * sw[e];
     }
-    out[(size_t)m * ldc + col] = bf16_rne(v);
+    uint16_t *o = out + (size_t)m * ldc + col;
+#pragma unroll
+    for (int e = 0; e < V; ++e) o[e] = bf16_rne(v[e]);
 }
 
 // --------------------------------------------------------------- host ---
@@ -564,9 +618,15 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
     int st = launch_status("w8a8_gemv");
     if (st || pl.splits == 1) return st;
     const uint64_t total = (uint64_t)rows * S.ntotal;
-    const unsigned rgrid = (unsigned)((total + kBlock - 1) / kBlock);
-    if (kind == W8A8_ROWSCALE) w8a8_reduce<0><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
-    else w8a8_reduce<1><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+    if (S.ntotal % 4 == 0) {
+        const unsigned rgrid = (unsigned)((total / 4 + kBlock - 1) / kBlock);
+        if (kind == W8A8_ROWSCALE) w8a8_reduce<0, 4><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+        else w8a8_reduce<1, 4><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+    } else {
+        const unsigned rgrid = (unsigned)((total + kBlock - 1) / kBlock);
+        if (kind == W8A8_ROWSCALE) w8a8_reduce<0, 1><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+        else w8a8_reduce<1, 1><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+    }
     return launch_status("w8a8_gemv (split-K reduction)");
 }
 
