@@ -488,17 +488,23 @@ __global__ __launch_bounds__(kBlock) void w8a8_reduce(const float *__restrict__ 
     const uint64_t total = (uint64_t)rows * S.ntotal;
     if (idx >= total) return;
     const uint32_t m = (uint32_t)(idx / S.ntotal), col = (uint32_t)(idx % S.ntotal);
-    float v[V];
-    if (V == 4) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (uint32_t s = 0; s < splits; ++s)
-            a += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(partials + (size_t)s * total + idx));
+    // all loads of a batch of 8 splits are issued before the first add, so
+    // the memory latency is paid once per batch, not once per split
+    typedef float fv __attribute__((ext_vector_type(V)));
+    fv acc = {};
+    for (uint32_t s0 = 0; s0 < splits; s0 += 8) {
+        fv t[8];
 #pragma unroll
-        for (int e = 0; e < V; ++e) v[e] = a[e];
-    } else {
-        v[0] = 0.0f;
-        for (uint32_t s = 0; s < splits; ++s) v[0] += partials[(size_t)s * total + idx];
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < splits)
+                t[u] = __builtin_nontemporal_load(reinterpret_cast<const fv *>(partials + (size_t)(s0 + u) * total + idx));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < splits) acc += t[u];
     }
+    float v[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = acc[e];
     if (KIND == 0) {
         const int sg = seg_of(S, col);
         const float *sw = S.s[sg] + (col - S.start[sg]);
