@@ -29,6 +29,7 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-ffp-contract=off",          # the quantizers are specified op by op; no silent FMA
+    "-mllvm", "-amdgpu-mfma-vgpr-form",   # MFMA accumulators in VGPRs: no AGPR copies in the epilogues
     "-fno-gpu-rdc",
     # keep packed fp32 VALU forms (v_pk_fma/mul/add_f32) out of the code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

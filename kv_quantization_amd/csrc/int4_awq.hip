@@ -338,7 +338,9 @@ Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles) {
     pl.u = piece_steps(pl.mt, gs / 32);
     const uint32_t npieces = k / (32 * pl.u);
     const uint64_t units = (uint64_t)ntiles * pl.nchunks;
-    uint64_t waves = kTargetWaves / (units ? units : 1);
+    // 2 <= m <= 16 streams the same weights as m = 1 with four times the
+    // matrix work per word: fewer, longer K slices exchange fewer partials
+    uint64_t waves = (m > 1 && m <= 16 ? kTargetWaves / 2 : kTargetWaves) / (units ? units : 1);
     if (waves > npieces) waves = npieces;
     pl.ks_b = (uint32_t)(waves / 4 ? waves / 4 : 1);
     const size_t tiles = (size_t)ntiles * pl.nchunks;

@@ -66,6 +66,18 @@ def test_shapes(m, gs):
     _check(x, projs, gs, _run(x, projs, gs), f"m={m} gs={gs}")
 
 
+@pytest.mark.parametrize("m", [33, 64, 100, 129, 256])
+@pytest.mark.parametrize("gs", [32, 64, 128, 256])
+def test_shapes_wide_m(m, gs):
+    # m > 32 (several row chunks per column tile), a partial last column tile
+    # (n = 96) and several K slices, with and without the workspace
+    print_case("int4 wide-m shapes", m, gs)
+    k = 1024
+    x, projs = synth.int4_awq(m, k, (256, 96, 96), gs, seed=1700 + m + gs)
+    _check(x, projs, gs, _run(x, projs, gs), f"m={m} gs={gs}")
+    _check(x, projs, gs, _run(x, projs, gs, use_workspace=False), f"nows m={m} gs={gs}")
+
+
 @pytest.mark.parametrize("m", [1, 16, 40])
 def test_without_workspace_same_bits_order_independent(m):
     print_case("int4 workspace vs none", m)
