@@ -175,6 +175,9 @@ def capture(torch, fns, stream):
 
 # ---------------------------------------------------------- cpu baseline --
 
+CPU_SECONDS = 10.0
+
+
 def cpu_baseline(host_inputs, table):
     """The oracle, as it stands, over one full step on the same inputs."""
     import oracle
@@ -186,25 +189,32 @@ def cpu_baseline(host_inputs, table):
     wq = [oracle.weight_quant(oracle.ROWSCALE, w) for w in qkv.weights]
     wd = [oracle.weight_quant(oracle.BLK128, w) for w in down.weights]
     awq = [(p.qweight, p.scales, p.zeros) for p in projs]
+    def one_step():
+        c8, s8 = oracle.kv_int8_quant(kv_x)
+        oracle.kv_int8_dequant(c8, s8)
+        p4, s4, z4 = oracle.kv_int4_quant(kv_x, KV_GS)
+        oracle.kv_int4_dequant(p4, s4, z4, KV_T, KV_D, KV_GS)
+        for m in QKV_MS:
+            q, sa = oracle.act_quant(oracle.ROWSCALE, qkv.x_bf16[:m], QKV_K)
+            oracle.w8a8_gemv(oracle.ROWSCALE, q, sa, wq)
+        for m in DOWN_MS:
+            q, sa = oracle.act_quant(oracle.BLK128, down.x_bf16[:m], DOWN_K, silu=True)
+            oracle.w8a8_gemv(oracle.BLK128, q, sa, wd)
+        for m in AWQ_MS:
+            oracle.int4_awq_qkv(x5[:m], awq, AWQ_GS)
+
+    # whole steps until about 10 s of CPU work (at most 30 steps)
+    steps = 0
     t0 = time.perf_counter()
-    c8, s8 = oracle.kv_int8_quant(kv_x)
-    oracle.kv_int8_dequant(c8, s8)
-    p4, s4, z4 = oracle.kv_int4_quant(kv_x, KV_GS)
-    oracle.kv_int4_dequant(p4, s4, z4, KV_T, KV_D, KV_GS)
-    for m in QKV_MS:
-        q, sa = oracle.act_quant(oracle.ROWSCALE, qkv.x_bf16[:m], QKV_K)
-        oracle.w8a8_gemv(oracle.ROWSCALE, q, sa, wq)
-    for m in DOWN_MS:
-        q, sa = oracle.act_quant(oracle.BLK128, down.x_bf16[:m], DOWN_K, silu=True)
-        oracle.w8a8_gemv(oracle.BLK128, q, sa, wd)
-    for m in AWQ_MS:
-        oracle.int4_awq_qkv(x5[:m], awq, AWQ_GS)
+    while steps < 30 and (steps == 0 or time.perf_counter() - t0 < CPU_SECONDS):
+        one_step()
+        steps += 1
     seconds = time.perf_counter() - t0
-    total = sum(r[1] for r in table)
+    total = sum(r[1] for r in table) * steps
     return {"value": round(total / seconds / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "one full step on the same inputs (every kernel at every M; products as fp64 numpy "
-                      "matmuls), offline weight quantization excluded, %.1f s" % seconds}
+            "sample": "%d full steps on the same inputs (every kernel at every M; products as fp64 numpy "
+                      "matmuls), offline weight quantization excluded, %.1f s" % (steps, seconds)}
 
 
 def tensors_of(s):

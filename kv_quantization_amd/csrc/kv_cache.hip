@@ -22,7 +22,10 @@ namespace {
 
 constexpr int kBlock = 256;           // 4 waves
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kUnroll = 4;            // 16-byte loads in flight per lane
+// 16-byte loads per lane per wave.  Small waves measured faster: the loads
+// of many short waves spread over the whole kernel instead of one burst.
+constexpr int kQuantUnroll = 2;
+constexpr int kDequantUnroll = 2;
 
 __device__ __forceinline__ uint32_t int8_code(float v, float s) {
     int c = (int)__builtin_rintf(v / s);
@@ -313,8 +316,8 @@ extern "C" int kvq_quant_int8_token(const float *x, int8_t *codes, float *scales
     const int L = team_lanes(head_dim);
     hipStream_t s = as_stream(stream);
     if (L) {
-        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int8_quant_team<LL, kUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kQuantUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int8_quant_team<LL, kQuantUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
                                (const f32x4 *)x, (uint32_t *)codes, scales, num_tokens)));
     } else {
         int8_quant_wave<<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(x, codes, scales, num_tokens,
@@ -330,8 +333,8 @@ extern "C" int kvq_dequant_int8_token(const int8_t *codes, const float *scales, 
     const int L = team_lanes(head_dim);
     hipStream_t s = as_stream(stream);
     if (L) {
-        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int8_dequant_team<LL, kUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kDequantUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int8_dequant_team<LL, kDequantUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
                                (const uint32_t *)codes, scales, (f32x4 *)y, num_tokens)));
     } else {
         int8_dequant_wave<<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(codes, scales, y, num_tokens,
@@ -358,8 +361,8 @@ extern "C" int kvq_quant_int4_group(const float *x, uint8_t *packed, float *scal
     const int L = team_lanes(group_size);
     hipStream_t s = as_stream(stream);
     if (L) {
-        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int4_quant_team<LL, kUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kQuantUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int4_quant_team<LL, kQuantUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
                                (const f32x4 *)x, (uint16_t *)packed, scales, zeros, groups)));
     } else {
         int4_quant_wave<<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(x, packed, scales, zeros, groups,
@@ -376,8 +379,8 @@ extern "C" int kvq_dequant_int4_group(const uint8_t *packed, const float *scales
     const int L = team_lanes(group_size);
     hipStream_t s = as_stream(stream);
     if (L) {
-        const uint64_t per_block = (uint64_t)kWavesPerBlock * kUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int4_dequant_team<LL, kUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kDequantUnroll * (kWave / L);
+        KVQ_TEAM_SWITCH(L, (int4_dequant_team<LL, kDequantUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
                                (const uint16_t *)packed, scales, zeros, (f32x4 *)y, groups)));
     } else {
         int4_dequant_wave<<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(packed, scales, zeros, y, groups,
