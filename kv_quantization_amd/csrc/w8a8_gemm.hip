@@ -82,24 +82,37 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 // ------------------------------------------------------------- skinny ---
 
-// MT 16-row tiles of activations (rows <= 16*MT); KIND 0 per-row, 1 block.
-template <int MT, int KIND>
-__global__ __launch_bounds__(kBlock) void w8a8_skinny(const uint8_t *__restrict__ q, const float *__restrict__ sa,
-                                                      uint32_t rows, uint32_t K, Segs S, uint16_t *__restrict__ out,
-                                                      uint32_t ldc) {
-    __shared__ f32x4 red[4][MT][kWave];
+// rows <= 32: a workgroup owns NT 16-column tiles; its W waves split K, each
+// streaming the weight rows of its slice with 16-byte loads straight into
+// MFMA operands (U K blocks in flight per lane) and the activation rows (L2)
+// as the other operand; partial sums meet in LDS.  MT 16-row tiles of
+// activations (rows <= 16*MT); KIND 0 per-row, 1 block scales.  NT > 1 reuses
+// each activation fragment for several column tiles.
+template <int MT, int NT, int W, int U, int KIND>
+__global__ __launch_bounds__(W * kWave) void w8a8_skinny(const uint8_t *__restrict__ q,
+                                                          const float *__restrict__ sa, uint32_t rows, uint32_t K,
+                                                          Segs S, uint16_t *__restrict__ out, uint32_t ldc) {
+    __shared__ f32x4 red[W][MT * NT][kWave];
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const uint32_t n0 = blockIdx.x * 16u;
-    const int sg = seg_of(S, n0);
-    const uint32_t jloc0 = n0 - S.start[sg];
-    const uint32_t jrow = jloc0 + r16;
-    const bool jok = jrow < S.n[sg];
-    const uint8_t *wrow = S.w[sg] + (size_t)(jok ? jrow : 0) * K + g * 16;
     const uint32_t nkb = K / 128;
-    const uint32_t kb0 = wv * nkb / 4, kb1 = (wv + 1) * nkb / 4;
+    const uint32_t kb0 = wv * nkb / W, kb1 = (wv + 1) * nkb / W;
 
+    int sg[NT];
+    uint32_t jloc0[NT], jrow[NT];
+    bool jok[NT];
+    const uint8_t *wrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t n0 = (blockIdx.x * NT + nt) * 16u;
+        const uint32_t nn = n0 < S.ntotal ? n0 : 0;
+        sg[nt] = seg_of(S, nn);
+        jloc0[nt] = nn - S.start[sg[nt]];
+        jrow[nt] = jloc0[nt] + r16;
+        jok[nt] = n0 < S.ntotal && jrow[nt] < S.n[sg[nt]];
+        wrow[nt] = S.w[sg[nt]] + (size_t)(jok[nt] ? jrow[nt] : 0) * K + g * 16;
+    }
     const uint8_t *arow[MT];
     bool aok[MT];
 #pragma unroll
@@ -108,82 +121,90 @@ __global__ __launch_bounds__(kBlock) void w8a8_skinny(const uint8_t *__restrict_
         aok[mt] = m < rows;
         arow[mt] = q + (size_t)(aok[mt] ? m : 0) * K + g * 16;
     }
-    // per-lane output rows of the result tile (for block scales)
-    f32x4 acc[MT];
+    f32x4 acc[MT][NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    const uint32_t kbs = K / 128;
 
-    constexpr int U = MT >= 3 ? 2 : 4;
+    auto step = [&](uint32_t kb, const i32x8 *b, const i32x8 *a) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (KIND == 0) {
+                    acc[mt][nt] = mfma_fp8(a[mt], b[nt], acc[mt][nt]);
+                } else {
+                    const f32x4 p = mfma_fp8(a[mt], b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+                    const float swb = S.s[sg[nt]][(size_t)(jloc0[nt] / 128) * nkb + kb];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t m = mt * 16 + 4 * g + i;
+                        const float sab = m < rows ? sa[(size_t)m * nkb + kb] : 0.0f;
+                        acc[mt][nt][i] = __builtin_fmaf(p[i], sab * swb, acc[mt][nt][i]);
+                    }
+                }
+            }
+        }
+    };
     uint32_t kb = kb0;
     for (; kb + U <= kb1; kb += U) {
-        i32x8 b[U], a[U][MT];
+        i32x8 b[U][NT], a[U][MT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            b[u] = jok ? load_frag(wrow + (size_t)(kb + u) * 128) : zero8;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) b[u][nt] = jok[nt] ? load_frag(wrow[nt] + (size_t)(kb + u) * 128) : zero8;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 a[u][mt] = aok[mt] ? load_frag_cached(arow[mt] + (size_t)(kb + u) * 128) : zero8;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (KIND == 0) {
-                    acc[mt] = mfma_fp8(a[u][mt], b[u], acc[mt]);
-                } else {
-                    const f32x4 p = mfma_fp8(a[u][mt], b[u], f32x4{0.f, 0.f, 0.f, 0.f});
-                    const float swb = S.s[sg][(size_t)(jloc0 / 128) * kbs + kb + u];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t m = mt * 16 + 4 * g + i;
-                        const float sab = m < rows ? sa[(size_t)m * kbs + kb + u] : 0.0f;
-                        acc[mt][i] = __builtin_fmaf(p[i], sab * swb, acc[mt][i]);
-                    }
-                }
-            }
-        }
+        for (int u = 0; u < U; ++u) step(kb + u, b[u], a[u]);
     }
     for (; kb < kb1; ++kb) {
-        const i32x8 b = jok ? load_frag(wrow + (size_t)kb * 128) : zero8;
+        i32x8 b[NT], a[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const i32x8 a = aok[mt] ? load_frag_cached(arow[mt] + (size_t)kb * 128) : zero8;
-            if (KIND == 0) {
-                acc[mt] = mfma_fp8(a, b, acc[mt]);
-            } else {
-                const f32x4 p = mfma_fp8(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
-                const float swb = S.s[sg][(size_t)(jloc0 / 128) * kbs + kb];
+        for (int nt = 0; nt < NT; ++nt) b[nt] = jok[nt] ? load_frag(wrow[nt] + (size_t)kb * 128) : zero8;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t m = mt * 16 + 4 * g + i;
-                    const float sab = m < rows ? sa[(size_t)m * kbs + kb] : 0.0f;
-                    acc[mt][i] = __builtin_fmaf(p[i], sab * swb, acc[mt][i]);
-                }
-            }
-        }
+        for (int mt = 0; mt < MT; ++mt) a[mt] = aok[mt] ? load_frag_cached(arow[mt] + (size_t)kb * 128) : zero8;
+        step(kb, b, a);
     }
 
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) red[wv][mt][lane] = acc[mt];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) red[wv][mt * NT + nt][lane] = acc[mt][nt];
     __syncthreads();
-    if (wv < MT) {
-        const int mt = wv;
-        const f32x4 t = red[0][mt][lane] + red[1][mt][lane] + red[2][mt][lane] + red[3][mt][lane];
-        const uint32_t j = n0 + r16;
-        if (jok) {
-            const float sw = KIND == 0 ? S.s[sg][jrow] : 1.0f;
+    for (int t = wv; t < MT * NT; t += W) {
+        const int mt = t / NT, nt = t % NT;
+        f32x4 v = red[0][t][lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += red[w][t][lane];
+        if (jok[nt]) {
+            const uint32_t j = (blockIdx.x * NT + nt) * 16u + r16;
+            const float sw = KIND == 0 ? S.s[sg[nt]][jrow[nt]] : 1.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t m = mt * 16 + 4 * g + i;
                 if (m < rows) {
-                    const float y = KIND == 0 ? t[i] * sa[m] * sw : t[i];
+                    const float y = KIND == 0 ? v[i] * sa[m] * sw : v[i];
                     out[(size_t)m * ldc + j] = bf16_rne(y);
                 }
             }
         }
     }
+}
+
+// launch for rows <= 32
+template <int MT, int NT, int W, int U>
+void skinny_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint32_t rows, uint32_t k,
+                   const Segs &S, uint16_t *out, uint32_t ldc, hipStream_t s) {
+    const unsigned grid = ((S.ntotal + 15) / 16 + NT - 1) / NT;
+    if (kind == W8A8_ROWSCALE)
+        w8a8_skinny<MT, NT, W, U, 0><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+    else
+        w8a8_skinny<MT, NT, W, U, 1><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
 }
 
 // --------------------------------------------------------------- wide ---
@@ -585,14 +606,12 @@ WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
 int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint32_t rows, uint32_t k, const Segs &S,
                 uint16_t *out, uint32_t ldc, void *workspace, size_t workspace_bytes, hipStream_t s) {
     if (rows <= 32) {
-        const unsigned grid = (S.ntotal + 15) / 16;
-        if (rows <= 16) {
-            if (kind == W8A8_ROWSCALE) w8a8_skinny<1, 0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
-            else w8a8_skinny<1, 1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
-        } else {
-            if (kind == W8A8_ROWSCALE) w8a8_skinny<2, 0><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
-            else w8a8_skinny<2, 1><<<grid, kBlock, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
-        }
+        // {MT, NT, W, U}: up to 4 rows, one column tile, 4 K slices, 8 K blocks
+        // in flight; more rows share each activation fragment between two
+        // column tiles (half the activation re-reads); 32 rows use 8 K slices
+        if (rows <= 4) skinny_launch<1, 1, 4, 8>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        else if (rows <= 16) skinny_launch<1, 2, 4, 8>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        else skinny_launch<2, 2, 8, 2>(kind, q, a_scales, rows, k, S, out, ldc, s);
         return launch_status("w8a8_gemv");
     }
     WidePlan pl = wide_plan(rows, k, S.ntotal);

@@ -94,7 +94,7 @@ def test_blk128_down_proj(m):
 
 
 @pytest.mark.parametrize("kind", [0, 1])
-@pytest.mark.parametrize("rows", [1, 3, 16, 17, 33, 63, 64, 65, 100, 255, 256])
+@pytest.mark.parametrize("rows", [1, 3, 4, 5, 8, 16, 17, 32, 33, 63, 64, 65, 100, 255, 256])
 def test_row_counts(kind, rows):
     print_case("w8a8 rows", kind, rows)
     seg_n = (48, 32, 21) if kind == 0 else (128, 256, 77)
