@@ -135,6 +135,14 @@ class StepBuffers:
         self.down_out = {m: e((m, DOWN_N), torch.bfloat16) for m in DOWN_MS}
         self.awq_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_MS}
 
+    def outputs(self):
+        out = [self.kv_codes, self.kv_scales, self.kv_y8, self.kv_packed, self.kv_s4, self.kv_z4, self.kv_y4]
+        for d in (self.qkv_q, self.qkv_sa, self.qkv_out, self.down_q, self.down_sa, self.down_out):
+            out += [d[m] for m in sorted(d)]
+        for m in sorted(self.awq_out):
+            out += self.awq_out[m]
+        return out
+
     # each launcher issues exactly one kernel
     def launchers(self, api):
         s = self.s
@@ -234,6 +242,7 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough for >= 512 MB)")
     ap.add_argument("--kernel-reps", type=int, default=100, help="launches per isolated kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the graph-vs-eager self-check")
     ap.add_argument("--verbose", action="store_true")
     args = ap.parse_args()
 
@@ -299,6 +308,26 @@ def main():
         per_kernel[name] = a.elapsed_time(b) / reps / 1e3     # seconds per launch
         del g
 
+    # ---- self-check: the replayed graphs (which share one cached workspace
+    # across every kernel of a step) must give the same bits as an eager run
+    # on a fresh stream, and so a fresh zero-filled workspace
+    check = "skipped"
+    if not args.no_check:
+        with torch.cuda.stream(stream):
+            step_graphs[0].replay()
+        torch.cuda.synchronize()
+        snap = [t.clone() for t in bufs[0].outputs()]
+        fresh = torch.cuda.Stream()
+        with torch.cuda.stream(fresh):
+            for _, f in launch[0]:
+                f()
+        torch.cuda.synchronize()
+        bad = [i for i, (a, b) in enumerate(zip(snap, bufs[0].outputs())) if not torch.equal(a, b)]
+        if bad:
+            print(f"bench.py: graph replay differs from a fresh eager run in outputs {bad}", file=sys.stderr)
+            sys.exit(1)
+        check = "graph replay == fresh eager run, bit for bit"
+
     breakdown = []
     for name, nbytes, flops, kind in table:
         sec = per_kernel[name]
@@ -332,6 +361,7 @@ def main():
             "input_sets": nsets,
             "step_bytes": step_bytes,
             "timing": "HIP graph per step, rotating input sets (no MALL reuse across steps)",
+            "check": check,
         },
         "roofline": roof,
         "breakdown": breakdown,

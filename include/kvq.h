@@ -45,6 +45,14 @@ const char *kvq_last_error(void);
 /* Library ABI version (major * 100 + minor). */
 int kvq_abi_version(void);
 
+/* Workspaces (w8a8_gemv, w8a8_proj, int4_awq_qkv_gemm): the first
+ * KVQ_WORKSPACE_COUNTER_BYTES bytes hold the counters through which the
+ * workgroups of one output tile find the last of them; every call leaves
+ * them at zero, and partial sums only ever go behind them.  One zero-filled
+ * buffer can therefore serve calls of all three kinds, in any order, as long
+ * as they are ordered on one stream. */
+#define KVQ_WORKSPACE_COUNTER_BYTES 4096u
+
 /* ======================================================================== */
 /* KV cache, symmetric per-token INT8                                       */
 /* [KVQ] sections "INT8 Per-Token Quantization" / "Dequantization".  The
@@ -147,7 +155,9 @@ typedef struct {
  * q, a_scales: as written by w8a8_act_quant; out: bf16 [rows][ldc], ldc >=
  * sum n; columns >= sum n of each row are not touched.
  * workspace: NULL, or device memory of at least w8a8_gemv_workspace_bytes(),
- * zero-filled before its first use; the call leaves it zero-filled again.
+ * zero-filled before its first use.  Split-K partial sums go behind its
+ * counter area (KVQ_WORKSPACE_COUNTER_BYTES), which the call leaves as it
+ * found it, so calls ordered on one stream can reuse the buffer.
  * Without it the call still works, with less parallelism for large rows.
  * Concurrent calls must not share a workspace. */
 int w8a8_gemv(w8a8_scale_t kind, const uint8_t *q, const float *a_scales,

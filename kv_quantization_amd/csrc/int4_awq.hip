@@ -35,9 +35,9 @@
 // and out-of-range lanes read zeros.  A workgroup's 4 waves take 4 K slices of
 // the same tile and meet in LDS; when more K slices are needed to fill the
 // GPU, workgroups exchange fp32 partial tiles through the caller's workspace
-// with agent-coherent (sc1) stores and loads, and the last workgroup of a tile
-// (a relaxed agent-scope counter) adds them in slice order and resets the
-// counter.
+// with device-scope (sc1) stores and loads, which bypass the per-XCD L2s that
+// are not coherent with each other, and an agent-scope counter; the last
+// workgroup of a tile adds them in slice order and resets the counter.
 #include "kvq_common.h"
 
 namespace kvq {
@@ -295,8 +295,11 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
     }
     if (ks_b == 1) return;
 
-    // Cross-workgroup K reduction (see the header comment).
-    __builtin_amdgcn_s_waitcnt(0);
+    // Cross-workgroup K reduction (see the header comment): every thread's
+    // device-scope stores have completed before the barrier, so they are
+    // visible at the coherence point before the counter moves; the last
+    // workgroup's device-scope loads are issued after it has seen the count.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(&counters[tile_id], 1u, __ATOMIC_RELAXED,
@@ -344,7 +347,8 @@ Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles) {
     if (waves > npieces) waves = npieces;
     pl.ks_b = (uint32_t)(waves / 4 ? waves / 4 : 1);
     const size_t tiles = (size_t)ntiles * pl.nchunks;
-    pl.counter_bytes = pl.ks_b > 1 ? ((tiles * 4 + 255) / 256) * 256 : 0;
+    if (tiles * 4 > KVQ_WORKSPACE_COUNTER_BYTES) pl.ks_b = 1;   // more tiles than counters: no exchange
+    pl.counter_bytes = pl.ks_b > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;
     pl.partial_bytes = pl.ks_b > 1 ? tiles * pl.ks_b * pl.mr * 128 * 4 : 0;
     return pl;
 }

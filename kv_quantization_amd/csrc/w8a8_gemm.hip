@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
         __builtin_amdgcn_s_barrier();   // this stage is refilled by the issue() two iterations on
     }
 
-    // ---- epilogue: bf16 output (no split) or fp32 partial tile
+    // ---- epilogue: bf16 output (no split) or fp32 partial tile [split][rows][N]
     float *part = partials + (size_t)split * rows * S.ntotal;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -584,6 +584,7 @@ int check_gemv(const char *fn, w8a8_scale_t kind, const uint8_t *q, const float 
 
 struct WidePlan {
     uint32_t mtw, ntiles, splits;
+    size_t counter_bytes;    // the workspace's counter area, left untouched
     size_t ws_bytes;
 };
 
@@ -599,7 +600,8 @@ WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
     if (sp > nkb) sp = nkb;
     if (sp < 1) sp = 1;
     p.splits = sp;
-    p.ws_bytes = sp > 1 ? (size_t)sp * rows * ntotal * sizeof(float) : 0;
+    p.counter_bytes = sp > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;   // partials go behind the counters
+    p.ws_bytes = sp > 1 ? p.counter_bytes + (size_t)sp * rows * ntotal * sizeof(float) : 0;
     return p;
 }
 
@@ -617,15 +619,18 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
     WidePlan pl = wide_plan(rows, k, S.ntotal);
     float *partials = nullptr;
     if (pl.splits > 1) {
-        if (workspace && workspace_bytes >= pl.ws_bytes && aligned16(workspace)) partials = static_cast<float *>(workspace);
-        else pl.splits = 1;
+        if (workspace && workspace_bytes >= pl.ws_bytes && aligned16(workspace))
+            partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.counter_bytes);
+        else
+            pl.splits = 1;
     }
     const unsigned grid = pl.ntiles * pl.splits;
     // tiles never straddle segments when every non-last segment is a multiple of 128 rows
     bool uni = true;
     for (uint32_t i = 0; i + 1 < S.count; ++i) uni = uni && (S.n[i] % kWideN == 0);
 #define KVQ_WIDE3(MTW, KIND, UNI) \
-    w8a8_wide<MTW, KIND, UNI><<<grid, kWideThreads, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles, partials)
+    w8a8_wide<MTW, KIND, UNI><<<grid, kWideThreads, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles, \
+                                                             partials)
 #define KVQ_WIDE(MTW)                                        \
     do {                                                     \
         if (kind == W8A8_BLK128) KVQ_WIDE3(MTW, 1, true);    \

@@ -142,3 +142,21 @@ def test_proj_equals_act_quant_then_gemv(kind, silu, with_up):
     np.testing.assert_array_equal(host(q), qo)
     ref, bound = _oracle.w8a8_gemv(kind, qo, so, [_oracle.weight_quant(kind, w) for w in inp.weights])
     _check(b, ref, bound, "proj")
+
+
+def test_shared_workspace_across_calls():
+    """One workspace serves split-K calls of every kind in turn: the counters
+    each call leaves at zero sit in a fixed area that no partial sum reaches."""
+    print_case("w8a8 shared workspace")
+    a = synth.w8a8(70, 512, (48, 32, 21), seed=601)     # N % 4 != 0: separate reduction kernel
+    b = synth.w8a8(70, 512, (64, 64, 64), seed=602)     # N % 4 == 0: sums inside the GEMM
+    x4, projs = synth.int4_awq(64, 1024, (256, 64, 64), 128, seed=603)
+    for _ in range(2):
+        for inp, what in ((a, "reduce kernel"), (b, "in-GEMM sums")):
+            _case(0, inp.x_bf16, 512, inp.weights, 70, what=f"shared workspace, {what}")
+        outs = api.int4_awq_qkv(dev(x4), [(dev(p.qweight.view(np.int32)), dev(p.scales), dev(p.zeros)) for p in projs],
+                                128)
+        torch.cuda.synchronize()
+        refs = _oracle.int4_awq_qkv(x4, [(p.qweight, p.scales, p.zeros) for p in projs], 128)
+        for o, (r, bnd) in zip(outs, refs):
+            assert np.all(np.abs(host(o).astype(np.float64) - r) <= 1e-3 * bnd), "int4 with shared workspace"
