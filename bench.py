@@ -183,6 +183,26 @@ def capture(torch, fns, stream):
 
 # ---------------------------------------------------------- cpu baseline --
 
+# HBM traffic of the dominant call (fetched + written bytes), from rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE passes over kv_quantization_amd/
+# traffic_probe.py, scaled by what the same counters read for a 256 MiB
+# device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Reported only while the
+# GEMM source is the one the counters were taken on.
+TRAFFIC = {"kernel": "w8a8_gemm_blk128_M256", "bytes": 175076455,
+           "source": "kv_quantization_amd/csrc/w8a8_gemm.hip",
+           "sha256": "ff86de7c66fbd9a76e1a67e2b1de7ab660dff5e5cac5421f9d5cf5f2b4662f08"}
+
+
+def measured_traffic(kernel):
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC["source"])
+    try:
+        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return TRAFFIC["bytes"] if kernel == TRAFFIC["kernel"] and digest == TRAFFIC["sha256"] else None
+
+
 CPU_SECONDS = 10.0
 
 
@@ -339,7 +359,7 @@ def main():
     dom = max(table, key=lambda r: per_kernel[r[0]])
     roof = roofline_for(*dom, per_kernel[dom[0]])
     roof["kernel"] = dom[0]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom[0])
 
     result = {
         "metric": METRIC,
