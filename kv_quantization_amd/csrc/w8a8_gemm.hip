@@ -322,7 +322,10 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wv >> 1, wn = wv & 1;
     const int r16 = lane & 15, g = lane >> 4;
-    const uint32_t tile = blockIdx.x % ntiles, split = blockIdx.x / ntiles;
+    // consecutive workgroups take the K slices of one column tile: with the
+    // usual round-robin dispatch over the 8 XCDs each XCD then works on few
+    // K slices, so fewer copies of the activation tile sit in its L2
+    const uint32_t split = blockIdx.x % splits, tile = blockIdx.x / splits;
     const uint32_t n0 = tile * kWideN;
     const uint32_t nkb = K / 128;
     const uint32_t kb0 = (uint32_t)((uint64_t)split * nkb / splits);
