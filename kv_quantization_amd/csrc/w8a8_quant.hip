@@ -121,8 +121,11 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 
 // ------------------------------------------------------------- kernels ---
 
-// One workgroup per row; the row's codes depend on one scale, so the values
-// are recomputed (from L2) in a second pass after the block-wide absmax.
+// One workgroup per row; the row's codes depend on one scale.  Rows of up to
+// kRowCached * 8 * 256 columns stay in registers between the block-wide
+// absmax and the encoding (one read of the row); longer rows are read again
+// (from L2) in a second pass.
+constexpr int kRowCached = 4;   // 8-value chunks per thread kept in registers
 template <bool SILU, bool UP>
 __global__ __launch_bounds__(kBlock) void act_quant_row(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ up, uint32_t ldx,
@@ -133,14 +136,34 @@ __global__ __launch_bounds__(kBlock) void act_quant_row(const uint16_t *__restri
     const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + (size_t)r * ldx);
     const u32x4 *ur = UP ? reinterpret_cast<const u32x4 *>(up + (size_t)r * ldx) : nullptr;
     u32x2 *qr = reinterpret_cast<u32x2 *>(q + (size_t)r * k);
-    float v[8];
+    const uint32_t nc = k / 8;
     float m = 0.0f;
-    for (uint32_t c = threadIdx.x; c < k / 8; c += kBlock) {
+    if (nc <= (uint32_t)kBlock * kRowCached) {
+        float v[kRowCached][8];
+#pragma unroll
+        for (int j = 0; j < kRowCached; ++j) {
+            const uint32_t c = threadIdx.x + j * kBlock;
+            if (c < nc) {
+                load8_bf16<SILU, UP>(xr, ur, c, v[j]);
+                m = fmaxf(m, absmax8(v[j]));
+            }
+        }
+        const float s = act_scale(block_max(m, red));
+#pragma unroll
+        for (int j = 0; j < kRowCached; ++j) {
+            const uint32_t c = threadIdx.x + j * kBlock;
+            if (c < nc) qr[c] = encode8(v[j], s);
+        }
+        if (threadIdx.x == 0) scales[r] = s;
+        return;
+    }
+    float v[8];
+    for (uint32_t c = threadIdx.x; c < nc; c += kBlock) {
         load8_bf16<SILU, UP>(xr, ur, c, v);
         m = fmaxf(m, absmax8(v));
     }
     const float s = act_scale(block_max(m, red));
-    for (uint32_t c = threadIdx.x; c < k / 8; c += kBlock) {
+    for (uint32_t c = threadIdx.x; c < nc; c += kBlock) {
         load8_bf16<SILU, UP>(xr, ur, c, v);
         qr[c] = encode8(v, s);
     }

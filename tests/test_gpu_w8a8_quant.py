@@ -48,7 +48,7 @@ def test_act_quant_g128_silu_down_shape(m, with_up):
 
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("silu,with_up", [(False, False), (True, False), (True, True)])
-@pytest.mark.parametrize("rows,k,ldx", [(1, 128, 128), (3, 384, 392), (256, 256, 256), (5, 2176, 2176)])
+@pytest.mark.parametrize("rows,k,ldx", [(1, 128, 128), (3, 384, 392), (256, 256, 256), (5, 2176, 2176), (2, 14336, 14344)])
 def test_act_quant_edges(kind, silu, with_up, rows, k, ldx):
     print_case("act edges", kind, silu, with_up, rows, k, ldx)
     inp = synth.w8a8(rows, ldx, (128,), seed=rows + k + ldx, with_up=with_up)
