@@ -269,9 +269,6 @@ __device__ __forceinline__ void lds_buf4(u32x4 rsrc, uint32_t voff, uint32_t sof
 __device__ __forceinline__ void lds_glb16(const void *g, uint32_t lds_wave_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_glb4(const void *g, uint32_t lds_wave_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
-}
 #pragma clang diagnostic pop
 
 // wait until at most N vector-memory operations of this wave are outstanding
