@@ -188,9 +188,9 @@ def capture(torch, fns, stream):
 # traffic_probe.py, scaled by what the same counters read for a 256 MiB
 # device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Reported only while the
 # GEMM source is the one the counters were taken on.
-TRAFFIC = {"kernel": "w8a8_gemm_blk128_M256", "bytes": 175076455,
+TRAFFIC = {"kernel": "w8a8_gemm_blk128_M256", "bytes": 132752804,
            "source": "kv_quantization_amd/csrc/w8a8_gemm.hip",
-           "sha256": "ff86de7c66fbd9a76e1a67e2b1de7ab660dff5e5cac5421f9d5cf5f2b4662f08"}
+           "sha256": "c2c74ee84464a1f7d89aad3d57cb09ff22fe18c018c1e58278bc972fe14c6c1b"}
 
 
 def measured_traffic(kernel):
