@@ -420,16 +420,15 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
     if (nks > 0) issue(0);
     if (nks > 1) issue(1);
     for (int it = 0; it < nks; ++it) {
-        // wait for stage it: the loads of later stages may stay in flight
-        if (it + 2 < nks) {
-            issue(it + 2);
-            wait_vm_plus<2 * C::N_INSTR>(sc_count(it + 1) + sc_count(it + 2));
-        } else if (it + 1 < nks) {
-            wait_vm_plus<C::N_INSTR>(sc_count(it + 1));
-        } else {
-            wait_vm<0>();
-        }
-        __builtin_amdgcn_s_barrier();
+        // this wave's loads of stage it have landed (stage it+1 may stay in
+        // flight); after the barrier so have everyone's, and everyone has
+        // finished multiplying stage it-1, whose buffer the next issue
+        // refills.  One barrier per K step; the asm form keeps LDS accesses
+        // on their side of it without waiting for the loads in flight.
+        if (it + 1 < nks) wait_vm_plus<C::N_INSTR>(sc_count(it + 1));
+        else wait_vm<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (it + 2 < nks) issue(it + 2);
         const int st = it % kStages;
         const uint32_t kbi = kb0 + it;
         const float *scs = &lds_sc[KIND == 1 ? (kbi >> 2) & 1 : 0][kbi & 3];   // [row * 4] of this K block
@@ -466,7 +465,6 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
                     for (int e = 0; e < 4; ++e) acc[mt][nt][e] = __builtin_fmaf(p[nt][e], sc[e], acc[mt][nt][e]);
             }
         }
-        __builtin_amdgcn_s_barrier();   // this stage is refilled by the issue() two iterations on
     }
 
     // ---- epilogue: bf16 output (no split) or fp32 partial tile [split][rows][N]
