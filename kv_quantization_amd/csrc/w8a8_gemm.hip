@@ -228,7 +228,6 @@ void skinny_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, u
 // (deterministic), applies per-row scales and writes bf16.
 
 constexpr int kWideN = 128;
-constexpr int kStages = 3;
 constexpr int kWideWaves = 8;
 constexpr int kWideThreads = kWideWaves * kWave;
 
@@ -292,6 +291,11 @@ struct WideCfg {
     static constexpr int SC_INSTR = (SA_ROWS * 4 + 63) / 64;        // dword loads per wave per chunk
     static constexpr int SC_BYTES = (BM + 1) * 16;                  // one chunk: [BM rows + sw][4 K blocks]
     static constexpr int N_INSTR = A_INSTR + B_INSTR;
+    // LDS ring depth: double buffering (one K step in flight while one is
+    // multiplied) measured fastest; 3..5 stages were slower (more loads in
+    // flight per CU, no better latency hiding).  At most 5 in any case: the
+    // double-buffered scale chunks are refilled 8 K blocks apart.
+    static constexpr int ST = 2;
     static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SA_ROWS % 8 == 0, "tile shape");
 };
 
@@ -306,13 +310,27 @@ __device__ __forceinline__ void wait_vm_plus(uint32_t extra) {
     }
 }
 
+// wait until at most `later` stages of N loads (plus `extra`, <= 3) are in flight
+template <int N, int MAXL>
+__device__ __forceinline__ void wait_stages(int later, uint32_t extra) {
+    if constexpr (MAXL >= 3) {
+        if (later == 3) { wait_vm_plus<3 * N>(extra); return; }
+    }
+    if constexpr (MAXL >= 2) {
+        if (later == 2) { wait_vm_plus<2 * N>(extra); return; }
+    }
+    if (later == 1) { wait_vm_plus<N>(extra); return; }
+    wait_vm<0>();
+}
+
+
 template <int MTW, int KIND, bool UNI>
 __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restrict__ q, const float *__restrict__ sa,
                                                           uint32_t rows, uint32_t K, Segs S,
                                                           uint16_t *__restrict__ out, uint32_t ldc, uint32_t splits,
                                                           uint32_t ntiles, float *__restrict__ partials) {
     using C = WideCfg<MTW, KIND>;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::ST * C::STAGE];
     // block scales (KIND 1), double-buffered in chunks of 4 K blocks
     __shared__ __attribute__((aligned(16))) float lds_sc[KIND == 1 ? 2 : 1][KIND == 1 ? C::SC_BYTES / 4 : 4];
     const int lane = lane_id();
@@ -385,7 +403,7 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
         return C::SC_INSTR + (wv == 0 ? 1 : 0);
     };
     auto issue = [&](int it) {
-        const uint32_t st = (uint32_t)(it % kStages);
+        const uint32_t st = (uint32_t)(it % C::ST);
         const uint32_t kb = kb0 + it;
         const uint32_t abase = lds0 + st * C::STAGE;
         const uint32_t bbase = abase + C::A_BYTES;
@@ -417,19 +435,21 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (nks > 0) issue(0);
-    if (nks > 1) issue(1);
+    for (int i = 0; i < C::ST - 1 && i < nks; ++i) issue(i);
     for (int it = 0; it < nks; ++it) {
-        // this wave's loads of stage it have landed (stage it+1 may stay in
+        // this wave's loads of stage it have landed (later stages may stay in
         // flight); after the barrier so have everyone's, and everyone has
         // finished multiplying stage it-1, whose buffer the next issue
         // refills.  One barrier per K step; the asm form keeps LDS accesses
         // on their side of it without waiting for the loads in flight.
-        if (it + 1 < nks) wait_vm_plus<C::N_INSTR>(sc_count(it + 1));
-        else wait_vm<0>();
+        int later = nks - 1 - it;
+        if (later > C::ST - 2) later = C::ST - 2;
+        uint32_t extra = 0;
+        for (int j = 1; j <= later; ++j) extra += sc_count(it + j);
+        wait_stages<C::N_INSTR, C::ST - 2>(later, extra);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (it + 2 < nks) issue(it + 2);
-        const int st = it % kStages;
+        if (it + C::ST - 1 < nks) issue(it + C::ST - 1);
+        const int st = it % C::ST;
         const uint32_t kbi = kb0 + it;
         const float *scs = &lds_sc[KIND == 1 ? (kbi >> 2) & 1 : 0][kbi & 3];   // [row * 4] of this K block
         const float swk = KIND == 1 ? scs[C::BM * 4] : 1.0f;
