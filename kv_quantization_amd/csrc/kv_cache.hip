@@ -27,17 +27,19 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kQuantUnroll = 2;
 constexpr int kDequantUnroll = 2;
 
-__device__ __forceinline__ uint32_t int8_code(float v, float s) {
-    int c = (int)__builtin_rintf(v / s);
+// y = 1/s (see div_by_scale)
+__device__ __forceinline__ uint32_t int8_code(float v, float s, float y) {
+    int c = (int)__builtin_rintf(div_by_scale(v, s, y));
     c = c < -128 ? -128 : (c > 127 ? 127 : c);
     return (uint32_t)c & 0xFFu;
 }
 
 __device__ __forceinline__ float int8_scale(float amax) { return fmaxf(amax / 127.0f, 1e-8f); }
 
-__device__ __forceinline__ uint32_t int4_code(float v, float mn, float sf) {
+// y = 1/sf (see div_by_scale)
+__device__ __forceinline__ uint32_t int4_code(float v, float mn, float sf, float y) {
     float d = v - mn;
-    int c = (int)__builtin_rintf(d / sf);
+    int c = (int)__builtin_rintf(div_by_scale(d, sf, y));
     c = c < 0 ? 0 : (c > 15 ? 15 : c);
     return (uint32_t)c;
 }
@@ -72,8 +74,9 @@ __global__ __launch_bounds__(kBlock) void int8_quant_team(const f32x4 *__restric
     for (int u = 0; u < U; ++u) {
         const uint64_t t = t0 + (uint64_t)u * TPI;
         const float s = int8_scale(team_max<L>(abs_max4(v[u])));
-        const uint32_t packed = int8_code(v[u].x, s) | (int8_code(v[u].y, s) << 8) |
-                                (int8_code(v[u].z, s) << 16) | (int8_code(v[u].w, s) << 24);
+        const float y = 1.0f / s;
+        const uint32_t packed = int8_code(v[u].x, s, y) | (int8_code(v[u].y, s, y) << 8) |
+                                (int8_code(v[u].z, s, y) << 16) | (int8_code(v[u].w, s, y) << 24);
         if (t < num_tokens) {
             codes[t * L + li] = packed;
             if (li == 0) scales[t] = s;
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void int8_quant_wave(const float *__restric
     const float s = int8_scale(team_max<kWave>(m));
     if (lane_id() == 0) scales[t] = s;
     for (uint32_t d = lane_id(); d < head_dim; d += kWave)
-        codes[t * head_dim + d] = (int8_t)(uint8_t)int8_code(row[d], s);
+        codes[t * head_dim + d] = (int8_t)(uint8_t)int8_code(row[d], s, 1.0f / s);
 }
 
 template <int L, int U>
@@ -165,8 +168,9 @@ __global__ __launch_bounds__(kBlock) void int4_quant_team(const f32x4 *__restric
         const float s = (mx - mn) / 15.0f;
         const float sf = fmaxf(s, 1e-8f);
         const float z = -mn / sf;
-        const uint32_t p = int4_code(v[u].x, mn, sf) | (int4_code(v[u].y, mn, sf) << 4) |
-                           (int4_code(v[u].z, mn, sf) << 8) | (int4_code(v[u].w, mn, sf) << 12);
+        const float y = 1.0f / sf;
+        const uint32_t p = int4_code(v[u].x, mn, sf, y) | (int4_code(v[u].y, mn, sf, y) << 4) |
+                           (int4_code(v[u].z, mn, sf, y) << 8) | (int4_code(v[u].w, mn, sf, y) << 12);
         if (g < num_groups) {
             packed[g * L + li] = (uint16_t)p;
             if (li == 0) {
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(kBlock) void int4_quant_wave(const float *__restric
     }
     uint8_t *out = packed + g * (group_size / 2);
     for (uint32_t p = lane_id(); p < group_size / 2; p += kWave)
-        out[p] = (uint8_t)(int4_code(grp[2 * p], mn, sf) | (int4_code(grp[2 * p + 1], mn, sf) << 4));
+        out[p] = (uint8_t)(int4_code(grp[2 * p], mn, sf, 1.0f / sf) | (int4_code(grp[2 * p + 1], mn, sf, 1.0f / sf) << 4));
 }
 
 template <int L, int U>

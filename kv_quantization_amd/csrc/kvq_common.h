@@ -56,4 +56,21 @@ __device__ __forceinline__ float team_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// RN(v / s) for a quantization scale s (normal, >= 1e-8) given y = RN(1/s),
+// in three operations instead of a full IEEE division: Markstein's sequence
+// (q = RN(v y); the residual v - q s is exact by FMA; RN(q + residual * y))
+// yields the correctly rounded quotient whenever the residual does not
+// underflow.  It can only underflow for |v| below about 2^-100, i.e. for
+// quotients below 2^-70 here (s >= 1e-8), far under every code boundary
+// (E4M3's smallest half-step 2^-10, rint's 0.5), so the codes equal those
+// of an IEEE division.  The sequence turns -0 / s into +0, so zeros pass
+// through unchanged (E4M3 has a negative-zero code).  (Checked on 2e9 random
+// pairs: same sign always, and every value mismatch had a quotient below
+// 2^-82.)
+__device__ __forceinline__ float div_by_scale(float v, float s, float y) {
+    const float q = v * y;
+    const float r = __builtin_fmaf(__builtin_fmaf(-q, s, v), y, q);
+    return v == 0.0f ? v : r;
+}
+
 }  // namespace kvq

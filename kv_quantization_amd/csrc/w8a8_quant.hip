@@ -102,10 +102,13 @@ __device__ __forceinline__ float absmax8(const float v[8]) {
     return m;
 }
 
-__device__ __forceinline__ u32x2 encode8(const float v[8], float s) {
+// y = 1/s (see div_by_scale)
+__device__ __forceinline__ u32x2 encode8(const float v[8], float s, float y) {
     u32x2 r;
-    r.x = e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
-    r.y = e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
+    r.x = e4m3x4(div_by_scale(v[0], s, y), div_by_scale(v[1], s, y), div_by_scale(v[2], s, y),
+                 div_by_scale(v[3], s, y));
+    r.y = e4m3x4(div_by_scale(v[4], s, y), div_by_scale(v[5], s, y), div_by_scale(v[6], s, y),
+                 div_by_scale(v[7], s, y));
     return r;
 }
 
@@ -149,10 +152,11 @@ __global__ __launch_bounds__(kBlock) void act_quant_row(const uint16_t *__restri
             }
         }
         const float s = act_scale(block_max(m, red));
+        const float y = 1.0f / s;
 #pragma unroll
         for (int j = 0; j < kRowCached; ++j) {
             const uint32_t c = threadIdx.x + j * kBlock;
-            if (c < nc) qr[c] = encode8(v[j], s);
+            if (c < nc) qr[c] = encode8(v[j], s, y);
         }
         if (threadIdx.x == 0) scales[r] = s;
         return;
@@ -163,9 +167,10 @@ __global__ __launch_bounds__(kBlock) void act_quant_row(const uint16_t *__restri
         m = fmaxf(m, absmax8(v));
     }
     const float s = act_scale(block_max(m, red));
+    const float y = 1.0f / s;
     for (uint32_t c = threadIdx.x; c < nc; c += kBlock) {
         load8_bf16<SILU, UP>(xr, ur, c, v);
-        qr[c] = encode8(v, s);
+        qr[c] = encode8(v, s, y);
     }
     if (threadIdx.x == 0) scales[r] = s;
 }
@@ -185,8 +190,9 @@ __global__ __launch_bounds__(kBlock) void act_quant_g128(const uint16_t *__restr
     float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (ok) load8_bf16<SILU, UP>(xr, ur, col / 8, v);
     const float s = act_scale(team_max<16>(absmax8(v)));
+    const float y = 1.0f / s;
     if (ok) {
-        *reinterpret_cast<u32x2 *>(q + (size_t)r * k + col) = encode8(v, s);
+        *reinterpret_cast<u32x2 *>(q + (size_t)r * k + col) = encode8(v, s, y);
         if (li == 0) scales[(size_t)r * (k / 128) + col / 128] = s;
     }
 }
@@ -205,9 +211,10 @@ __global__ __launch_bounds__(kBlock) void weight_quant_row(const float *__restri
         m = fmaxf(m, absmax8(v));
     }
     const float s = act_scale(block_max(m, red));
+    const float y = 1.0f / s;
     for (uint32_t c = threadIdx.x; c < k / 8; c += kBlock) {
         load8_f32(wr, c, v);
-        qr[c] = encode8(v, s);
+        qr[c] = encode8(v, s, y);
     }
     if (threadIdx.x == 0) scales[j] = s;
 }

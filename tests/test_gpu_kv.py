@@ -97,3 +97,15 @@ def test_degenerate_inputs():
     _int8_case(x)
     _int4_case(x, 32)
     _int4_case(x, 2)
+
+
+def test_wide_range_codes():
+    # magnitudes over many binades per token / group: the codes of the
+    # reciprocal-and-correction division must equal the oracle's IEEE division
+    print_case("kv wide range")
+    rng = np.random.default_rng(78)
+    top = np.exp2(rng.uniform(-30, 30, (4096, 1)))
+    x = (top * np.exp2(-rng.uniform(0, 24, (4096, 128))) * rng.choice([-1.0, 1.0], (4096, 128))).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] = 0.0
+    _int8_case(x)
+    _int4_case(x, 32)

@@ -118,3 +118,23 @@ def test_e4m3_encoder_ragged(n):
     torch.cuda.synchronize()
     assert_bits_equal(host(out), _oracle.e4m3_encode(x), "e4m3")
     assert_canary(raw, n)
+
+
+def _wide_range(rows, k, seed):
+    """Rows whose magnitudes span many binades (log-uniform 2^-40 .. 2^40 per
+    row, elements log-uniform over 2^-30 of that, random signs, some exact
+    zeros and row maxima): quotients v / s land on every E4M3 code boundary."""
+    rng = np.random.default_rng(seed)
+    top = np.exp2(rng.uniform(-40, 40, (rows, 1)))
+    x = top * np.exp2(-rng.uniform(0, 30, (rows, k))) * rng.choice([-1.0, 1.0], (rows, k))
+    x[rng.random((rows, k)) < 0.01] = 0.0
+    x[:, 0] = top[:, 0]
+    return synth.to_bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_act_quant_wide_range_codes(kind):
+    # the encoders divide by the scale with a reciprocal and one correction
+    # step; codes must still equal those of an IEEE division (the oracle's)
+    print_case("act wide range", kind)
+    _act_case(_wide_range(256, 8192, 77 + kind), 8192, kind)
