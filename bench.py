@@ -188,9 +188,9 @@ def capture(torch, fns, stream):
 # traffic_probe.py, scaled by what the same counters read for a 256 MiB
 # device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Reported only while the
 # GEMM source is the one the counters were taken on.
-TRAFFIC = {"kernel": "w8a8_gemm_blk128_M256", "bytes": 132752804,
+TRAFFIC = {"kernel": "w8a8_gemm_blk128_M256", "bytes": 136096741,
            "source": "kv_quantization_amd/csrc/w8a8_gemm.hip",
-           "sha256": "c2c74ee84464a1f7d89aad3d57cb09ff22fe18c018c1e58278bc972fe14c6c1b"}
+           "sha256": "46e08ac4bbddf11ccd73bb01feaaaed2e9804bb81fbed6bf9f49cd6ae0bd194f"}
 
 
 def measured_traffic(kernel):
@@ -267,8 +267,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU; every kernel here runs on a single MI355X "
-              "(see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: measures one GPU only; every kernel here runs on a single MI355X "
+              "and no multi-GPU path exists. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
