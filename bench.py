@@ -5,7 +5,9 @@ One *step* is one pass over every kernel of the path, each at its workload
 shape, on one set of synthetic inputs already resident in HBM:
 
   KV cache 32768 x 128 fp32: INT8 per-token quant + dequant, INT4 g32 quant + dequant
-  W8A8 per-row fused QKV (K=4096, N=4096+1024+1024): act-quant + GEMV at M = 1, 8, 32
+  W8A8 per-row fused QKV (K=4096, N=4096+1024+1024): projection with the
+    activation quantization inside the GEMV (one launch) at M = 1, 8;
+    act-quant + GEMV at M = 32
   W8A8 128x128-block down projection (K=14336, N=4096): SiLU g128 act-quant + GEMM at M = 64, 128, 256
   INT4 AWQ fused QKV (K=4096, N=4096+1024+1024, g128): GEMV/GEMM at M = 1, 16, 128
 
@@ -38,6 +40,7 @@ QKV_K, QKV_SEG = 4096, (4096, 1024, 1024)
 DOWN_K, DOWN_N = 14336, 4096
 AWQ_K, AWQ_NS, AWQ_GS = 4096, (4096, 1024, 1024), 128
 QKV_MS, DOWN_MS, AWQ_MS = (1, 8, 32), (64, 128, 256), (1, 16, 128)
+FUSED_MAX_ROWS = 8             # w8a8_proj is one launch up to this many rows
 
 
 # ----------------------------------------------------------- work model ---
@@ -53,6 +56,12 @@ def kernel_table():
     rows.append(("kv_int4_dequant", kv_in + KV_T * KV_D // 2 + g * 8, 0, "hbm"))
     n = sum(QKV_SEG)
     for m in QKV_MS:
+        if m <= FUSED_MAX_ROWS:
+            # bf16 activations in, codes + scales to the scratch, weights, bf16 out
+            rows.append((f"w8a8_proj_rowscale_M{m}",
+                         m * QKV_K * 2 + m * QKV_K + m * 4 + n * QKV_K + n * 4 + m * n * 2,
+                         2 * m * n * QKV_K, "fp8"))
+            continue
         rows.append((f"w8a8_act_quant_row_M{m}", m * QKV_K * 2 + m * QKV_K + m * 4, 0, "hbm"))
         rows.append((f"w8a8_gemv_rowscale_M{m}", n * QKV_K + n * 4 + m * QKV_K + m * 4 + m * n * 2,
                      2 * m * n * QKV_K, "fp8"))
@@ -154,6 +163,11 @@ class StepBuffers:
         L.append(("kv_int4_dequant", lambda: api.dequant_int4_group(self.kv_packed, self.kv_s4, self.kv_z4, KV_T,
                                                                      KV_D, KV_GS, self.kv_y4)))
         for m in QKV_MS:
+            if m <= FUSED_MAX_ROWS:
+                L.append((f"w8a8_proj_rowscale_M{m}",
+                          lambda m=m: api.proj(s["qkv_x"][:m], self.qkv_weight, out=self.qkv_out[m],
+                                               scratch=(self.qkv_q[m], self.qkv_sa[m]))))
+                continue
             L.append((f"w8a8_act_quant_row_M{m}",
                       lambda m=m: api.act_quant(s["qkv_x"][:m], QKV_K, api.ROWSCALE, False, None, self.qkv_q[m],
                                                 self.qkv_sa[m])))

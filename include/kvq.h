@@ -169,7 +169,12 @@ int w8a8_gemv(w8a8_scale_t kind, const uint8_t *q, const float *a_scales,
 int w8a8_gemv_workspace_bytes(w8a8_scale_t kind, uint32_t rows, uint32_t k,
                               uint32_t n_total, size_t *bytes);
 
-/* w8a8_proj: act_quant into (q, a_scales) then gemv, on one stream. */
+/* w8a8_proj: act_quant into (q, a_scales) then gemv, on one stream.  With
+ * rows <= 8 (and, for ROWSCALE, k <= 4096) it is ONE launch: the GEMV kernel
+ * quantizes the activations itself, writes the same codes and scales to
+ * (q, a_scales) and returns the same output bits as the two-step form;
+ * otherwise two launches.  The workspace is used only by the two-launch
+ * form (see w8a8_gemv). */
 int w8a8_proj(w8a8_scale_t kind, int silu, const uint16_t *x,
               const uint16_t *up, uint32_t ldx, uint32_t rows, uint32_t k,
               const w8a8_segment_t *segs, uint32_t nseg, uint16_t *out,

@@ -184,12 +184,21 @@ def gemv(q: torch.Tensor, a_scales: torch.Tensor, weight: W8a8Weight, out=None, 
     return out
 
 
-def proj(x: torch.Tensor, weight: W8a8Weight, silu: bool = False, up=None, out=None):
-    """act_quant + gemv in one call (metrale w8a8_proj)."""
+def proj(x: torch.Tensor, weight: W8a8Weight, silu: bool = False, up=None, out=None, scratch=None):
+    """act_quant + gemv in one call (metrale w8a8_proj); one launch for <= 8
+    rows.  scratch: optional (codes uint8 [rows, k], scales fp32) that receive
+    the activation codes and scales."""
     rows, ldx = x.shape
     k = weight.k
-    q = _empty((rows, k), torch.uint8, x)
-    sa = _empty((rows,) if weight.kind == ROWSCALE else (rows, k // 128), torch.float32, x)
+    if scratch is None:
+        q = _empty((rows, k), torch.uint8, x)
+        sa = _empty((rows,) if weight.kind == ROWSCALE else (rows, k // 128), torch.float32, x)
+    else:
+        q, sa = scratch
+        _dev(q, torch.uint8, "scratch codes")
+        _dev(sa, torch.float32, "scratch scales")
+        if q.numel() < rows * k or sa.numel() < rows * (1 if weight.kind == ROWSCALE else k // 128):
+            raise ValueError("scratch buffers too small for rows x k")
     n = weight.n
     out = _empty((rows, n), torch.bfloat16, x) if out is None else out
     stream = _stream(x)

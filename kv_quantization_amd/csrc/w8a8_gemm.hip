@@ -29,6 +29,7 @@
 // accumulator (fp32 accumulation throughout; products of two E4M3 values are
 // exact in the MFMA).
 #include "kvq_common.h"
+#include "w8a8_act.h"
 
 namespace kvq {
 namespace {
@@ -50,6 +51,10 @@ struct Segs {
 __device__ __forceinline__ int seg_of(const Segs &S, uint32_t j) {
     return (S.count > 1 && j >= S.start[1]) ? ((S.count > 2 && j >= S.start[2]) ? 2 : 1) : 0;
 }
+
+// Cache-policy operand of the buffer intrinsics for streamed weights: nt
+// (non-temporal), as the nontemporal global loads below.
+constexpr int kAuxNt = 2;
 
 __device__ __forceinline__ i32x8 load_frag(const uint8_t *p) {
     // 16 bytes at p and 16 bytes at p + 64 (see the operand layout above)
@@ -205,6 +210,259 @@ void skinny_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, u
         w8a8_skinny<MT, NT, W, U, 0><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
     else
         w8a8_skinny<MT, NT, W, U, 1><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+}
+
+// --------------------------------------------------------- fused proj ---
+//
+// rows <= kFusedRows: w8a8_proj in one launch.  The skinny GEMV above, with
+// each workgroup quantizing the activations it needs itself: it reads the
+// bf16 rows (from L2 after the first touch), computes the scales and codes
+// with the same arithmetic as the stand-alone quantizer, and hands the codes
+// to the MFMAs through a per-wave LDS area.  Workgroup 0 also writes codes
+// and scales to the caller's scratch, as the two-launch form does.  K split,
+// operand layout and accumulation order are those of w8a8_skinny<1, NT, 4,
+// U>, so the output equals that of act_quant + gemv bit for bit.
+//
+// Per wave and chunk of U K blocks: activation loads first, then the weight
+// loads, so the in-order load counter lets the encoding run while the weights
+// are still in flight.  Per-row scales need the whole row's absmax, i.e. a
+// workgroup barrier after every wave has its part; the host keeps per-row
+// calls to one chunk per wave (K <= 4 * U * 128), where that barrier sits
+// between the first loads and the first MFMAs.  Block scales are local to
+// one 128-column group (a 16-lane team) and any K works.
+constexpr uint32_t kFusedRows = 8;
+
+// R: activation rows the kernel is built for (rows <= R); W waves split K.
+template <int NT, int R, int W, int U, int KIND, bool SILU, bool UP>
+__global__ __launch_bounds__(W * kWave) void w8a8_fused(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ up, uint32_t ldx, uint32_t rows, uint32_t K, Segs S,
+    uint16_t *__restrict__ out, uint32_t ldc, uint8_t *__restrict__ qout, float *__restrict__ saout) {
+    constexpr int XJ = U / 4;          // 16-byte activation loads per row per chunk (64 lanes x 8 values)
+    constexpr int RS = U * 128 + 16;   // byte stride of a staged code row (padded against bank conflicts)
+    static_assert(U % 4 == 0, "a chunk is a whole number of 4-block wave loads");
+    __shared__ __attribute__((aligned(16))) uint8_t lq[W][R][RS];
+    __shared__ float lgs[W][R][U];
+    __shared__ float lamax[W][R];
+    __shared__ float ls[R];
+    __shared__ f32x4 red[W][NT][kWave];
+    const int lane = lane_id();
+    const int wv = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const uint32_t nkb = K / 128;
+    const uint32_t kb0 = wv * nkb / W, kb1 = (wv + 1) * nkb / W;
+    const bool writer = blockIdx.x == 0;
+
+    // weights through buffer resources (one per column tile; a tile lies in
+    // one segment), activations through one over the rows used
+    int sg[NT];
+    uint32_t jloc0[NT], jrow[NT], woff[NT];
+    bool jok[NT];
+    rsrc_t rw[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t n0 = (blockIdx.x * NT + nt) * 16u;
+        const uint32_t nn = n0 < S.ntotal ? n0 : 0;
+        sg[nt] = seg_of(S, nn);
+        jloc0[nt] = nn - pick(sg[nt], S.start[0], S.start[1], S.start[2]);
+        jrow[nt] = jloc0[nt] + r16;
+        const uint32_t segn = pick(sg[nt], S.n[0], S.n[1], S.n[2]);
+        jok[nt] = n0 < S.ntotal && jrow[nt] < segn;
+        rw[nt] = make_rsrc(pick(sg[nt], S.w[0], S.w[1], S.w[2]), segn * K);
+        woff[nt] = jok[nt] ? jrow[nt] * K + g * 16 : kOffNone;
+    }
+    const uint32_t xbytes = ((rows - 1) * ldx + K) * 2;
+    const rsrc_t rx = make_rsrc(x, xbytes);
+    const rsrc_t ru = make_rsrc(UP ? up : x, xbytes);
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    // lane's 8 activation values of load j: block 4j + g of the chunk,
+    // columns 8*r16 .. +7; rows >= rows and blocks past the chunk read zeros
+    u32x4 xw[R][XJ], xu[R][XJ];
+    i32x8 b[U][NT];
+    auto load_chunk = [&](uint32_t kbc, uint32_t nb) {
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) {
+                const bool ok = (uint32_t)m < rows && (uint32_t)(4 * j + g) < nb;
+                const uint32_t off = ok ? (m * ldx + kbc * 128 + j * 512 + lane * 8) * 2 : kOffNone;
+                xw[m][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+                if (UP) xu[m][j] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const uint32_t off = (uint32_t)u < nb ? woff[nt] + (kbc + u) * 128 : kOffNone;
+                const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], off, 0, kAuxNt);
+                const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], off, 64, kAuxNt);
+                b[u][nt] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        }
+        // issue every load before any use: the first wait on an activation
+        // must not hold back the weight loads behind it
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // (an empty slice loads nothing and leaves zeros)
+    load_chunk(kb0, kb1 - kb0 < (uint32_t)U ? kb1 - kb0 : (uint32_t)U);
+
+    if (KIND == 0) {
+        // row absmax: this wave's part, then across the waves (one chunk per wave)
+        float am[R];
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            am[m] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) {
+                float v[8];
+                act8<SILU, UP>(xw[m][j], xu[m][j], v);
+                am[m] = fmaxf(am[m], absmax8(v));
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < R; ++m) am[m] = wave_absmax_dpp(am[m]);
+        if (lane == 0) {
+#pragma unroll
+            for (int m = 0; m < R; ++m) lamax[wv][m] = am[m];
+        }
+        // barriers over LDS only: the weight loads stay in flight
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (threadIdx.x < R) {
+            float am = lamax[0][threadIdx.x];
+#pragma unroll
+            for (int w = 1; w < W; ++w) am = fmaxf(am, lamax[w][threadIdx.x]);
+            const float s = act_scale(am);
+            ls[threadIdx.x] = s;
+            if (writer && threadIdx.x < rows) saout[threadIdx.x] = s;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+
+    for (uint32_t kbc = kb0; kbc < kb1; kbc += U) {
+        const uint32_t nb = kb1 - kbc < (uint32_t)U ? kb1 - kbc : (uint32_t)U;
+        if (kbc != kb0) load_chunk(kbc, nb);
+        // codes (and block scales) of the chunk -> this wave's LDS rows
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            if ((uint32_t)m >= rows) break;
+            const float srow = KIND == 0 ? ls[m] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) {
+                const uint32_t blk = 4 * j + g;
+                const bool ok = blk < nb;
+                float v[8];
+                act8<SILU, UP>(xw[m][j], xu[m][j], v);
+                const float s = KIND == 0 ? srow : act_scale(team_absmax_dpp<16>(absmax8(v)));
+                const float y = 1.0f / s;
+                const u32x2 c = encode8(v, s, y);
+                if (ok) {
+                    *reinterpret_cast<u32x2 *>(&lq[wv][m][blk * 128 + r16 * 8]) = c;
+                    if (KIND == 1 && r16 == 0) lgs[wv][m][blk] = s;
+                    if (writer) {
+                        *reinterpret_cast<u32x2 *>(qout + (size_t)m * K + (size_t)(kbc + blk) * 128 + r16 * 8) = c;
+                        if (KIND == 1 && r16 == 0) saout[(size_t)m * nkb + kbc + blk] = s;
+                    }
+                }
+            }
+        }
+        // the LDS writes above were made by other lanes of this wave; a wave's
+        // LDS operations complete in order, so only code motion must be stopped
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if ((uint32_t)u >= nb) break;
+            i32x8 a = zero8;
+            if ((uint32_t)r16 < rows) {
+                const u32x4 lo = *reinterpret_cast<const u32x4 *>(&lq[wv][r16][u * 128 + g * 16]);
+                const u32x4 hi = *reinterpret_cast<const u32x4 *>(&lq[wv][r16][u * 128 + 64 + g * 16]);
+                a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+                a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (KIND == 0) {
+                    acc[nt] = mfma_fp8(a, b[u][nt], acc[nt]);
+                } else {
+                    const f32x4 p = mfma_fp8(a, b[u][nt], f32x4{0.f, 0.f, 0.f, 0.f});
+                    const float swb = S.s[sg[nt]][(size_t)(jloc0[nt] / 128) * nkb + kbc + u];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t m = 4 * g + i;
+                        const float sab = m < rows ? lgs[wv][m][u] : 0.0f;
+                        acc[nt][i] = __builtin_fmaf(p[i], sab * swb, acc[nt][i]);
+                    }
+                }
+            }
+        }
+        // the next chunk overwrites this wave's LDS rows
+        asm volatile("" ::: "memory");
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) red[wv][nt][lane] = acc[nt];
+    __syncthreads();
+    for (int nt = wv; nt < NT; nt += W) {
+        f32x4 v = red[0][nt][lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += red[w][nt][lane];
+        if (jok[nt]) {
+            const uint32_t j = (blockIdx.x * NT + nt) * 16u + r16;
+            const float sw = KIND == 0 ? S.s[sg[nt]][jrow[nt]] : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t m = 4 * g + i;
+                if (m < rows) {
+                    const float y = KIND == 0 ? v[i] * ls[m] * sw : v[i];
+                    out[(size_t)m * ldc + j] = bf16_rne(y);
+                }
+            }
+        }
+    }
+}
+
+// Shapes {NT, W, U} shared by the skinny GEMV and the fused projection for
+// the same row counts (same K split, so both forms give the same bits): up
+// to 4 rows one column tile, 4 K slices, 8 K blocks in flight; 5..8 rows two
+// column tiles (each activation fragment serves both) over 8 K slices of 4
+// blocks, which halves each wave's share of the activation encoding.
+// W * U is kFusedMaxBlocksRow: with per-row scales K may have that many
+// 128-blocks (one chunk per wave).
+constexpr uint32_t kFusedMaxBlocksRow = 32;
+
+// Whether w8a8_proj runs as one launch (see the fused kernel's comment).
+bool fused_ok(w8a8_scale_t kind, uint32_t rows, uint32_t k, uint32_t ldx) {
+    return rows <= kFusedRows && (kind == W8A8_BLK128 || k / 128 <= kFusedMaxBlocksRow) &&
+           ((uint64_t)(rows - 1) * ldx + k) * 2 < 0x80000000ull;
+}
+
+template <int NT, int W, int U, int KIND, bool SILU, bool UP>
+void fused_launch3(const uint16_t *x, const uint16_t *up, uint32_t ldx, uint32_t rows, uint32_t k, const Segs &S,
+                   uint16_t *out, uint32_t ldc, uint8_t *q, float *a_scales, hipStream_t s) {
+    static_assert(W * U == (int)kFusedMaxBlocksRow, "per-row scales: one chunk per wave");
+    const unsigned grid = ((S.ntotal + 15) / 16 + NT - 1) / NT;
+    w8a8_fused<NT, 4 * NT, W, U, KIND, SILU, UP><<<grid, W * kWave, 0, s>>>(x, up, ldx, rows, k, S, out, ldc, q,
+                                                                            a_scales);
+}
+
+template <int NT, int W, int U>
+void fused_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t *up, uint32_t ldx, uint32_t rows,
+                  uint32_t k, const Segs &S, uint16_t *out, uint32_t ldc, uint8_t *q, float *a_scales,
+                  hipStream_t s) {
+#define KVQ_FUSED(KIND)                                                                                               \
+    do {                                                                                                              \
+        if (!silu) fused_launch3<NT, W, U, KIND, false, false>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);    \
+        else if (!up) fused_launch3<NT, W, U, KIND, true, false>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);  \
+        else fused_launch3<NT, W, U, KIND, true, true>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);            \
+    } while (0)
+    if (kind == W8A8_ROWSCALE) KVQ_FUSED(0);
+    else KVQ_FUSED(1);
+#undef KVQ_FUSED
 }
 
 // --------------------------------------------------------------- wide ---
@@ -626,10 +884,11 @@ WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
 int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint32_t rows, uint32_t k, const Segs &S,
                 uint16_t *out, uint32_t ldc, void *workspace, size_t workspace_bytes, hipStream_t s) {
     if (rows <= 32) {
-        // {MT, NT, W, U}: up to 4 rows, one column tile, 4 K slices, 8 K blocks
-        // in flight; more rows share each activation fragment between two
-        // column tiles (half the activation re-reads); 32 rows use 8 K slices
+        // {MT, NT, W, U}: up to 8 rows as the fused projection (see there); up
+        // to 16 rows two column tiles per activation fragment (half the
+        // activation re-reads), 4 K slices; 32 rows use 8 K slices
         if (rows <= 4) skinny_launch<1, 1, 4, 8>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        else if (rows <= 8) skinny_launch<1, 2, 8, 4>(kind, q, a_scales, rows, k, S, out, ldc, s);
         else if (rows <= 16) skinny_launch<1, 2, 4, 8>(kind, q, a_scales, rows, k, S, out, ldc, s);
         else skinny_launch<2, 2, 8, 2>(kind, q, a_scales, rows, k, S, out, ldc, s);
         return launch_status("w8a8_gemv");
@@ -715,6 +974,12 @@ extern "C" int w8a8_proj(w8a8_scale_t kind, int silu, const uint16_t *x, const u
     Segs S;
     st = check_gemv("w8a8_proj", kind, q, a_scales, rows, k, segs, nseg, out, ldc, &S);
     if (st) return st;
+    if (fused_ok(kind, rows, k, ldx)) {
+        // one launch: the GEMV quantizes the activations itself (and fills q, a_scales)
+        if (rows <= 4) fused_launch<1, 4, 8>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
+        else fused_launch<2, 8, 4>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
+        return launch_status("w8a8_proj");
+    }
     st = act_quant_launch(kind, silu, x, up, ldx, rows, k, q, a_scales, as_stream(stream));
     if (st) return st;
     return gemv_launch(kind, q, a_scales, rows, k, S, out, ldc, workspace, workspace_bytes, as_stream(stream));

@@ -160,3 +160,52 @@ def test_shared_workspace_across_calls():
         refs = _oracle.int4_awq_qkv(x4, [(p.qweight, p.scales, p.zeros) for p in projs], 128)
         for o, (r, bnd) in zip(outs, refs):
             assert np.all(np.abs(host(o).astype(np.float64) - r) <= 1e-3 * bnd), "int4 with shared workspace"
+
+
+# w8a8_proj with <= 8 rows is one launch (the GEMV quantizes its activations);
+# its output must equal act_quant + gemv bit for bit, its scratch must hold the
+# oracle's codes and scales, and the output must meet the oracle's bound.
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("silu,with_up", [(False, False), (True, False), (True, True)])
+@pytest.mark.parametrize("rows,k,seg_n", [(1, 128, (16,)), (3, 384, (48, 32, 21)), (4, 1152, (256, 128, 77)),
+                                          (5, 4096, (128, 256)), (8, 4096, (1024, 256, 100)),
+                                          (2, 4736, (256, 31)), (8, 14336, (256,)), (6, 8192, (128, 128))])
+def test_proj_single_launch(kind, silu, with_up, rows, k, seg_n):
+    if kind == 1 and any(n % 128 for n in seg_n[:-1]):
+        pytest.skip("BLK128 needs 128-aligned non-last segments")
+    print_case("w8a8 proj fused", kind, silu, with_up, rows, k, seg_n)
+    inp = synth.w8a8(rows, k + 8, seg_n, seed=700 + rows + k, with_up=with_up)
+    xb = inp.x_bf16.copy()
+    if rows >= 3:
+        xb[1] = 0                                   # zero row: floor scale
+    segs = [_oracle.weight_quant(kind, w[:, :k].copy()) for w in inp.weights]
+    weight = api.W8a8Weight(kind, [(dev(q), dev(s)) for q, s in segs])
+    x = dev(xb)                                     # ldx = k + 8
+    up = None if inp.up_bf16 is None else dev(inp.up_bf16)
+    sshape = (rows,) if kind == 0 else (rows, k // 128)
+    q, raw_q = poisoned((rows, k), torch.uint8)
+    sa, raw_s = poisoned(sshape, torch.float32)
+    b = host(api.proj(x, weight, silu=silu, up=up, scratch=(q, sa)))
+    q2, sa2 = api.act_quant(x, k, kind, silu, up)
+    a = host(api.gemv(q2, sa2, weight))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a.view(np.uint16), b.view(np.uint16))
+    qo, so = _oracle.act_quant(kind, xb, k, silu=silu, up_bf16=inp.up_bf16)
+    np.testing.assert_array_equal(host(q), qo)
+    np.testing.assert_array_equal(host(sa).view(np.uint32), so.view(np.uint32))
+    assert_canary(raw_q, rows * k)
+    assert_canary(raw_s, int(np.prod(sshape)) * 4)
+    ref, bound = _oracle.w8a8_gemv(kind, qo, so, segs)
+    _check(b, ref, bound, "proj fused")
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_proj_single_launch_qkv_shape(m):
+    print_case("w8a8 proj fused qkv", m)
+    inp = synth.w8a8_qkv()
+    segs, weight = _weights(0, inp.weights)
+    x = dev(inp.x_bf16[:m])
+    b = host(api.proj(x, weight))
+    qo, so = _oracle.act_quant(0, inp.x_bf16[:m], 4096)
+    ref, bound = _oracle.w8a8_gemv(0, qo, so, segs)
+    _check(b, ref, bound, f"proj qkv M={m}", strict=True)
