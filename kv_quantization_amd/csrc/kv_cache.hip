@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void int8_quant_team(const f32x4 *__restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint64_t t = t0 + (uint64_t)u * TPI;
-        const float s = int8_scale(team_max<L>(abs_max4(v[u])));
+        const float s = int8_scale(team_absmax<L>(abs_max4(v[u])));
         const float y = 1.0f / s;
         const uint32_t packed = int8_code(v[u].x, s, y) | (int8_code(v[u].y, s, y) << 8) |
                                 (int8_code(v[u].z, s, y) << 16) | (int8_code(v[u].w, s, y) << 24);
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kBlock) void int8_quant_wave(const float *__restric
     const float *row = x + t * head_dim;
     float m = 0.0f;
     for (uint32_t d = lane_id(); d < head_dim; d += kWave) m = fmaxf(m, fabsf(row[d]));
-    const float s = int8_scale(team_max<kWave>(m));
+    const float s = int8_scale(team_absmax<kWave>(m));
     if (lane_id() == 0) scales[t] = s;
     for (uint32_t d = lane_id(); d < head_dim; d += kWave)
         codes[t * head_dim + d] = (int8_t)(uint8_t)int8_code(row[d], s, 1.0f / s);

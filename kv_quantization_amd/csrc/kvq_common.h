@@ -31,65 +31,60 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- device --
 
-// Butterfly reductions over aligned lane teams of size W (a power of two <=
-// 64); every lane of the team ends with the result.
-template <int W>
-__device__ __forceinline__ float team_max(float v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-
-template <int W>
-__device__ __forceinline__ float team_min(float v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-
-template <int W>
-__device__ __forceinline__ float team_sum(float v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Max of NON-NEGATIVE floats (absolute values) over lane teams with DPP lane
-// moves inside the VALU, no LDS round trip.  Non-negative floats order like
-// their bit patterns as unsigned integers, so the max runs on the bits (no
-// NaN canonicalisation; +0 is the identity, which lanes outside a DPP row
-// mask read).  Steps: swap neighbours, swap pairs, mirror half-rows of 8,
-// mirror rows of 16; after each, a lane holds the max over its aligned 2, 4,
-// 8, 16 lanes.
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
-    return v > o ? v : o;
+// Reductions over aligned lane teams of W = 1..64 lanes, every lane of the
+// team ending with the result, without LDS round trips: DPP lane moves inside
+// the VALU for teams up to a row of 16 (swap neighbours, swap pairs, mirror
+// half-rows of 8, mirror rows of 16: after each step a lane holds the result
+// over its aligned 2, 4, 8, 16 lanes), then v_permlane16_swap (rows 0<->1,
+// 2<->3) and v_permlane32_swap (halves).  Called with both operands equal, a
+// swap returns each lane its own and its partner's value, whichever way the
+// rows move.  The reductions run on integers: finite floats map to signed
+// integers of the same order (-0 just below +0), and non-negative floats
+// (absolute values) are already ordered by their bits.
+template <int CTRL, bool MAX>
+__device__ __forceinline__ int dpp_ext(int v) {
+    const int id = MAX ? (int)0x80000000 : 0x7FFFFFFF;   // identity: what a masked lane reads
+    const int o = __builtin_amdgcn_update_dpp(id, v, CTRL, 0xF, 0xF, false);
+    return MAX ? (v > o ? v : o) : (v < o ? v : o);
 }
 
-// Aligned teams of W <= 16 lanes; every lane of the team gets the result.
+template <int W, bool MAX>
+__device__ __forceinline__ int team_ext(int v) {
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "teams of 1..64 lanes");
+    if (W >= 2) v = dpp_ext<0xB1, MAX>(v);       // quad_perm [1,0,3,2]
+    if (W >= 4) v = dpp_ext<0x4E, MAX>(v);       // quad_perm [2,3,0,1]
+    if (W >= 8) v = dpp_ext<0x141, MAX>(v);      // row_half_mirror
+    if (W >= 16) v = dpp_ext<0x140, MAX>(v);     // row_mirror
+    if (W >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        const int a = (int)r[0], b = (int)r[1];
+        v = MAX ? (a > b ? a : b) : (a < b ? a : b);
+    }
+    if (W >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        const int a = (int)r[0], b = (int)r[1];
+        v = MAX ? (a > b ? a : b) : (a < b ? a : b);
+    }
+    return v;
+}
+
+__device__ __forceinline__ int float_order(float f) {
+    const int b = __float_as_int(f);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float order_float(int o) { return __int_as_float(o ^ ((o >> 31) & 0x7FFFFFFF)); }
+
 template <int W>
-__device__ __forceinline__ float team_absmax_dpp(float a) {
-    static_assert(W == 2 || W == 4 || W == 8 || W == 16, "DPP teams of 2..16 lanes");
-    uint32_t v = __float_as_uint(a);
-    v = dpp_umax<0xB1>(v);                   // quad_perm [1,0,3,2]
-    if (W >= 4) v = dpp_umax<0x4E>(v);       // quad_perm [2,3,0,1]
-    if (W >= 8) v = dpp_umax<0x141>(v);      // row_half_mirror
-    if (W >= 16) v = dpp_umax<0x140>(v);     // row_mirror
-    return __uint_as_float(v);
-}
+__device__ __forceinline__ float team_max(float v) { return order_float(team_ext<W, true>(float_order(v))); }
 
-// The whole wave, as a uniform value: rows of 16 as above, then lane 15 of
-// each row into the next row (rows 1 and 3), lane 31 into rows 2 and 3, and
-// lane 63 (which then holds the max of all four rows) read out.
-__device__ __forceinline__ float wave_absmax_dpp(float a) {
-    uint32_t v = __float_as_uint(team_absmax_dpp<16>(a));
-    v = dpp_umax<0x142, 0xA>(v);             // row_bcast:15
-    v = dpp_umax<0x143, 0xC>(v);             // row_bcast:31
-    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 63));
-}
+template <int W>
+__device__ __forceinline__ float team_min(float v) { return order_float(team_ext<W, false>(float_order(v))); }
+
+// Max of non-negative floats (absolute values).
+template <int W>
+__device__ __forceinline__ float team_absmax(float v) { return __int_as_float(team_ext<W, true>(__float_as_int(v))); }
 
 // Raw buffer resources: loads through them take an SGPR base, a per-lane
 // 32-bit offset and a uniform offset, and a lane whose offset is at or past

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
             }
         }
 #pragma unroll
-        for (int m = 0; m < R; ++m) am[m] = wave_absmax_dpp(am[m]);
+        for (int m = 0; m < R; ++m) am[m] = team_absmax<kWave>(am[m]);
         if (lane == 0) {
 #pragma unroll
             for (int m = 0; m < R; ++m) lamax[wv][m] = am[m];
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
                 const bool ok = blk < nb;
                 float v[8];
                 act8<SILU, UP>(xw[m][j], xu[m][j], v);
-                const float s = KIND == 0 ? srow : act_scale(team_absmax_dpp<16>(absmax8(v)));
+                const float s = KIND == 0 ? srow : act_scale(team_absmax<16>(absmax8(v)));
                 const float y = 1.0f / s;
                 const u32x2 c = encode8(v, s, y);
                 if (ok) {

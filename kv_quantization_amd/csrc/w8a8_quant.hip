@@ -29,7 +29,7 @@ __device__ __forceinline__ void load8_f32(const f32x4 *x, uint32_t idx, float v[
 
 // Max over the 256 threads of the block; every thread gets the result.
 __device__ __forceinline__ float block_max(float v, float *red) {
-    v = team_max<kWave>(v);
+    v = team_absmax<kWave>(v);
     if (lane_id() == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kBlock) void act_quant_g128(const uint16_t *__restr
     const u32x4 *ur = UP ? reinterpret_cast<const u32x4 *>(up + (size_t)r * ldx) : nullptr;
     float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (ok) load8_bf16<SILU, UP>(xr, ur, col / 8, v);
-    const float s = act_scale(team_max<16>(absmax8(v)));
+    const float s = act_scale(team_absmax<16>(absmax8(v)));
     const float y = 1.0f / s;
     if (ok) {
         *reinterpret_cast<u32x2 *>(q + (size_t)r * k + col) = encode8(v, s, y);
