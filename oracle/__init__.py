@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
             "oracle_num_threads": ([], ctypes.c_int),
             "oracle_kv_int8_quant": ([p, p, p, i64, i64], None),
             "oracle_kv_int8_dequant": ([p, p, p, i64, i64], None),
+            "oracle_kv_int8_quant_tensor": ([p, p, p, i64], None),
+            "oracle_kv_int8_dequant_tensor": ([p, ctypes.c_float, p, i64], None),
             "oracle_kv_fp8_quant": ([p, p, p, i64, i64], None),
             "oracle_kv_fp8_dequant": ([p, p, p, i64, i64], None),
             "oracle_kv_int4_quant": ([p, p, p, p, i64, i64, i64], None),
@@ -129,6 +131,28 @@ def kv_int8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     t, d = codes.shape
     y = np.empty((t, d), np.float32)
     lib().oracle_kv_int8_dequant(_p(codes), _p(scales), _p(y), t, d)
+    return y
+
+
+def kv_int8_quant_tensor(x: np.ndarray):
+    """Per-tensor symmetric INT8: the declared ``mode = 0`` of the page's
+    parameter block, read as the per-token rule over the whole tensor.
+
+    x: float32, any shape -> (codes int8, same shape; scale float32 [1])."""
+    x = _c(x, np.float32)
+    _finite(x)
+    codes = np.empty(x.shape, np.int8)
+    scale = np.empty(1, np.float32)
+    lib().oracle_kv_int8_quant_tensor(_p(x), _p(codes), _p(scale), x.size)
+    return codes, scale
+
+
+def kv_int8_dequant_tensor(codes: np.ndarray, scale) -> np.ndarray:
+    """float(code) * scale with the tensor's one scale."""
+    codes = _c(codes, np.int8)
+    y = np.empty(codes.shape, np.float32)
+    lib().oracle_kv_int8_dequant_tensor(_p(codes), float(np.float32(np.asarray(scale).reshape(-1)[0])), _p(y),
+                                        codes.size)
     return y
 
 

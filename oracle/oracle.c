@@ -10,6 +10,7 @@
  * Sources (web pages; each function names the section it follows):
  *   [KVQ]  boostr, src/ops/wgpu/shaders/cache/kv_cache_quant.wgsl
  *          sections "FP8 Per-Token Quantization/Dequantization",
+ *          the declared per-tensor mode of its parameter block,
  *          "INT4 Per-Group Quantization/Dequantization",
  *          "INT8 Per-Token Quantization/Dequantization".
  *   [W8A8] metrale_model_layers, layers/ops/w8a8_decode.rs
@@ -80,6 +81,31 @@ void oracle_kv_int8_dequant(const int8_t *codes, const float *scales, float *y,
         for (i64 d = 0; d < head_dim; ++d)
             y[t * head_dim + d] = (float)codes[t * head_dim + d] * scale;
     }
+}
+
+/* [KVQ] INT8 per-tensor mode.  The page's shared parameter block declares a
+ * mode (0 = per tensor, 1 = per token) but only per-token kernels are on it;
+ * the reading taken here is the per-token rule with the absmax taken over the
+ * whole tensor: one scale = max(absmax / 127, 1e-8) for all n values, codes
+ * = clamp(rint(x / scale), -128, 127).  x is the flattened tensor. */
+void oracle_kv_int8_quant_tensor(const float *x, int8_t *codes, float *scale, i64 n) {
+    float max_val = 0.0f;
+    for (i64 i = 0; i < n; ++i) max_val = fmaxf(max_val, fabsf(x[i]));
+    float s = fmaxf(max_val / 127.0f, 1e-8f);
+    *scale = s;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < n; ++i) {
+        int c = (int)rintf(x[i] / s);
+        if (c < -128) c = -128;
+        if (c > 127) c = 127;
+        codes[i] = (int8_t)c;
+    }
+}
+
+/* [KVQ] INT8 per-tensor dequantization: value = float(code) * scale. */
+void oracle_kv_int8_dequant_tensor(const int8_t *codes, float scale, float *y, i64 n) {
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < n; ++i) y[i] = (float)codes[i] * scale;
 }
 
 /* [KVQ] the page's "FP8" per-token quantizer, transcribed from its own

@@ -128,3 +128,51 @@ def test_int4_pack_positions(oracle_mod):
     packed, s, z = oracle_mod.kv_int4_quant(x, 16)
     assert s[0] == 1.0
     np.testing.assert_array_equal(packed, np.array([(2 * i) | ((2 * i + 1) << 4) for i in range(8)], np.uint8))
+
+
+# ------------------------------------------------- INT8 per-tensor mode ----
+
+def test_int8_tensor_worked_examples(oracle_mod):
+    g = json.loads((GOLDEN / "kv_int8_tensor_worked.json").read_text())
+    for case in g["cases"]:
+        x = np.array(case["x"], np.float32)
+        codes, scale = oracle_mod.kv_int8_quant_tensor(x)
+        np.testing.assert_array_equal(codes, np.array(case["codes"], np.int8))
+        np.testing.assert_array_equal(_bits(scale), _bits(np.array([_hexf(case["scale_hex"])], np.float32)))
+        np.testing.assert_array_equal(oracle_mod.kv_int8_dequant_tensor(codes, scale),
+                                      np.array(case["dequant"], np.float32))
+
+
+@pytest.mark.parametrize("d", [1, 7, 128])
+def test_int8_tensor_single_token_is_per_token(oracle_mod, d):
+    x = synth.kv_cache(1, d, seed=40 + d)
+    c1, s1 = oracle_mod.kv_int8_quant_tensor(x)
+    c2, s2 = oracle_mod.kv_int8_quant(x)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(_bits(s1), _bits(s2))
+
+
+@pytest.mark.parametrize("t,d", [(300, 128), (17, 5)])
+def test_int8_tensor_equals_per_token_with_shared_absmax(oracle_mod, t, d):
+    """Appending the tensor's absmax to every token gives each token that
+    absmax, so the (separately pinned) per-token codec then uses the tensor's
+    scale everywhere and must reproduce the per-tensor codes."""
+    x = synth.kv_cache(t, d, seed=50 + t)
+    codes, scale = oracle_mod.kv_int8_quant_tensor(x)
+    a = np.float32(np.abs(x).max())
+    xa = np.concatenate([x, np.full((t, 1), a, np.float32)], axis=1)
+    c2, s2 = oracle_mod.kv_int8_quant(xa)
+    np.testing.assert_array_equal(_bits(s2), np.full(t, _bits(scale)[0], np.uint32))
+    np.testing.assert_array_equal(codes, c2[:, :d])
+
+
+def test_int8_tensor_bound_and_extremes(oracle_mod):
+    x = synth.kv_cache(2000, 64, seed=60)
+    codes, scale = oracle_mod.kv_int8_quant_tensor(x)
+    s = float(scale[0])
+    assert abs(s - max(float(np.abs(x).astype(np.float64).max()) / 127.0, 1e-8)) <= 2.0 ** -23 * s
+    y = oracle_mod.kv_int8_dequant_tensor(codes, scale)
+    assert np.all(np.abs(x.astype(np.float64) - y) <= s * (0.5 + 2.0 ** -16))
+    i = np.unravel_index(np.abs(x).argmax(), x.shape)
+    assert abs(int(codes[i])) == 127
+    assert codes.min() >= -127 and codes.max() <= 127
