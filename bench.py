@@ -79,6 +79,13 @@ def kernel_table():
     return rows
 
 
+def extra_table():
+    """Kernels timed beside the step but not part of it (the per-tensor KV
+    mode, a widening of the path): (name, algorithmic bytes, flops, kind)."""
+    kv = KV_T * KV_D * 4 + KV_T * KV_D + 4
+    return [("kv_int8_quant_tensor", kv, 0, "hbm"), ("kv_int8_dequant_tensor", kv, 0, "hbm")]
+
+
 def roofline_for(name, nbytes, flops, kind, seconds):
     peak_tf = {"fp8": FP8_PEAK_TFLOPS, "fp16": FP16_PEAK_TFLOPS}.get(kind)
     gbs = nbytes / seconds / 1e9
@@ -134,6 +141,9 @@ class StepBuffers:
         self.kv_s4 = e((g,), torch.float32)
         self.kv_z4 = e((g,), torch.float32)
         self.kv_y4 = e((KV_T, KV_D), torch.float32)
+        self.kvt_codes = e((KV_T, KV_D), torch.int8)
+        self.kvt_scale = e((1,), torch.float32)
+        self.kvt_y = e((KV_T, KV_D), torch.float32)
         self.qkv_weight = api.W8a8Weight(api.ROWSCALE, s["qkv_w"])
         self.down_weight = api.W8a8Weight(api.BLK128, s["down_w"])
         self.qkv_q = {m: e((m, QKV_K), torch.uint8) for m in QKV_MS}
@@ -152,7 +162,13 @@ class StepBuffers:
             out += self.awq_out[m]
         return out
 
-    # each launcher issues exactly one kernel
+    def extra_launchers(self, api):
+        s = self.s
+        return [("kv_int8_quant_tensor", lambda: api.quant_int8_tensor(s["kv_x"], self.kvt_codes, self.kvt_scale)),
+                ("kv_int8_dequant_tensor", lambda: api.dequant_int8_tensor(self.kvt_codes, self.kvt_scale,
+                                                                           self.kvt_y))]
+
+    # each launcher issues exactly one call
     def launchers(self, api):
         s = self.s
         L = []
@@ -220,7 +236,7 @@ def measured_traffic(kernel):
 CPU_SECONDS = 10.0
 
 
-def cpu_baseline(host_inputs, table):
+def cpu_baseline(host_inputs, table, single_core=True):
     """The oracle, as it stands, over one full step on the same inputs."""
     import oracle
     from kv_quantization_amd import synth
@@ -253,10 +269,22 @@ def cpu_baseline(host_inputs, table):
         steps += 1
     seconds = time.perf_counter() - t0
     total = sum(r[1] for r in table) * steps
-    return {"value": round(total / seconds / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%d full steps on the same inputs (every kernel at every M; products as fp64 numpy "
-                      "matmuls), offline weight quantization excluded, %.1f s" % (steps, seconds)}
+    cores = oracle.num_threads()
+    res = {"value": round(total / seconds / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": "%d full steps on the same inputs (every kernel at every M; products as fp64 numpy "
+                     "matmuls), offline weight quantization excluded, %.1f s" % (steps, seconds)}
+    if single_core:
+        # one step on one thread: the oracle's OpenMP loops and numpy's BLAS
+        from threadpoolctl import threadpool_limits
+        oracle.set_num_threads(1)
+        with threadpool_limits(limits=1, user_api="blas"):
+            t0 = time.perf_counter()
+            one_step()
+            s1 = time.perf_counter() - t0
+        oracle.set_num_threads(cores)
+        res["single_thread"] = {"value": round(sum(r[1] for r in table) / s1 / 1e9, 3), "unit": "GB/s",
+                                "sample": "1 full step, oracle loops and BLAS on 1 thread, %.1f s" % s1}
+    return res
 
 
 def tensors_of(s):
@@ -276,6 +304,7 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough for >= 512 MB)")
     ap.add_argument("--kernel-reps", type=int, default=100, help="launches per isolated kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-core", action="store_true", help="skip the one-thread oracle step")
     ap.add_argument("--no-check", action="store_true", help="skip the graph-vs-eager self-check")
     ap.add_argument("--verbose", action="store_true")
     args = ap.parse_args()
@@ -303,10 +332,13 @@ def main():
     bufs = [StepBuffers(torch, api, s) for s in sets]
     launch = [b.launchers(api) for b in bufs]
     assert [n for n, _ in launch[0]] == names
+    xtable = extra_table()
+    xlaunch = [b.extra_launchers(api) for b in bufs]
+    assert [n for n, _ in xlaunch[0]] == [r[0] for r in xtable]
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for L in launch:                    # eager pass: allocates workspaces, checks launches
+        for L in launch + xlaunch:          # eager pass: allocates workspaces, checks launches
             for _, f in L:
                 f()
     torch.cuda.synchronize()
@@ -330,8 +362,10 @@ def main():
     # ---- per-kernel durations (graphs of R launches rotating over the sets)
     per_kernel = {}
     reps = max(nsets, args.kernel_reps // nsets * nsets)
-    for ki, name in enumerate(names):
-        g = capture(torch, [launch[r % nsets][ki][1] for r in range(reps)], stream)
+    timed = [(name, launch, ki) for ki, name in enumerate(names)]
+    timed += [(r[0], xlaunch, ki) for ki, r in enumerate(xtable)]
+    for name, lset, ki in timed:
+        g = capture(torch, [lset[r % nsets][ki][1] for r in range(reps)], stream)
         with torch.cuda.stream(stream):
             g.replay()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -370,6 +404,11 @@ def main():
         if flops:
             entry["TFLOP/s"] = round(flops / sec / 1e12, 2)
         breakdown.append(entry)
+    extras = []
+    for name, nbytes, _, _ in xtable:
+        sec = per_kernel[name]
+        extras.append({"kernel": name, "us": round(sec * 1e6, 2), "GB/s": round(nbytes / sec / 1e9, 1),
+                       "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "in_step": False})
     dom = max(table, key=lambda r: per_kernel[r[0]])
     roof = roofline_for(*dom, per_kernel[dom[0]])
     roof["kernel"] = dom[0]
@@ -390,8 +429,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "decode hot-path pass: KV cache 32768x128 INT8 + INT4(g32) quant/dequant; W8A8 rowscale "
-                        "fused-QKV act-quant+GEMV K=4096 N=6144 M=1,8,32; W8A8 blk128 SiLU act-quant+GEMM "
-                        "K=14336 N=4096 M=64,128,256; INT4 AWQ fused QKV K=4096 N=6144 g128 M=1,16,128",
+                        "fused-QKV K=4096 N=6144: projection with act-quant inside the GEMV (one launch) at "
+                        "M=1,8, act-quant+GEMV at M=32; W8A8 blk128 SiLU act-quant+GEMM K=14336 N=4096 "
+                        "M=64,128,256; INT4 AWQ fused QKV K=4096 N=6144 g128 M=1,16,128",
             "input_sets": nsets,
             "step_bytes": step_bytes,
             "timing": "HIP graph per step, rotating input sets (no MALL reuse across steps)",
@@ -399,10 +439,11 @@ def main():
         },
         "roofline": roof,
         "breakdown": breakdown,
+        "extras": extras,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle")
-        result["cpu_baseline"] = cpu_baseline(host_inputs, table)
+        result["cpu_baseline"] = cpu_baseline(host_inputs, table, single_core=not args.no_single_core)
     print(json.dumps(result), flush=True)
 
 

@@ -76,6 +76,26 @@ int kvq_quant_fp8_token(const float *x, int8_t *codes, float *scales,
 int kvq_dequant_fp8_token(const int8_t *codes, const float *scales, float *y,
                           uint32_t num_tokens, uint32_t head_dim, void *stream);
 
+/* KV cache INT8, one scale for the whole tensor.
+ * [KVQ] the parameter block's declared mode 0 ("per_tensor"); the page shows
+ * only per-token kernels, so this is the per-token rule above with the
+ * absmax taken over all num_tokens*head_dim values:
+ *
+ *   scale = max(max |x| / 127, 1e-8);   codes = clamp(rint(x / scale), -128, 127)
+ *   y = (float)codes * scale
+ *
+ * x, y: fp32 [num_tokens*head_dim]; codes: int8, same size; scale: fp32 [1].
+ * The quantizer runs two launches (partial absmax per workgroup into the
+ * workspace, then encode) and needs a device workspace of at least
+ * KVQ_INT8_TENSOR_WORKSPACE_BYTES (16-byte aligned); it writes only behind
+ * the counter area, so the workspace of the other calls can be shared. */
+#define KVQ_INT8_TENSOR_WORKSPACE_BYTES (KVQ_WORKSPACE_COUNTER_BYTES + 2048u)
+int kvq_quant_int8_tensor(const float *x, int8_t *codes, float *scale,
+                          uint32_t num_tokens, uint32_t head_dim,
+                          void *workspace, size_t workspace_bytes, void *stream);
+int kvq_dequant_int8_tensor(const int8_t *codes, const float *scale, float *y,
+                            uint32_t num_tokens, uint32_t head_dim, void *stream);
+
 /* ======================================================================== */
 /* KV cache, asymmetric per-group INT4                                      */
 /* [KVQ] sections "INT4 Per-Group Quantization" / "Dequantization".  Groups

@@ -36,6 +36,8 @@ SIGNATURES = {
     "kvq_dequant_int8_token": [_p, _p, _p, _u32, _u32, _p],
     "kvq_quant_fp8_token": [_p, _p, _p, _u32, _u32, _p],
     "kvq_dequant_fp8_token": [_p, _p, _p, _u32, _u32, _p],
+    "kvq_quant_int8_tensor": [_p, _p, _p, _u32, _u32, _p, _sz, _p],
+    "kvq_dequant_int8_tensor": [_p, _p, _p, _u32, _u32, _p],
     "kvq_quant_int4_group": [_p, _p, _p, _p, _u32, _u32, _u32, _p],
     "kvq_dequant_int4_group": [_p, _p, _p, _p, _u32, _u32, _u32, _p],
     "w8a8_act_quant": [_i, _i, _p, _p, _u32, _u32, _u32, _p, _p, _p],
@@ -50,6 +52,9 @@ SIGNATURES = {
                           ctypes.POINTER(Int4AwqProj), _p, _sz, _p],
     "int4_awq_workspace_bytes": [_u32, _u32, _u32, _u32, _psz],
 }
+
+# include/kvq.h: KVQ_INT8_TENSOR_WORKSPACE_BYTES (counter area + 512 partials)
+INT8_TENSOR_WORKSPACE_BYTES = 4096 + 2048
 
 _lib = None
 

@@ -44,8 +44,9 @@ _workspaces: dict = {}
 
 def workspace(device: torch.device, nbytes: int, stream: int) -> torch.Tensor:
     """A zero-filled device buffer of at least nbytes, cached per (device,
-    stream).  The kernels leave their workspace zero-filled, so reuse by calls
-    ordered on one stream is safe."""
+    stream).  The kernels leave the counter area at its start zero-filled and
+    put partial results only behind it, so reuse by calls ordered on one
+    stream is safe."""
     key = (torch.device(device), stream)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
@@ -70,6 +71,29 @@ def dequant_int8_token(codes: torch.Tensor, scales: torch.Tensor, out=None):
     t, d = codes.shape
     out = _empty((t, d), torch.float32, codes) if out is None else out
     _lib.call("kvq_dequant_int8_token", _dev(codes, torch.int8, "codes"), _dev(scales, torch.float32, "scales"),
+              _dev(out, torch.float32, "out"), t, d, _stream(codes))
+    return out
+
+
+def quant_int8_tensor(x: torch.Tensor, codes=None, scale=None):
+    """Per-tensor INT8 (the KV page's declared per-tensor mode): x fp32 [T, D]
+    -> (codes int8 [T, D], scale fp32 [1]).  Two launches; uses the shared
+    workspace for the partial maxima."""
+    t, d = x.shape
+    codes = _empty((t, d), torch.int8, x) if codes is None else codes
+    scale = _empty((1,), torch.float32, x) if scale is None else scale
+    stream = _stream(x)
+    nbytes = _lib.INT8_TENSOR_WORKSPACE_BYTES
+    ws = workspace(x.device, nbytes, stream)
+    _lib.call("kvq_quant_int8_tensor", _dev(x, torch.float32, "x"), _dev(codes, torch.int8, "codes"),
+              _dev(scale, torch.float32, "scale"), t, d, ws.data_ptr(), nbytes, stream)
+    return codes, scale
+
+
+def dequant_int8_tensor(codes: torch.Tensor, scale: torch.Tensor, out=None):
+    t, d = codes.shape
+    out = _empty((t, d), torch.float32, codes) if out is None else out
+    _lib.call("kvq_dequant_int8_tensor", _dev(codes, torch.int8, "codes"), _dev(scale, torch.float32, "scale"),
               _dev(out, torch.float32, "out"), t, d, _stream(codes))
     return out
 

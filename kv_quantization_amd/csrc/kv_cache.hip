@@ -141,6 +141,108 @@ __global__ __launch_bounds__(kBlock) void int8_dequant_wave(const int8_t *__rest
         y[t * head_dim + d] = (float)codes[t * head_dim + d] * s;
 }
 
+// ------------------------------------------------------ INT8 per tensor --
+//
+// The declared per-tensor mode: one scale from the absmax of the whole
+// tensor.  Pass 1: each of up to kTensorBlocks workgroups takes a
+// grid-strided share of the flattened tensor and writes its absmax to the
+// caller's workspace.  Pass 2: each workgroup issues the loads of its slice,
+// then reduces all partials (the max is exact in any order, so every
+// workgroup gets the same scale), and encodes its slice; the second read of
+// the tensor is served by the MALL for tensors that fit it.  Values past the
+// last multiple of 4 are handled one per thread by the last workgroup.
+constexpr uint32_t kTensorBlocks = 512;
+static_assert(KVQ_INT8_TENSOR_WORKSPACE_BYTES >= KVQ_WORKSPACE_COUNTER_BYTES + kTensorBlocks * 4, "workspace size");
+constexpr int kTensorUnroll = 4;
+
+__global__ __launch_bounds__(kBlock) void int8_tensor_absmax(const float *__restrict__ x, uint64_t n,
+                                                             float *__restrict__ partials) {
+    __shared__ float red[kWavesPerBlock];
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+    const uint64_t n4 = n / 4;
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+    uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    float m = 0.0f;
+    for (; i + (kTensorUnroll - 1) * stride < n4; i += kTensorUnroll * stride) {
+        f32x4 v[kTensorUnroll];
+#pragma unroll
+        for (int u = 0; u < kTensorUnroll; ++u) v[u] = x4[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kTensorUnroll; ++u) m = fmaxf(m, abs_max4(v[u]));
+    }
+    for (; i < n4; i += stride) m = fmaxf(m, abs_max4(x4[i]));
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < n - n4 * 4) m = fmaxf(m, fabsf(x[n4 * 4 + threadIdx.x]));
+    m = team_absmax<kWave>(m);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(kBlock) void int8_tensor_quant(const float *__restrict__ x, uint64_t n,
+                                                            const float *__restrict__ partials, uint32_t np,
+                                                            int8_t *__restrict__ codes, float *__restrict__ scale) {
+    __shared__ float red[kWavesPerBlock];
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+    uint32_t *c4 = reinterpret_cast<uint32_t *>(codes);
+    const uint64_t n4 = n / 4;
+    const uint64_t i0 = (uint64_t)blockIdx.x * (kBlock * kTensorUnroll) + threadIdx.x;
+    f32x4 v[kTensorUnroll];
+#pragma unroll
+    for (int u = 0; u < kTensorUnroll; ++u) {
+        const uint64_t i = i0 + (uint64_t)u * kBlock;
+        v[u] = i < n4 ? __builtin_nontemporal_load(&x4[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float m = 0.0f;
+    for (uint32_t p = threadIdx.x; p < np; p += kBlock) m = fmaxf(m, partials[p]);
+    m = team_absmax<kWave>(m);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float s = int8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int u = 0; u < kTensorUnroll; ++u) {
+        const uint64_t i = i0 + (uint64_t)u * kBlock;
+        if (i < n4)
+            c4[i] = int8_code(v[u].x, s, y) | (int8_code(v[u].y, s, y) << 8) | (int8_code(v[u].z, s, y) << 16) |
+                    (int8_code(v[u].w, s, y) << 24);
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < n - n4 * 4) {
+        const uint64_t e = n4 * 4 + threadIdx.x;
+        codes[e] = (int8_t)(uint8_t)int8_code(x[e], s, y);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+}
+
+__global__ __launch_bounds__(kBlock) void int8_tensor_dequant(const int8_t *__restrict__ codes,
+                                                              const float *__restrict__ scale,
+                                                              float *__restrict__ y, uint64_t n) {
+    const uint32_t *c4 = reinterpret_cast<const uint32_t *>(codes);
+    f32x4 *y4 = reinterpret_cast<f32x4 *>(y);
+    const uint64_t n4 = n / 4;
+    const float s = *scale;
+    const uint64_t i0 = (uint64_t)blockIdx.x * (kBlock * kTensorUnroll) + threadIdx.x;
+    uint32_t w[kTensorUnroll];
+#pragma unroll
+    for (int u = 0; u < kTensorUnroll; ++u) {
+        const uint64_t i = i0 + (uint64_t)u * kBlock;
+        w[u] = i < n4 ? __builtin_nontemporal_load(&c4[i]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kTensorUnroll; ++u) {
+        const uint64_t i = i0 + (uint64_t)u * kBlock;
+        f32x4 o;
+        o.x = (float)(int8_t)(w[u]) * s;
+        o.y = (float)(int8_t)(w[u] >> 8) * s;
+        o.z = (float)(int8_t)(w[u] >> 16) * s;
+        o.w = (float)(int8_t)(w[u] >> 24) * s;
+        if (i < n4) __builtin_nontemporal_store(o, &y4[i]);
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < n - n4 * 4) {
+        const uint64_t e = n4 * 4 + threadIdx.x;
+        y[e] = (float)codes[e] * s;
+    }
+}
+
 // ------------------------------------------------------------ INT4 ------
 
 // L lanes per group (group_size = 4L); a wave covers U*(64/L) groups.
@@ -391,4 +493,40 @@ extern "C" int kvq_dequant_int4_group(const uint8_t *packed, const float *scales
                                                                                 group_size);
     }
     return launch_status("kvq_dequant_int4_group");
+}
+
+extern "C" int kvq_quant_int8_tensor(const float *x, int8_t *codes, float *scale, uint32_t num_tokens,
+                                     uint32_t head_dim, void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "kvq_quant_int8_tensor";
+    int st = check_kv_common(fn, x, codes, scale, num_tokens, head_dim);
+    if (st) return st;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < KVQ_INT8_TENSOR_WORKSPACE_BYTES)
+        return fail(KVQ_E_INVALID, "%s: needs a 16-byte aligned workspace of >= %u bytes (got %zu)", fn,
+                    KVQ_INT8_TENSOR_WORKSPACE_BYTES, workspace ? workspace_bytes : (size_t)0);
+    const uint64_t n = (uint64_t)num_tokens * head_dim;
+    const uint64_t n4 = n / 4;
+    uint64_t np = (n4 + kBlock - 1) / kBlock;
+    np = np < 1 ? 1 : (np > kTensorBlocks ? kTensorBlocks : np);
+    float *partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
+    hipStream_t s = as_stream(stream);
+    int8_tensor_absmax<<<(unsigned)np, kBlock, 0, s>>>(x, n, partials);
+    st = launch_status(fn);
+    if (st) return st;
+    const uint64_t blocks = n4 ? (n4 + kBlock * kTensorUnroll - 1) / (kBlock * kTensorUnroll) : 1;
+    if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: tensor too large", fn);
+    int8_tensor_quant<<<(unsigned)blocks, kBlock, 0, s>>>(x, n, partials, (uint32_t)np, codes, scale);
+    return launch_status(fn);
+}
+
+extern "C" int kvq_dequant_int8_tensor(const int8_t *codes, const float *scale, float *y, uint32_t num_tokens,
+                                       uint32_t head_dim, void *stream) {
+    const char *fn = "kvq_dequant_int8_tensor";
+    int st = check_kv_common(fn, codes, scale, y, num_tokens, head_dim);
+    if (st) return st;
+    const uint64_t n = (uint64_t)num_tokens * head_dim;
+    const uint64_t n4 = n / 4;
+    const uint64_t blocks = n4 ? (n4 + kBlock * kTensorUnroll - 1) / (kBlock * kTensorUnroll) : 1;
+    if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: tensor too large", fn);
+    int8_tensor_dequant<<<(unsigned)blocks, kBlock, 0, as_stream(stream)>>>(codes, scale, y, n);
+    return launch_status(fn);
 }

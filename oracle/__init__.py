@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         p = ctypes.c_void_p
         sig = {
             "oracle_num_threads": ([], ctypes.c_int),
+            "oracle_set_num_threads": ([ctypes.c_int], None),
             "oracle_kv_int8_quant": ([p, p, p, i64, i64], None),
             "oracle_kv_int8_dequant": ([p, p, p, i64, i64], None),
             "oracle_kv_int8_quant_tensor": ([p, p, p, i64], None),
@@ -92,6 +93,11 @@ def lib() -> ctypes.CDLL:
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops from now on (timing only)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:

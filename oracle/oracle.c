@@ -48,6 +48,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the parallel loops that follow (timing only; no effect on
+ * any result). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* [KVQ] INT8 per-token quantization.
  * For token t over its head_dim values: the absolute maximum, starting from

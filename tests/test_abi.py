@@ -150,3 +150,28 @@ def test_workspace_sizes(lib):
     assert lib.int4_awq_workspace_bytes(1, 512, 128, 512, ctypes.byref(b)) == 0
     assert b.value == 0         # tiny problem: one workgroup per tile
     assert lib.w8a8_gemv_workspace_bytes(0, 8, 4096, 6144, ctypes.byref(b)) == 0
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((0, FAKE, FAKE, 4, 8), "null"),
+    ((MISALIGNED, FAKE, FAKE, 4, 8), "aligned"),
+    ((FAKE, FAKE, FAKE, 0, 8), "num_tokens=0"),
+    ((FAKE, FAKE, FAKE, 4, 0), "head_dim=0"),
+])
+def test_kv_int8_tensor_validation(lib, args, frag):
+    st, msg = _err(lib, "kvq_quant_int8_tensor", *args, FAKE, 1 << 20, None)
+    assert st == _lib.KVQ_E_INVALID and frag in msg, msg
+    st, msg = _err(lib, "kvq_dequant_int8_tensor", *args, None)
+    assert st == _lib.KVQ_E_INVALID and frag in msg, msg
+
+
+def test_kv_int8_tensor_workspace_rules(lib):
+    need = _lib.INT8_TENSOR_WORKSPACE_BYTES
+    text = HEADER.read_text()
+    counter = int(re.search(r"#define KVQ_WORKSPACE_COUNTER_BYTES (\d+)u", text).group(1))
+    extra = int(re.search(r"#define KVQ_INT8_TENSOR_WORKSPACE_BYTES \(KVQ_WORKSPACE_COUNTER_BYTES \+ (\d+)u\)",
+                          text).group(1))
+    assert need == counter + extra
+    for ws, nbytes in ((None, need), (FAKE, need - 1), (MISALIGNED, need)):
+        st, msg = _err(lib, "kvq_quant_int8_tensor", FAKE, FAKE, FAKE, 4, 8, ws, nbytes, None)
+        assert st == _lib.KVQ_E_INVALID and "workspace" in msg, msg

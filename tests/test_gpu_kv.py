@@ -109,3 +109,58 @@ def test_wide_range_codes():
     x[rng.random(x.shape) < 0.01] = 0.0
     _int8_case(x)
     _int4_case(x, 32)
+
+
+# -------------------------------------------------- INT8 per-tensor mode ----
+
+def _int8_tensor_case(x):
+    t, d = x.shape
+    codes, raw_c = poisoned((t, d), torch.int8)
+    scale, raw_s = poisoned((1,), torch.float32)
+    api.quant_int8_tensor(dev(x), codes, scale)
+    rc, rs = _oracle.kv_int8_quant_tensor(x)
+    y, raw_y = poisoned((t, d), torch.float32)
+    api.dequant_int8_tensor(dev(rc), dev(rs), y)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(codes), rc, "int8 tensor codes")
+    assert_bits_equal(host(scale), rs, "int8 tensor scale")
+    assert_bits_equal(host(y), _oracle.kv_int8_dequant_tensor(rc, rs), "int8 tensor dequant")
+    assert_canary(raw_c, t * d)
+    assert_canary(raw_s, 4)
+    assert_canary(raw_y, t * d * 4)
+
+
+@pytest.mark.parametrize("t,d", INT8_SHAPES + [(65536, 128), (3, 1), (1023, 3)])
+def test_int8_tensor_parity(t, d):
+    print_case("kv int8 tensor", t, d)
+    _int8_tensor_case(synth.kv_cache(t, d, seed=2 if (t, d) == (32768, 128) else 300 + t + d))
+
+
+def test_int8_tensor_worked_examples_and_edges():
+    print_case("kv int8 tensor worked + edges")
+    g = json.loads((GOLDEN / "kv_int8_tensor_worked.json").read_text())
+    for case in g["cases"]:
+        x = np.array(case["x"], np.float32)
+        codes, scale = api.quant_int8_tensor(dev(x))
+        np.testing.assert_array_equal(host(codes), np.array(case["codes"], np.int8))
+        np.testing.assert_array_equal(host(api.dequant_int8_tensor(codes, scale)), np.array(case["dequant"], np.float32))
+    x = np.zeros((64, 128), np.float32)
+    x[2, ::2] = -0.0
+    x[4, 5] = 1e-40
+    _int8_tensor_case(x)                      # all (signed) zeros and a subnormal: floor scale
+    x[7, 100] = -3.0e38                        # one huge value sets the scale for everything
+    x[5] = np.tile([2.5, -2.5, 0.5, 1.5], 32)
+    _int8_tensor_case(x)
+    rng = np.random.default_rng(79)
+    w = (np.exp2(rng.uniform(-40, 40, (2048, 64))) * rng.choice([-1.0, 1.0], (2048, 64))).astype(np.float32)
+    _int8_tensor_case(w)                      # magnitudes over 80 binades
+
+
+def test_int8_tensor_repeated_calls_share_workspace():
+    """Back-to-back calls on one stream reuse the cached workspace (partials
+    behind the counter area) and interleave with split-K GEMV calls."""
+    print_case("kv int8 tensor + shared workspace")
+    a = synth.kv_cache(4096, 128, seed=81)
+    b = synth.kv_cache(100, 33, seed=82)
+    for x in (a, b, a):
+        _int8_tensor_case(x)
