@@ -246,6 +246,15 @@ int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k,
 int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_size,
                              uint32_t n_total, size_t *bytes);
 
+/* ======================================================================== */
+/* Measurement helper (not part of the method)                              */
+/* kvq_stream_read: reads `bytes` (a positive multiple of 16) at `src` (16-
+ * byte aligned device memory) with 16-byte loads across the whole GPU and
+ * writes almost nothing (sink: one device uint32, written only for an
+ * impossible data pattern).  Its rate is the empirical read ceiling the
+ * benchmark reports beside each kernel's bandwidth. */
+int kvq_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,7 @@ SIGNATURES = {
     "int4_awq_qkv_gemm": [_p, _u32, _u32, _u32, ctypes.POINTER(Int4AwqProj), ctypes.POINTER(Int4AwqProj),
                           ctypes.POINTER(Int4AwqProj), _p, _sz, _p],
     "int4_awq_workspace_bytes": [_u32, _u32, _u32, _u32, _psz],
+    "kvq_stream_read": [_p, _sz, _p, _p],
 }
 
 # include/kvq.h: KVQ_INT8_TENSOR_WORKSPACE_BYTES (counter area + 512 partials)

@@ -275,3 +275,12 @@ def int4_awq_qkv(x: torch.Tensor, projections, group_size: int, outs=None, use_w
     _lib.call("int4_awq_qkv_gemm", _dev(x, torch.float32, "x"), m, k, group_size, ctypes.byref(structs[0]), kp, vp,
               ws_ptr, ws_bytes, stream)
     return res
+
+
+# ---------------------------------------------------------- measurement ----
+
+def stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor) -> None:
+    """Read nbytes of buf on the device (the empirical read ceiling)."""
+    if not buf.is_cuda or not buf.is_contiguous() or buf.numel() * buf.element_size() < nbytes:
+        raise ValueError("buf must be a contiguous device tensor of at least nbytes")
+    _lib.call("kvq_stream_read", buf.data_ptr(), nbytes, _dev(sink, torch.int32, "sink"), _stream(buf))

@@ -47,6 +47,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBlock = 256;
 constexpr int kTargetWaves = 2048;
+constexpr uint32_t kXcds = 8;           // XCDs of an MI355X (workgroups are dealt to them in turn)
 
 struct Projs {
     const uint32_t *qw[3];
@@ -121,10 +122,25 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
     const int wc = lane & 15, kg = lane >> 4;
 
-    uint32_t b = blockIdx.x;
-    const uint32_t bs = b % ks_b;
-    b /= ks_b;
-    const uint32_t c = b % nchunks, t = b / nchunks;
+    // Workgroups go to the XCDs in turn (index mod kXcds), and each XCD has
+    // its own L2.  With several row chunks, all workgroups of one tile (its
+    // chunks and K slices) are placed on the XCD of index t mod kXcds, so
+    // the tile's weights are fetched from HBM once instead of once per chunk
+    // (M=128: 65 -> ~30 MB fetched per call); slots past the last tile exit
+    // at once.  With one chunk, consecutive workgroups take the K slices of a
+    // tile (measured faster at M=1: 9.6 vs 11.0 us).
+    const uint32_t per_tile = nchunks * ks_b;
+    uint32_t t, r;
+    if (nchunks > 1) {
+        const uint32_t j = blockIdx.x / kXcds;
+        t = blockIdx.x % kXcds + kXcds * (j / per_tile);
+        r = j % per_tile;
+        if (t >= P.ntiles) return;
+    } else {
+        t = blockIdx.x / per_tile;
+        r = blockIdx.x % per_tile;
+    }
+    const uint32_t c = r / ks_b, bs = r % ks_b;
     const int p = (P.count > 1 && t >= P.tstart[1]) ? ((P.count > 2 && t >= P.tstart[2]) ? 2 : 1) : 0;
     const uint32_t np = pick(p, P.n[0], P.n[1], P.n[2]), wp = np / 8;
     const uint32_t tp = t - pick(p, P.tstart[0], P.tstart[1], P.tstart[2]);   // tile within the projection
@@ -427,7 +443,8 @@ extern "C" int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k, uint32_
             partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.counter_bytes);
         }
     }
-    const uint64_t blocks = (uint64_t)P.ntiles * pl.nchunks * pl.ks_b;
+    const uint64_t tile_slots = pl.nchunks > 1 ? (uint64_t)kXcds * ((P.ntiles + kXcds - 1) / kXcds) : P.ntiles;
+    const uint64_t blocks = tile_slots * pl.nchunks * pl.ks_b;
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
     hipStream_t s = as_stream(stream);
     const uint32_t ksg = group_size / 32;
