@@ -226,6 +226,48 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
     return (_c(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+# 16-bit value formats of the KV codecs: 1 = fp16, 2 = bf16 (0 = fp32).
+
+def widen16(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """fp16 or bf16 bits (uint16) -> fp32, exact (every 16-bit value is an fp32)."""
+    bits = _c(bits, np.uint16)
+    if dtype == 1:
+        return bits.view(np.float16).astype(np.float32)
+    if dtype == 2:
+        return bf16_to_f32(bits)
+    raise ValueError("dtype must be 1 (fp16) or 2 (bf16)")
+
+
+def narrow16(x: np.ndarray, dtype: int) -> np.ndarray:
+    """fp32 -> fp16 or bf16 bits, round to nearest even (numpy's IEEE cast for
+    fp16, the C routine above for bf16)."""
+    x = _c(x, np.float32)
+    if dtype == 1:
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).view(np.uint16)
+    if dtype == 2:
+        return f32_to_bf16(x)
+    raise ValueError("dtype must be 1 (fp16) or 2 (bf16)")
+
+
+def kv_int8_quant_dt(x_bits: np.ndarray, dtype: int):
+    """INT8 per token of a 16-bit cache: the fp32 codec on the exactly widened values."""
+    return kv_int8_quant(widen16(x_bits, dtype))
+
+
+def kv_int8_dequant_dt(codes, scales, dtype: int) -> np.ndarray:
+    """fp32 dequantization, then rounding to the 16-bit type."""
+    return narrow16(kv_int8_dequant(codes, scales), dtype)
+
+
+def kv_int4_quant_dt(x_bits: np.ndarray, group_size: int, dtype: int):
+    return kv_int4_quant(widen16(x_bits, dtype), group_size)
+
+
+def kv_int4_dequant_dt(packed, scales, zeros, num_tokens: int, head_dim: int, group_size: int, dtype: int):
+    return narrow16(kv_int4_dequant(packed, scales, zeros, num_tokens, head_dim, group_size), dtype)
+
+
 def e4m3_encode(x) -> np.ndarray:
     """fp32 -> E4M3FN codes (RNE, saturating, sign kept), element by element in C."""
     x = _c(np.atleast_1d(x), np.float32)

@@ -127,3 +127,29 @@ def test_silu_against_float64(oracle_mod):
     assert got[np.where(v == 0)[0][0]] == 0.0
     # a few fp32 roundings of a well-conditioned expression
     assert np.all(np.abs(got - ref) <= 4 * 2.0 ** -24 * np.abs(ref) + 1e-37)
+
+
+# ------------------------------------------------ 16-bit KV value formats ----
+
+def test_fp16_widen_narrow_exhaustive_and_vs_torch(oracle_mod):
+    """Every finite fp16 pattern widens to the fp32 torch gives and narrows
+    back to itself; random fp32 values narrow as torch's fp16 cast does."""
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = np.isfinite(bits.view(np.float16))
+    w = oracle_mod.widen16(bits[fin], 1)
+    t = torch.from_numpy(bits[fin].view(np.int16)).view(torch.float16).float().numpy()
+    np.testing.assert_array_equal(w.view(np.uint32), t.view(np.uint32))
+    np.testing.assert_array_equal(oracle_mod.narrow16(w, 1), bits[fin])
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(1 << 20) * np.exp2(rng.uniform(-30, 17, 1 << 20))).astype(np.float32)
+    x = x[np.abs(x) < 65504]
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle_mod.narrow16(x, 1), ref)
+
+
+def test_bf16_widen_narrow_round_trip(oracle_mod):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = np.isfinite(oracle_mod.bf16_to_f32(bits))
+    w = oracle_mod.widen16(bits[fin], 2)
+    np.testing.assert_array_equal(oracle_mod.narrow16(w, 2), bits[fin])
