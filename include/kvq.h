@@ -76,6 +76,30 @@ int kvq_quant_fp8_token(const float *x, int8_t *codes, float *scales,
 int kvq_dequant_fp8_token(const int8_t *codes, const float *scales, float *y,
                           uint32_t num_tokens, uint32_t head_dim, void *stream);
 
+/* KV codecs with 16-bit values (the page's kernels carry an _f32 suffix;
+ * these are the same codecs for fp16/bf16 caches).  dtype: KVQ_DT_F32,
+ * KVQ_DT_F16 or KVQ_DT_BF16.  A 16-bit input is widened exactly to fp32 and
+ * coded by the fp32 rule above (codes and scales equal those of the fp32
+ * call on the widened values); a 16-bit output is the fp32 dequantized value
+ * rounded to nearest even.  x / y hold num_tokens*head_dim values of that
+ * type; every other argument, layout and rule is that of the fp32 call.
+ * KVQ_DT_F32 gives exactly the fp32 calls. */
+typedef enum { KVQ_DT_F32 = 0, KVQ_DT_F16 = 1, KVQ_DT_BF16 = 2 } kvq_dtype_t;
+int kvq_quant_int8_token_dt(const void *x, int x_dtype, int8_t *codes,
+                            float *scales, uint32_t num_tokens,
+                            uint32_t head_dim, void *stream);
+int kvq_dequant_int8_token_dt(const int8_t *codes, const float *scales,
+                              void *y, int y_dtype, uint32_t num_tokens,
+                              uint32_t head_dim, void *stream);
+int kvq_quant_int4_group_dt(const void *x, int x_dtype, uint8_t *packed,
+                            float *scales, float *zeros, uint32_t num_tokens,
+                            uint32_t head_dim, uint32_t group_size,
+                            void *stream);
+int kvq_dequant_int4_group_dt(const uint8_t *packed, const float *scales,
+                              const float *zeros, void *y, int y_dtype,
+                              uint32_t num_tokens, uint32_t head_dim,
+                              uint32_t group_size, void *stream);
+
 /* KV cache INT8, one scale for the whole tensor.
  * [KVQ] the parameter block's declared mode 0 ("per_tensor"); the page shows
  * only per-token kernels, so this is the per-token rule above with the

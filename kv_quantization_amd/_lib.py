@@ -37,6 +37,10 @@ SIGNATURES = {
     "kvq_quant_fp8_token": [_p, _p, _p, _u32, _u32, _p],
     "kvq_dequant_fp8_token": [_p, _p, _p, _u32, _u32, _p],
     "kvq_quant_int8_tensor": [_p, _p, _p, _u32, _u32, _p, _sz, _p],
+    "kvq_quant_int8_token_dt": [_p, _i, _p, _p, _u32, _u32, _p],
+    "kvq_dequant_int8_token_dt": [_p, _p, _p, _i, _u32, _u32, _p],
+    "kvq_quant_int4_group_dt": [_p, _i, _p, _p, _p, _u32, _u32, _u32, _p],
+    "kvq_dequant_int4_group_dt": [_p, _p, _p, _p, _i, _u32, _u32, _u32, _p],
     "kvq_dequant_int8_tensor": [_p, _p, _p, _u32, _u32, _p],
     "kvq_quant_int4_group": [_p, _p, _p, _p, _u32, _u32, _u32, _p],
     "kvq_dequant_int4_group": [_p, _p, _p, _p, _u32, _u32, _u32, _p],

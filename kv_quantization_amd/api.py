@@ -57,21 +57,42 @@ def workspace(device: torch.device, nbytes: int, stream: int) -> torch.Tensor:
 
 # ----------------------------------------------------------- KV cache ------
 
+# value dtypes of the KV codecs (kvq_dtype_t)
+_KV_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+def _kv_dt(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _KV_DT:
+        raise TypeError(f"{name} must be float32, float16 or bfloat16, got {t.dtype}")
+    return _KV_DT[t.dtype]
+
+
 def quant_int8_token(x: torch.Tensor, codes=None, scales=None):
-    """x fp32 [T, D] -> (codes int8 [T, D], scales fp32 [T])."""
+    """x fp32/fp16/bf16 [T, D] -> (codes int8 [T, D], scales fp32 [T])."""
     t, d = x.shape
     codes = _empty((t, d), torch.int8, x) if codes is None else codes
     scales = _empty((t,), torch.float32, x) if scales is None else scales
-    _lib.call("kvq_quant_int8_token", _dev(x, torch.float32, "x"), _dev(codes, torch.int8, "codes"),
-              _dev(scales, torch.float32, "scales"), t, d, _stream(x))
+    dt = _kv_dt(x, "x")
+    if dt == 0:
+        _lib.call("kvq_quant_int8_token", _dev(x, torch.float32, "x"), _dev(codes, torch.int8, "codes"),
+                  _dev(scales, torch.float32, "scales"), t, d, _stream(x))
+    else:
+        _lib.call("kvq_quant_int8_token_dt", _dev(x, x.dtype, "x"), dt, _dev(codes, torch.int8, "codes"),
+                  _dev(scales, torch.float32, "scales"), t, d, _stream(x))
     return codes, scales
 
 
-def dequant_int8_token(codes: torch.Tensor, scales: torch.Tensor, out=None):
+def dequant_int8_token(codes: torch.Tensor, scales: torch.Tensor, out=None, dtype=torch.float32):
+    """-> y [T, D] of `dtype` (or of out's dtype): fp32 value, 16-bit rounded to nearest even."""
     t, d = codes.shape
-    out = _empty((t, d), torch.float32, codes) if out is None else out
-    _lib.call("kvq_dequant_int8_token", _dev(codes, torch.int8, "codes"), _dev(scales, torch.float32, "scales"),
-              _dev(out, torch.float32, "out"), t, d, _stream(codes))
+    out = _empty((t, d), dtype, codes) if out is None else out
+    dt = _kv_dt(out, "out")
+    if dt == 0:
+        _lib.call("kvq_dequant_int8_token", _dev(codes, torch.int8, "codes"),
+                  _dev(scales, torch.float32, "scales"), _dev(out, torch.float32, "out"), t, d, _stream(codes))
+    else:
+        _lib.call("kvq_dequant_int8_token_dt", _dev(codes, torch.int8, "codes"),
+                  _dev(scales, torch.float32, "scales"), _dev(out, out.dtype, "out"), dt, t, d, _stream(codes))
     return out
 
 
@@ -99,24 +120,35 @@ def dequant_int8_tensor(codes: torch.Tensor, scale: torch.Tensor, out=None):
 
 
 def quant_int4_group(x: torch.Tensor, group_size: int, packed=None, scales=None, zeros=None):
-    """x fp32 [T, D] -> (packed uint8 [T*D/2], scales fp32 [G], zeros fp32 [G])."""
+    """x fp32/fp16/bf16 [T, D] -> (packed uint8 [T*D/2], scales fp32 [G], zeros fp32 [G])."""
     t, d = x.shape
     total = t * d
     g = total // group_size if group_size else 0
     packed = _empty((total // 2,), torch.uint8, x) if packed is None else packed
     scales = _empty((g,), torch.float32, x) if scales is None else scales
     zeros = _empty((g,), torch.float32, x) if zeros is None else zeros
-    _lib.call("kvq_quant_int4_group", _dev(x, torch.float32, "x"), _dev(packed, torch.uint8, "packed"),
-              _dev(scales, torch.float32, "scales"), _dev(zeros, torch.float32, "zeros"), t, d, group_size,
-              _stream(x))
+    dt = _kv_dt(x, "x")
+    args = (_dev(packed, torch.uint8, "packed"), _dev(scales, torch.float32, "scales"),
+            _dev(zeros, torch.float32, "zeros"), t, d, group_size, _stream(x))
+    if dt == 0:
+        _lib.call("kvq_quant_int4_group", _dev(x, torch.float32, "x"), *args)
+    else:
+        _lib.call("kvq_quant_int4_group_dt", _dev(x, x.dtype, "x"), dt, *args)
     return packed, scales, zeros
 
 
-def dequant_int4_group(packed, scales, zeros, num_tokens: int, head_dim: int, group_size: int, out=None):
-    out = _empty((num_tokens, head_dim), torch.float32, packed) if out is None else out
-    _lib.call("kvq_dequant_int4_group", _dev(packed, torch.uint8, "packed"), _dev(scales, torch.float32, "scales"),
-              _dev(zeros, torch.float32, "zeros"), _dev(out, torch.float32, "out"), num_tokens, head_dim,
-              group_size, _stream(packed))
+def dequant_int4_group(packed, scales, zeros, num_tokens: int, head_dim: int, group_size: int, out=None,
+                       dtype=torch.float32):
+    out = _empty((num_tokens, head_dim), dtype, packed) if out is None else out
+    dt = _kv_dt(out, "out")
+    head = (_dev(packed, torch.uint8, "packed"), _dev(scales, torch.float32, "scales"),
+            _dev(zeros, torch.float32, "zeros"))
+    if dt == 0:
+        _lib.call("kvq_dequant_int4_group", *head, _dev(out, torch.float32, "out"), num_tokens, head_dim,
+                  group_size, _stream(packed))
+    else:
+        _lib.call("kvq_dequant_int4_group_dt", *head, _dev(out, out.dtype, "out"), dt, num_tokens, head_dim,
+                  group_size, _stream(packed))
     return out
 
 

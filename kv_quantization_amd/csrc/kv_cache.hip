@@ -36,6 +36,47 @@ __device__ __forceinline__ uint32_t int8_code(float v, float s, float y) {
 
 __device__ __forceinline__ float int8_scale(float amax) { return fmaxf(amax / 127.0f, 1e-8f); }
 
+// Element I/O.  DT 0: fp32 values in memory; 1: fp16; 2: bf16.  Values are
+// fp32 in registers: 16-bit inputs widen exactly, so the arithmetic is that
+// of the fp32 codec on the same numbers; 16-bit outputs round the fp32
+// result to nearest even.  Index i4 counts groups of 4 consecutive values.
+template <int DT>
+__device__ __forceinline__ float from16(uint32_t h) {
+    if (DT == 1) return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    return __uint_as_float(h << 16);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t to16(float f) {
+    if (DT == 1) return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+template <int DT>
+__device__ __forceinline__ f32x4 load4(const void *p, uint64_t i4) {
+    if (DT == 0) return __builtin_nontemporal_load(static_cast<const f32x4 *>(p) + i4);
+    const u32x2 w = __builtin_nontemporal_load(static_cast<const u32x2 *>(p) + i4);
+    return f32x4{from16<DT>(w.x & 0xFFFFu), from16<DT>(w.x >> 16), from16<DT>(w.y & 0xFFFFu), from16<DT>(w.y >> 16)};
+}
+template <int DT>
+__device__ __forceinline__ float load1(const void *p, uint64_t i) {
+    if (DT == 0) return static_cast<const float *>(p)[i];
+    return from16<DT>(static_cast<const uint16_t *>(p)[i]);
+}
+template <int DT>
+__device__ __forceinline__ void store4(void *p, uint64_t i4, f32x4 v) {
+    if (DT == 0) {
+        __builtin_nontemporal_store(v, static_cast<f32x4 *>(p) + i4);
+    } else {
+        const u32x2 w = {to16<DT>(v.x) | (to16<DT>(v.y) << 16), to16<DT>(v.z) | (to16<DT>(v.w) << 16)};
+        __builtin_nontemporal_store(w, static_cast<u32x2 *>(p) + i4);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void store1(void *p, uint64_t i, float v) {
+    if (DT == 0) static_cast<float *>(p)[i] = v;
+    else static_cast<uint16_t *>(p)[i] = (uint16_t)to16<DT>(v);
+}
+
 // y = 1/sf (see div_by_scale)
 __device__ __forceinline__ uint32_t int4_code(float v, float mn, float sf, float y) {
     float d = v - mn;
@@ -55,8 +96,8 @@ __device__ __forceinline__ uint64_t global_wave() {
 // ------------------------------------------------------------ INT8 ------
 
 // L lanes per token (head_dim = 4L); a wave covers U*(64/L) tokens.
-template <int L, int U>
-__global__ __launch_bounds__(kBlock) void int8_quant_team(const f32x4 *__restrict__ x,
+template <int L, int U, int DT>
+__global__ __launch_bounds__(kBlock) void int8_quant_team(const void *__restrict__ x,
                                                           uint32_t *__restrict__ codes,
                                                           float *__restrict__ scales,
                                                           uint64_t num_tokens) {
@@ -68,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void int8_quant_team(const f32x4 *__restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint64_t t = t0 + (uint64_t)u * TPI;
-        v[u] = t < num_tokens ? __builtin_nontemporal_load(&x[t * L + li]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[u] = t < num_tokens ? load4<DT>(x, t * L + li) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -85,25 +126,26 @@ __global__ __launch_bounds__(kBlock) void int8_quant_team(const f32x4 *__restric
 }
 
 // Any head_dim: one wave per token.
-__global__ __launch_bounds__(kBlock) void int8_quant_wave(const float *__restrict__ x,
+template <int DT>
+__global__ __launch_bounds__(kBlock) void int8_quant_wave(const void *__restrict__ x,
                                                           int8_t *__restrict__ codes,
                                                           float *__restrict__ scales,
                                                           uint64_t num_tokens, uint32_t head_dim) {
     const uint64_t t = global_wave();
     if (t >= num_tokens) return;
-    const float *row = x + t * head_dim;
+    const uint64_t row = t * head_dim;
     float m = 0.0f;
-    for (uint32_t d = lane_id(); d < head_dim; d += kWave) m = fmaxf(m, fabsf(row[d]));
+    for (uint32_t d = lane_id(); d < head_dim; d += kWave) m = fmaxf(m, fabsf(load1<DT>(x, row + d)));
     const float s = int8_scale(team_absmax<kWave>(m));
     if (lane_id() == 0) scales[t] = s;
     for (uint32_t d = lane_id(); d < head_dim; d += kWave)
-        codes[t * head_dim + d] = (int8_t)(uint8_t)int8_code(row[d], s, 1.0f / s);
+        codes[row + d] = (int8_t)(uint8_t)int8_code(load1<DT>(x, row + d), s, 1.0f / s);
 }
 
-template <int L, int U>
+template <int L, int U, int DT>
 __global__ __launch_bounds__(kBlock) void int8_dequant_team(const uint32_t *__restrict__ codes,
                                                             const float *__restrict__ scales,
-                                                            f32x4 *__restrict__ y,
+                                                            void *__restrict__ y,
                                                             uint64_t num_tokens) {
     constexpr int TPI = kWave / L;
     const int lane = lane_id();
@@ -126,19 +168,20 @@ __global__ __launch_bounds__(kBlock) void int8_dequant_team(const uint32_t *__re
         o.y = (float)(int8_t)(w[u] >> 8) * s[u];
         o.z = (float)(int8_t)(w[u] >> 16) * s[u];
         o.w = (float)(int8_t)(w[u] >> 24) * s[u];
-        if (t < num_tokens) __builtin_nontemporal_store(o, &y[t * L + li]);
+        if (t < num_tokens) store4<DT>(y, t * L + li, o);
     }
 }
 
+template <int DT>
 __global__ __launch_bounds__(kBlock) void int8_dequant_wave(const int8_t *__restrict__ codes,
                                                             const float *__restrict__ scales,
-                                                            float *__restrict__ y,
+                                                            void *__restrict__ y,
                                                             uint64_t num_tokens, uint32_t head_dim) {
     const uint64_t t = global_wave();
     if (t >= num_tokens) return;
     const float s = scales[t];
     for (uint32_t d = lane_id(); d < head_dim; d += kWave)
-        y[t * head_dim + d] = (float)codes[t * head_dim + d] * s;
+        store1<DT>(y, t * head_dim + d, (float)codes[t * head_dim + d] * s);
 }
 
 // ------------------------------------------------------ INT8 per tensor --
@@ -246,8 +289,8 @@ __global__ __launch_bounds__(kBlock) void int8_tensor_dequant(const int8_t *__re
 // ------------------------------------------------------------ INT4 ------
 
 // L lanes per group (group_size = 4L); a wave covers U*(64/L) groups.
-template <int L, int U>
-__global__ __launch_bounds__(kBlock) void int4_quant_team(const f32x4 *__restrict__ x,
+template <int L, int U, int DT>
+__global__ __launch_bounds__(kBlock) void int4_quant_team(const void *__restrict__ x,
                                                           uint16_t *__restrict__ packed,
                                                           float *__restrict__ scales,
                                                           float *__restrict__ zeros,
@@ -260,7 +303,7 @@ __global__ __launch_bounds__(kBlock) void int4_quant_team(const f32x4 *__restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint64_t g = g0 + (uint64_t)u * GPI;
-        v[u] = g < num_groups ? __builtin_nontemporal_load(&x[g * L + li]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[u] = g < num_groups ? load4<DT>(x, g * L + li) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -284,18 +327,20 @@ __global__ __launch_bounds__(kBlock) void int4_quant_team(const f32x4 *__restric
 }
 
 // Any even group_size: one wave per group, one byte (two codes) per step.
-__global__ __launch_bounds__(kBlock) void int4_quant_wave(const float *__restrict__ x,
+template <int DT>
+__global__ __launch_bounds__(kBlock) void int4_quant_wave(const void *__restrict__ x,
                                                           uint8_t *__restrict__ packed,
                                                           float *__restrict__ scales,
                                                           float *__restrict__ zeros,
                                                           uint64_t num_groups, uint32_t group_size) {
     const uint64_t g = global_wave();
     if (g >= num_groups) return;
-    const float *grp = x + g * group_size;
-    float mn = grp[0], mx = grp[0];
+    const uint64_t g0 = g * group_size;
+    float mn = load1<DT>(x, g0), mx = mn;
     for (uint32_t i = lane_id(); i < group_size; i += kWave) {
-        mn = fminf(mn, grp[i]);
-        mx = fmaxf(mx, grp[i]);
+        const float v = load1<DT>(x, g0 + i);
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
     }
     mn = team_min<kWave>(mn);
     mx = team_max<kWave>(mx);
@@ -308,14 +353,15 @@ __global__ __launch_bounds__(kBlock) void int4_quant_wave(const float *__restric
     }
     uint8_t *out = packed + g * (group_size / 2);
     for (uint32_t p = lane_id(); p < group_size / 2; p += kWave)
-        out[p] = (uint8_t)(int4_code(grp[2 * p], mn, sf, 1.0f / sf) | (int4_code(grp[2 * p + 1], mn, sf, 1.0f / sf) << 4));
+        out[p] = (uint8_t)(int4_code(load1<DT>(x, g0 + 2 * p), mn, sf, 1.0f / sf) |
+                           (int4_code(load1<DT>(x, g0 + 2 * p + 1), mn, sf, 1.0f / sf) << 4));
 }
 
-template <int L, int U>
+template <int L, int U, int DT>
 __global__ __launch_bounds__(kBlock) void int4_dequant_team(const uint16_t *__restrict__ packed,
                                                             const float *__restrict__ scales,
                                                             const float *__restrict__ zeros,
-                                                            f32x4 *__restrict__ y,
+                                                            void *__restrict__ y,
                                                             uint64_t num_groups) {
     constexpr int GPI = kWave / L;
     const int lane = lane_id();
@@ -340,25 +386,26 @@ __global__ __launch_bounds__(kBlock) void int4_dequant_team(const uint16_t *__re
         o.y = (float)((w[u] >> 4) & 15u) * s[u] - zs;
         o.z = (float)((w[u] >> 8) & 15u) * s[u] - zs;
         o.w = (float)((w[u] >> 12) & 15u) * s[u] - zs;
-        if (g < num_groups) __builtin_nontemporal_store(o, &y[g * L + li]);
+        if (g < num_groups) store4<DT>(y, g * L + li, o);
     }
 }
 
+template <int DT>
 __global__ __launch_bounds__(kBlock) void int4_dequant_wave(const uint8_t *__restrict__ packed,
                                                             const float *__restrict__ scales,
                                                             const float *__restrict__ zeros,
-                                                            float *__restrict__ y,
+                                                            void *__restrict__ y,
                                                             uint64_t num_groups, uint32_t group_size) {
     const uint64_t g = global_wave();
     if (g >= num_groups) return;
     const float s = scales[g];
     const float zs = zeros[g] * s;
     const uint8_t *in = packed + g * (group_size / 2);
-    float *out = y + g * group_size;
+    const uint64_t o0 = g * group_size;
     for (uint32_t p = lane_id(); p < group_size / 2; p += kWave) {
         const uint32_t b = in[p];
-        out[2 * p] = (float)(b & 15u) * s - zs;
-        out[2 * p + 1] = (float)(b >> 4) * s - zs;
+        store1<DT>(y, o0 + 2 * p, (float)(b & 15u) * s - zs);
+        store1<DT>(y, o0 + 2 * p + 1, (float)(b >> 4) * s - zs);
     }
 }
 
@@ -415,38 +462,108 @@ int check_int4(const char *fn, const void *a, const void *b, const void *c, cons
 
 using namespace kvq;
 
-extern "C" int kvq_quant_int8_token(const float *x, int8_t *codes, float *scales, uint32_t num_tokens,
-                                    uint32_t head_dim, void *stream) {
-    int st = check_kv_common("kvq_quant_int8_token", x, codes, scales, num_tokens, head_dim);
+namespace kvq {
+namespace {
+
+int check_dtype(const char *fn, int dt) {
+    if (dt != KVQ_DT_F32 && dt != KVQ_DT_F16 && dt != KVQ_DT_BF16)
+        return fail(KVQ_E_INVALID, "%s: dtype %d is not fp32 (0), fp16 (1) or bf16 (2)", fn, dt);
+    return KVQ_OK;
+}
+
+#define KVQ_DT_SWITCH(DTV, CALL)                                  \
+    switch (DTV) {                                                \
+        case KVQ_DT_F32: { constexpr int D_ = 0; CALL; } break;   \
+        case KVQ_DT_F16: { constexpr int D_ = 1; CALL; } break;   \
+        default: { constexpr int D_ = 2; CALL; } break;           \
+    }
+
+int int8_quant(const char *fn, const void *x, int dt, int8_t *codes, float *scales, uint32_t num_tokens,
+               uint32_t head_dim, hipStream_t s) {
+    int st = check_kv_common(fn, x, codes, scales, num_tokens, head_dim);
+    if (!st) st = check_dtype(fn, dt);
     if (st) return st;
     const int L = team_lanes(head_dim);
-    hipStream_t s = as_stream(stream);
     if (L) {
         const uint64_t per_block = (uint64_t)kWavesPerBlock * kQuantUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int8_quant_team<LL, kQuantUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
-                               (const f32x4 *)x, (uint32_t *)codes, scales, num_tokens)));
+        KVQ_DT_SWITCH(dt, KVQ_TEAM_SWITCH(L, (int8_quant_team<LL, kQuantUnroll, D_><<<blocks_for(num_tokens, per_block),
+                                                                                       kBlock, 0, s>>>(
+                                                 x, (uint32_t *)codes, scales, num_tokens))));
     } else {
-        int8_quant_wave<<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(x, codes, scales, num_tokens,
-                                                                                  head_dim);
+        KVQ_DT_SWITCH(dt, (int8_quant_wave<D_><<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(
+                              x, codes, scales, num_tokens, head_dim)));
     }
-    return launch_status("kvq_quant_int8_token");
+    return launch_status(fn);
+}
+
+int int8_dequant(const char *fn, const int8_t *codes, const float *scales, void *y, int dt, uint32_t num_tokens,
+                 uint32_t head_dim, hipStream_t s) {
+    int st = check_kv_common(fn, codes, scales, y, num_tokens, head_dim);
+    if (!st) st = check_dtype(fn, dt);
+    if (st) return st;
+    const int L = team_lanes(head_dim);
+    if (L) {
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kDequantUnroll * (kWave / L);
+        KVQ_DT_SWITCH(dt, KVQ_TEAM_SWITCH(L, (int8_dequant_team<LL, kDequantUnroll, D_><<<
+                                                 blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
+                                                 (const uint32_t *)codes, scales, y, num_tokens))));
+    } else {
+        KVQ_DT_SWITCH(dt, (int8_dequant_wave<D_><<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(
+                              codes, scales, y, num_tokens, head_dim)));
+    }
+    return launch_status(fn);
+}
+
+int int4_quant(const char *fn, const void *x, int dt, uint8_t *packed, float *scales, float *zeros,
+               uint32_t num_tokens, uint32_t head_dim, uint32_t group_size, hipStream_t s) {
+    int st = check_int4(fn, x, packed, scales, zeros, num_tokens, head_dim, group_size);
+    if (!st) st = check_dtype(fn, dt);
+    if (st) return st;
+    const uint64_t groups = (uint64_t)num_tokens * head_dim / group_size;
+    const int L = team_lanes(group_size);
+    if (L) {
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kQuantUnroll * (kWave / L);
+        KVQ_DT_SWITCH(dt, KVQ_TEAM_SWITCH(L, (int4_quant_team<LL, kQuantUnroll, D_><<<blocks_for(groups, per_block),
+                                                                                       kBlock, 0, s>>>(
+                                                 x, (uint16_t *)packed, scales, zeros, groups))));
+    } else {
+        KVQ_DT_SWITCH(dt, (int4_quant_wave<D_><<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(
+                              x, packed, scales, zeros, groups, group_size)));
+    }
+    return launch_status(fn);
+}
+
+int int4_dequant(const char *fn, const uint8_t *packed, const float *scales, const float *zeros, void *y, int dt,
+                 uint32_t num_tokens, uint32_t head_dim, uint32_t group_size, hipStream_t s) {
+    int st = check_int4(fn, packed, scales, zeros, y, num_tokens, head_dim, group_size);
+    if (!st) st = check_dtype(fn, dt);
+    if (st) return st;
+    const uint64_t groups = (uint64_t)num_tokens * head_dim / group_size;
+    const int L = team_lanes(group_size);
+    if (L) {
+        const uint64_t per_block = (uint64_t)kWavesPerBlock * kDequantUnroll * (kWave / L);
+        KVQ_DT_SWITCH(dt, KVQ_TEAM_SWITCH(L, (int4_dequant_team<LL, kDequantUnroll, D_><<<
+                                                 blocks_for(groups, per_block), kBlock, 0, s>>>(
+                                                 (const uint16_t *)packed, scales, zeros, y, groups))));
+    } else {
+        KVQ_DT_SWITCH(dt, (int4_dequant_wave<D_><<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(
+                              packed, scales, zeros, y, groups, group_size)));
+    }
+    return launch_status(fn);
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" int kvq_quant_int8_token(const float *x, int8_t *codes, float *scales, uint32_t num_tokens,
+                                    uint32_t head_dim, void *stream) {
+    return int8_quant("kvq_quant_int8_token", x, KVQ_DT_F32, codes, scales, num_tokens, head_dim, as_stream(stream));
 }
 
 extern "C" int kvq_dequant_int8_token(const int8_t *codes, const float *scales, float *y, uint32_t num_tokens,
                                       uint32_t head_dim, void *stream) {
-    int st = check_kv_common("kvq_dequant_int8_token", codes, scales, y, num_tokens, head_dim);
-    if (st) return st;
-    const int L = team_lanes(head_dim);
-    hipStream_t s = as_stream(stream);
-    if (L) {
-        const uint64_t per_block = (uint64_t)kWavesPerBlock * kDequantUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int8_dequant_team<LL, kDequantUnroll><<<blocks_for(num_tokens, per_block), kBlock, 0, s>>>(
-                               (const uint32_t *)codes, scales, (f32x4 *)y, num_tokens)));
-    } else {
-        int8_dequant_wave<<<blocks_for(num_tokens, kWavesPerBlock), kBlock, 0, s>>>(codes, scales, y, num_tokens,
-                                                                                    head_dim);
-    }
-    return launch_status("kvq_dequant_int8_token");
+    return int8_dequant("kvq_dequant_int8_token", codes, scales, y, KVQ_DT_F32, num_tokens, head_dim,
+                        as_stream(stream));
 }
 
 extern "C" int kvq_quant_fp8_token(const float *x, int8_t *codes, float *scales, uint32_t num_tokens,
@@ -461,38 +578,38 @@ extern "C" int kvq_dequant_fp8_token(const int8_t *codes, const float *scales, f
 
 extern "C" int kvq_quant_int4_group(const float *x, uint8_t *packed, float *scales, float *zeros,
                                     uint32_t num_tokens, uint32_t head_dim, uint32_t group_size, void *stream) {
-    int st = check_int4("kvq_quant_int4_group", x, packed, scales, zeros, num_tokens, head_dim, group_size);
-    if (st) return st;
-    const uint64_t groups = (uint64_t)num_tokens * head_dim / group_size;
-    const int L = team_lanes(group_size);
-    hipStream_t s = as_stream(stream);
-    if (L) {
-        const uint64_t per_block = (uint64_t)kWavesPerBlock * kQuantUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int4_quant_team<LL, kQuantUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
-                               (const f32x4 *)x, (uint16_t *)packed, scales, zeros, groups)));
-    } else {
-        int4_quant_wave<<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(x, packed, scales, zeros, groups,
-                                                                              group_size);
-    }
-    return launch_status("kvq_quant_int4_group");
+    return int4_quant("kvq_quant_int4_group", x, KVQ_DT_F32, packed, scales, zeros, num_tokens, head_dim,
+                      group_size, as_stream(stream));
 }
 
 extern "C" int kvq_dequant_int4_group(const uint8_t *packed, const float *scales, const float *zeros, float *y,
                                       uint32_t num_tokens, uint32_t head_dim, uint32_t group_size, void *stream) {
-    int st = check_int4("kvq_dequant_int4_group", packed, scales, zeros, y, num_tokens, head_dim, group_size);
-    if (st) return st;
-    const uint64_t groups = (uint64_t)num_tokens * head_dim / group_size;
-    const int L = team_lanes(group_size);
-    hipStream_t s = as_stream(stream);
-    if (L) {
-        const uint64_t per_block = (uint64_t)kWavesPerBlock * kDequantUnroll * (kWave / L);
-        KVQ_TEAM_SWITCH(L, (int4_dequant_team<LL, kDequantUnroll><<<blocks_for(groups, per_block), kBlock, 0, s>>>(
-                               (const uint16_t *)packed, scales, zeros, (f32x4 *)y, groups)));
-    } else {
-        int4_dequant_wave<<<blocks_for(groups, kWavesPerBlock), kBlock, 0, s>>>(packed, scales, zeros, y, groups,
-                                                                                group_size);
-    }
-    return launch_status("kvq_dequant_int4_group");
+    return int4_dequant("kvq_dequant_int4_group", packed, scales, zeros, y, KVQ_DT_F32, num_tokens, head_dim,
+                        group_size, as_stream(stream));
+}
+
+extern "C" int kvq_quant_int8_token_dt(const void *x, int x_dtype, int8_t *codes, float *scales,
+                                       uint32_t num_tokens, uint32_t head_dim, void *stream) {
+    return int8_quant("kvq_quant_int8_token_dt", x, x_dtype, codes, scales, num_tokens, head_dim, as_stream(stream));
+}
+
+extern "C" int kvq_dequant_int8_token_dt(const int8_t *codes, const float *scales, void *y, int y_dtype,
+                                         uint32_t num_tokens, uint32_t head_dim, void *stream) {
+    return int8_dequant("kvq_dequant_int8_token_dt", codes, scales, y, y_dtype, num_tokens, head_dim,
+                        as_stream(stream));
+}
+
+extern "C" int kvq_quant_int4_group_dt(const void *x, int x_dtype, uint8_t *packed, float *scales, float *zeros,
+                                       uint32_t num_tokens, uint32_t head_dim, uint32_t group_size, void *stream) {
+    return int4_quant("kvq_quant_int4_group_dt", x, x_dtype, packed, scales, zeros, num_tokens, head_dim,
+                      group_size, as_stream(stream));
+}
+
+extern "C" int kvq_dequant_int4_group_dt(const uint8_t *packed, const float *scales, const float *zeros, void *y,
+                                         int y_dtype, uint32_t num_tokens, uint32_t head_dim, uint32_t group_size,
+                                         void *stream) {
+    return int4_dequant("kvq_dequant_int4_group_dt", packed, scales, zeros, y, y_dtype, num_tokens, head_dim,
+                        group_size, as_stream(stream));
 }
 
 extern "C" int kvq_quant_int8_tensor(const float *x, int8_t *codes, float *scale, uint32_t num_tokens,

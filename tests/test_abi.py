@@ -175,3 +175,20 @@ def test_kv_int8_tensor_workspace_rules(lib):
     for ws, nbytes in ((None, need), (FAKE, need - 1), (MISALIGNED, need)):
         st, msg = _err(lib, "kvq_quant_int8_tensor", FAKE, FAKE, FAKE, 4, 8, ws, nbytes, None)
         assert st == _lib.KVQ_E_INVALID and "workspace" in msg, msg
+
+
+@pytest.mark.parametrize("dt", [3, -1])
+def test_kv_dtype_validation(lib, dt):
+    for fn, args in (("kvq_quant_int8_token_dt", (FAKE, dt, FAKE, FAKE, 4, 8, None)),
+                     ("kvq_dequant_int8_token_dt", (FAKE, FAKE, FAKE, dt, 4, 8, None)),
+                     ("kvq_quant_int4_group_dt", (FAKE, dt, FAKE, FAKE, FAKE, 4, 8, 4, None)),
+                     ("kvq_dequant_int4_group_dt", (FAKE, FAKE, FAKE, FAKE, dt, 4, 8, 4, None))):
+        st, msg = _err(lib, fn, *args)
+        assert st == _lib.KVQ_E_INVALID and "dtype" in msg, (fn, msg)
+
+
+def test_kv_dtype_calls_share_the_fp32_checks(lib):
+    st, msg = _err(lib, "kvq_quant_int8_token_dt", FAKE, 1, FAKE, FAKE, 0, 8, None)
+    assert st == _lib.KVQ_E_INVALID and "num_tokens=0" in msg
+    st, msg = _err(lib, "kvq_quant_int4_group_dt", FAKE, 2, FAKE, FAKE, FAKE, 4, 8, 3, None)
+    assert st == _lib.KVQ_E_INVALID and "group_size" in msg

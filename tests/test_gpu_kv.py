@@ -164,3 +164,101 @@ def test_int8_tensor_repeated_calls_share_workspace():
     b = synth.kv_cache(100, 33, seed=82)
     for x in (a, b, a):
         _int8_tensor_case(x)
+
+
+# ----------------------------------------------- 16-bit KV value formats ----
+
+_TDT = {1: torch.float16, 2: torch.bfloat16}
+
+
+def _dev16(bits, dt):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(_TDT[dt])
+
+
+def _bits16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _to16(x, dt):
+    return _oracle.narrow16(x, dt)
+
+
+def _int8_dt_case(xb, dt):
+    t, d = xb.shape
+    codes, raw_c = poisoned((t, d), torch.int8)
+    scales, raw_s = poisoned((t,), torch.float32)
+    api.quant_int8_token(_dev16(xb, dt), codes, scales)
+    rc, rs = _oracle.kv_int8_quant_dt(xb, dt)
+    y, raw_y = poisoned((t, d), _TDT[dt])
+    api.dequant_int8_token(dev(rc), dev(rs), y)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(codes), rc, f"int8 codes dt={dt}")
+    assert_bits_equal(host(scales), rs, f"int8 scales dt={dt}")
+    assert_bits_equal(_bits16(y), _oracle.kv_int8_dequant_dt(rc, rs, dt), f"int8 dequant dt={dt}")
+    for raw, nb in ((raw_c, t * d), (raw_s, t * 4), (raw_y, t * d * 2)):
+        assert_canary(raw, nb)
+
+
+def _int4_dt_case(xb, gs, dt):
+    t, d = xb.shape
+    n = t * d
+    packed, raw_p = poisoned((n // 2,), torch.uint8)
+    scales, raw_s = poisoned((n // gs,), torch.float32)
+    zeros, raw_z = poisoned((n // gs,), torch.float32)
+    api.quant_int4_group(_dev16(xb, dt), gs, packed, scales, zeros)
+    rp, rs, rz = _oracle.kv_int4_quant_dt(xb, gs, dt)
+    y, raw_y = poisoned((t, d), _TDT[dt])
+    api.dequant_int4_group(dev(rp), dev(rs), dev(rz), t, d, gs, y)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(packed), rp, f"int4 packed dt={dt}")
+    assert_bits_equal(host(scales), rs, f"int4 scales dt={dt}", zero_by_value=True)
+    assert_bits_equal(host(zeros), rz, f"int4 zeros dt={dt}", zero_by_value=True)
+    assert_bits_equal(_bits16(y), _oracle.kv_int4_dequant_dt(rp, rs, rz, t, d, gs, dt), f"int4 dequant dt={dt}")
+    for raw, nb in ((raw_p, n // 2), (raw_s, n // gs * 4), (raw_z, n // gs * 4), (raw_y, n * 2)):
+        assert_canary(raw, nb)
+
+
+@pytest.mark.parametrize("dt", [1, 2])
+@pytest.mark.parametrize("t,d", [(32768, 128), (3, 7), (33, 4), (1001, 96), (2, 300)])
+def test_int8_16bit_parity(dt, t, d):
+    print_case("kv int8 16-bit", dt, t, d)
+    _int8_dt_case(_to16(synth.kv_cache(t, d, seed=2 if (t, d) == (32768, 128) else 400 + t + d), dt), dt)
+
+
+@pytest.mark.parametrize("dt", [1, 2])
+@pytest.mark.parametrize("t,d,gs", [(32768, 128, 32), (8, 10, 2), (17, 96, 6), (6, 128, 256), (1001, 128, 32)])
+def test_int4_16bit_parity(dt, t, d, gs):
+    print_case("kv int4 16-bit", dt, t, d, gs)
+    _int4_dt_case(_to16(synth.kv_cache(t, d, seed=2 if (t, d) == (32768, 128) else 500 + t + d + gs), dt), gs, dt)
+
+
+@pytest.mark.parametrize("dt", [1, 2])
+def test_16bit_edges(dt):
+    """Signed zeros, the format's smallest and largest finite values, exact ties."""
+    print_case("kv 16-bit edges", dt)
+    x = np.zeros((64, 128), np.float32)
+    x[2, ::2] = -0.0
+    x[3] = 6e-8 if dt == 1 else 1e-38            # fp16 subnormal / bf16 near the normal floor
+    x[4, :5] = [65504.0, -65504.0, 1.0, -1.0, 0.5] if dt == 1 else [1.0e38, -1.0e38, 1.0, -1.0, 0.5]
+    x[5] = np.tile([2.5, -2.5, 0.5, 1.5], 32)
+    rng = np.random.default_rng(90 + dt)
+    x[6:] = rng.standard_normal((58, 128)) * np.exp2(rng.integers(-12, 12, (58, 1)))
+    xb = _to16(x, dt)
+    _int8_dt_case(xb, dt)
+    _int4_dt_case(xb, 32, dt)
+    _int4_dt_case(xb, 2, dt)
+
+
+def test_fp32_dtype_path_equals_fp32_calls():
+    """The dtype entry points with fp32 are the fp32 calls."""
+    print_case("kv dt=fp32 path")
+    x = synth.kv_cache(100, 64, seed=91)
+    c1, s1 = api.quant_int8_token(dev(x))
+    c2 = torch.empty_like(c1)
+    s2 = torch.empty_like(s1)
+    xd = dev(x)
+    from kv_quantization_amd import _lib
+    _lib.call("kvq_quant_int8_token_dt", xd.data_ptr(), 0, c2.data_ptr(), s2.data_ptr(), 100, 64,
+              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
