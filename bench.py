@@ -79,11 +79,30 @@ def kernel_table():
     return rows
 
 
+AWQ_EXTRA_MS = (4, 8)
+
+
+def awq_bytes(m, xbytes=4):
+    na = sum(AWQ_NS)
+    return AWQ_K * na // 2 + 2 * (AWQ_K // AWQ_GS) * na * 4 + m * AWQ_K * xbytes + m * na * 4
+
+
 def extra_table():
-    """Kernels timed beside the step but not part of it (the per-tensor KV
-    mode, a widening of the path): (name, algorithmic bytes, flops, kind)."""
+    """Kernels timed beside the step but not part of it (widenings of the
+    path: per-tensor KV mode, bf16 KV caches, INT4 at M between the
+    configurations and with fp16 activations): (name, bytes, flops, kind)."""
     kv = KV_T * KV_D * 4 + KV_T * KV_D + 4
-    return [("kv_int8_quant_tensor", kv, 0, "hbm"), ("kv_int8_dequant_tensor", kv, 0, "hbm")]
+    n = KV_T * KV_D
+    g = n // KV_GS
+    na = sum(AWQ_NS)
+    rows = [("kv_int8_quant_tensor", kv, 0, "hbm"), ("kv_int8_dequant_tensor", kv, 0, "hbm"),
+            ("kv_int8_quant_bf16", n * 2 + n + KV_T * 4, 0, "hbm"),
+            ("kv_int8_dequant_bf16", n * 2 + n + KV_T * 4, 0, "hbm"),
+            ("kv_int4_quant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm"),
+            ("kv_int4_dequant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm")]
+    rows += [(f"int4_awq_qkv_M{m}", awq_bytes(m), 2 * m * na * AWQ_K, "fp16") for m in AWQ_EXTRA_MS]
+    rows += [(f"int4_awq_qkv_f16x_M{m}", awq_bytes(m, 2), 2 * m * na * AWQ_K, "fp16") for m in (1, 16)]
+    return rows
 
 
 def roofline_for(name, nbytes, flops, kind, seconds):
@@ -112,6 +131,8 @@ def make_inputs(torch, api, synth):
     s["down_w"] = [api.weight_quant(dev(w), api.BLK128) for w in down.weights]
     x5, projs = synth.int4_qkv(seed=5)
     s["awq_x"] = dev(x5)
+    s["awq_x16"] = s["awq_x"].to(torch.float16)
+    s["kv_x16"] = s["kv_x"].to(torch.bfloat16)
     s["awq_p"] = [(dev(p.qweight.view(np.int32)), dev(p.scales), dev(p.zeros)) for p in projs]
     torch.cuda.synchronize()
     return s, (qkv, down, x5, projs)
@@ -144,6 +165,15 @@ class StepBuffers:
         self.kvt_codes = e((KV_T, KV_D), torch.int8)
         self.kvt_scale = e((1,), torch.float32)
         self.kvt_y = e((KV_T, KV_D), torch.float32)
+        self.kv16_codes = e((KV_T, KV_D), torch.int8)
+        self.kv16_scales = e((KV_T,), torch.float32)
+        self.kv16_y = e((KV_T, KV_D), torch.bfloat16)
+        self.kv16_packed = e((KV_T * KV_D // 2,), torch.uint8)
+        self.kv16_s4 = e((g,), torch.float32)
+        self.kv16_z4 = e((g,), torch.float32)
+        self.kv16_y4 = e((KV_T, KV_D), torch.bfloat16)
+        self.awqx_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_EXTRA_MS + (1, 16)}
+        self.awq16_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in (1, 16)}
         self.qkv_weight = api.W8a8Weight(api.ROWSCALE, s["qkv_w"])
         self.down_weight = api.W8a8Weight(api.BLK128, s["down_w"])
         self.qkv_q = {m: e((m, QKV_K), torch.uint8) for m in QKV_MS}
@@ -164,9 +194,22 @@ class StepBuffers:
 
     def extra_launchers(self, api):
         s = self.s
-        return [("kv_int8_quant_tensor", lambda: api.quant_int8_tensor(s["kv_x"], self.kvt_codes, self.kvt_scale)),
-                ("kv_int8_dequant_tensor", lambda: api.dequant_int8_tensor(self.kvt_codes, self.kvt_scale,
-                                                                           self.kvt_y))]
+        L = [("kv_int8_quant_tensor", lambda: api.quant_int8_tensor(s["kv_x"], self.kvt_codes, self.kvt_scale)),
+             ("kv_int8_dequant_tensor", lambda: api.dequant_int8_tensor(self.kvt_codes, self.kvt_scale, self.kvt_y)),
+             ("kv_int8_quant_bf16", lambda: api.quant_int8_token(s["kv_x16"], self.kv16_codes, self.kv16_scales)),
+             ("kv_int8_dequant_bf16", lambda: api.dequant_int8_token(self.kv16_codes, self.kv16_scales,
+                                                                     self.kv16_y)),
+             ("kv_int4_quant_bf16", lambda: api.quant_int4_group(s["kv_x16"], KV_GS, self.kv16_packed, self.kv16_s4,
+                                                                 self.kv16_z4)),
+             ("kv_int4_dequant_bf16", lambda: api.dequant_int4_group(self.kv16_packed, self.kv16_s4, self.kv16_z4,
+                                                                     KV_T, KV_D, KV_GS, self.kv16_y4))]
+        for m in AWQ_EXTRA_MS:
+            L.append((f"int4_awq_qkv_M{m}", lambda m=m: api.int4_awq_qkv(s["awq_x"][:m], s["awq_p"], AWQ_GS,
+                                                                          outs=self.awqx_out[m])))
+        for m in (1, 16):
+            L.append((f"int4_awq_qkv_f16x_M{m}", lambda m=m: api.int4_awq_qkv(s["awq_x16"][:m], s["awq_p"], AWQ_GS,
+                                                                               outs=self.awq16_out[m])))
+        return L
 
     # each launcher issues exactly one call
     def launchers(self, api):

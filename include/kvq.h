@@ -270,6 +270,17 @@ int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k,
 int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_size,
                              uint32_t n_total, size_t *bytes);
 
+/* The same call with 16-bit activations (kvq_dtype_t: KVQ_DT_F32, KVQ_DT_F16
+ * or KVQ_DT_BF16; x holds m*k values of that type).  fp16 values go to the
+ * matrix cores unchanged; bf16 values are widened exactly and rounded to
+ * fp16 like fp32 input (exact for |x| in [2^-14, 65504]).  Outputs stay fp32.
+ * KVQ_DT_F32 is exactly int4_awq_qkv_gemm. */
+int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k,
+                         uint32_t group_size, const int4_awq_proj_t *q_proj,
+                         const int4_awq_proj_t *k_proj,
+                         const int4_awq_proj_t *v_proj, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* ======================================================================== */
 /* Measurement helper (not part of the method)                              */
 /* kvq_stream_read: reads `bytes` (a positive multiple of 16) at `src` (16-

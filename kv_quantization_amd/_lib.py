@@ -55,6 +55,8 @@ SIGNATURES = {
     "int4_awq_qkv_gemm": [_p, _u32, _u32, _u32, ctypes.POINTER(Int4AwqProj), ctypes.POINTER(Int4AwqProj),
                           ctypes.POINTER(Int4AwqProj), _p, _sz, _p],
     "int4_awq_workspace_bytes": [_u32, _u32, _u32, _u32, _psz],
+    "int4_awq_qkv_gemm_dt": [_p, _i, _u32, _u32, _u32, ctypes.POINTER(Int4AwqProj), ctypes.POINTER(Int4AwqProj),
+                             ctypes.POINTER(Int4AwqProj), _p, _sz, _p],
     "kvq_stream_read": [_p, _sz, _p, _p],
 }
 

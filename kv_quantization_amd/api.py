@@ -276,7 +276,7 @@ def int4_workspace_bytes(m: int, k: int, group_size: int, n_total: int) -> int:
 
 
 def int4_awq_qkv(x: torch.Tensor, projections, group_size: int, outs=None, use_workspace: bool = True):
-    """x fp32 [m, k]; projections: 1 or 3 of (qweight int32/uint32 [k, n/8],
+    """x fp32/fp16/bf16 [m, k]; projections: 1 or 3 of (qweight int32/uint32 [k, n/8],
     scales fp32 [k/gs, n], zeros fp32 [k/gs, n]) -> list of fp32 [m, n]."""
     m, k = x.shape
     if len(projections) not in (1, 3):
@@ -304,8 +304,13 @@ def int4_awq_qkv(x: torch.Tensor, projections, group_size: int, outs=None, use_w
             ws_ptr = workspace(x.device, ws_bytes, stream).data_ptr()
     kp = ctypes.byref(structs[1]) if len(structs) == 3 else None
     vp = ctypes.byref(structs[2]) if len(structs) == 3 else None
-    _lib.call("int4_awq_qkv_gemm", _dev(x, torch.float32, "x"), m, k, group_size, ctypes.byref(structs[0]), kp, vp,
-              ws_ptr, ws_bytes, stream)
+    xdt = _kv_dt(x, "x")
+    if xdt == 0:
+        _lib.call("int4_awq_qkv_gemm", _dev(x, torch.float32, "x"), m, k, group_size, ctypes.byref(structs[0]), kp,
+                  vp, ws_ptr, ws_bytes, stream)
+    else:
+        _lib.call("int4_awq_qkv_gemm_dt", _dev(x, x.dtype, "x"), xdt, m, k, group_size, ctypes.byref(structs[0]),
+                  kp, vp, ws_ptr, ws_bytes, stream)
     return res
 
 

@@ -106,12 +106,28 @@ __device__ __forceinline__ f32x4 mfma16(const f16x8 &a, const f16x8 &b, const f3
 
 __device__ __forceinline__ f32x4 as_f32x4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
 
+// Activation formats: XT 0 fp32 (two 16-byte loads per 8 values), 1 fp16
+// (one load; the values go to the matrix cores unchanged), 2 bf16 (one load;
+// widened exactly, then rounded to fp16 like fp32 input).
+template <int XT>
+__device__ __forceinline__ f16x8 act_f16x8(const u32x4 &lo, const u32x4 &hi) {
+    if (XT == 0) return to_f16x8(as_f32x4(lo), as_f32x4(hi));
+    if (XT == 1) return __builtin_bit_cast(f16x8, lo);
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[2 * i] = (_Float16)__uint_as_float(lo[i] << 16);
+        h[2 * i + 1] = (_Float16)__uint_as_float(lo[i] & 0xFFFF0000u);
+    }
+    return h;
+}
+
 // MT: 16-row activation tiles per chunk (1 or 2).  R: accumulator rows per
 // lane that can hold real outputs (1 when m == 1, else 4).  KSG: 32-wide K
 // steps per quantization group.  U: K steps loaded together (a "piece"; U
 // divides KSG).  PF: prefetch the next piece while computing this one.
-template <int MT, int R, int KSG, int U, bool PF>
-__global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, uint32_t M, uint32_t K, Projs P,
+template <int MT, int R, int KSG, int U, bool PF, int XT>
+__global__ __launch_bounds__(kBlock) void awq_gemm(const void *__restrict__ x, uint32_t M, uint32_t K, Projs P,
                                                    uint32_t nchunks, uint32_t ks_b, uint32_t *__restrict__ counters,
                                                    float *__restrict__ partials) {
     constexpr int MR = 16 * MT;
@@ -157,13 +173,14 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
     const uint32_t wbytes = K * wp * 4;
     const rsrc_t rw = make_rsrc(pick(p, P.qw[0], P.qw[1], P.qw[2]), wbytes);
     const uint32_t voff_w = wok ? ((uint32_t)(kg * 8) * wp + lw) * 4 : wbytes;
-    const uint32_t xbytes = M * K * 4;
+    constexpr uint32_t XB = XT == 0 ? 4 : 2;   // bytes per activation value
+    const uint32_t xbytes = M * K * XB;
     const rsrc_t rx = make_rsrc(x, xbytes);
     uint32_t voff_x[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const uint32_t m = c * MR + mt * 16 + wc;
-        voff_x[mt] = m < M ? (m * K + kg * 8) * 4 : xbytes;
+        voff_x[mt] = m < M ? (m * K + kg * 8) * XB : xbytes;
     }
     const uint32_t szbytes = (K / GS) * np * 4;
     const rsrc_t rs = make_rsrc(pick(p, P.sc[0], P.sc[1], P.sc[2]), szbytes);
@@ -202,8 +219,8 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
                 pz.w[u][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, (k0 + i) * wp * 4, 0);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                pz.xv[u][mt][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * 4, 0);
-                pz.xv[u][mt][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * 4 + 16, 0);
+                pz.xv[u][mt][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * XB, 0);
+                if (XT == 0) pz.xv[u][mt][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * 4 + 16, 0);
             }
         }
     };
@@ -214,7 +231,7 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const float *__restrict__ x, 
             awq_operands(pz.w[u], B);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const f16x8 a = to_f16x8(as_f32x4(pz.xv[u][mt][0]), as_f32x4(pz.xv[u][mt][1]));
+                const f16x8 a = act_f16x8<XT>(pz.xv[u][mt][0], pz.xv[u][mt][1]);
                 xg[mt] = mfma16(a, ones, xg[mt]);
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = mfma16(a, B[cc], pg[mt][cc]);
@@ -394,11 +411,14 @@ extern "C" int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_s
     return KVQ_OK;
 }
 
-extern "C" int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k, uint32_t group_size,
-                                 const int4_awq_proj_t *q_proj, const int4_awq_proj_t *k_proj,
-                                 const int4_awq_proj_t *v_proj, void *workspace, size_t workspace_bytes,
-                                 void *stream) {
-    const char *fn = "int4_awq_qkv_gemm";
+namespace kvq {
+namespace {
+
+int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint32_t group_size,
+            const int4_awq_proj_t *q_proj, const int4_awq_proj_t *k_proj, const int4_awq_proj_t *v_proj,
+            void *workspace, size_t workspace_bytes, void *stream) {
+    if (xt != KVQ_DT_F32 && xt != KVQ_DT_F16 && xt != KVQ_DT_BF16)
+        return fail(KVQ_E_INVALID, "%s: x dtype %d is not fp32 (0), fp16 (1) or bf16 (2)", fn, xt);
     if (!x || !q_proj) return fail(KVQ_E_INVALID, "%s: null x or q projection", fn);
     if (!aligned16(x)) return fail(KVQ_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
     if (m == 0) return fail(KVQ_E_INVALID, "%s: m == 0", fn);
@@ -448,9 +468,18 @@ extern "C" int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k, uint32_
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
     hipStream_t s = as_stream(stream);
     const uint32_t ksg = group_size / 32;
-#define KVQ_AWQ(MT, R, KSG, U, PF)                                                                            \
-    awq_gemm<MT, R, KSG, U, PF><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b, counters, \
-                                                                    partials)
+#define KVQ_AWQ(MT, R, KSG, U, PF)                                                                               \
+    do {                                                                                                         \
+        if (xt == KVQ_DT_F32)                                                                                    \
+            awq_gemm<MT, R, KSG, U, PF, 0><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b,  \
+                                                                               counters, partials);              \
+        else if (xt == KVQ_DT_F16)                                                                               \
+            awq_gemm<MT, R, KSG, U, PF, 1><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b,  \
+                                                                               counters, partials);              \
+        else                                                                                                     \
+            awq_gemm<MT, R, KSG, U, PF, 2><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b,  \
+                                                                               counters, partials);              \
+    } while (0)
 #define KVQ_AWQ_K(MT, R, CAP, PF)                                   \
     switch (ksg) {                                                  \
         case 1: KVQ_AWQ(MT, R, 1, 1, PF); break;                    \
@@ -467,4 +496,23 @@ extern "C" int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k, uint32_
 #undef KVQ_AWQ_K
 #undef KVQ_AWQ
     return launch_status(fn);
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k, uint32_t group_size,
+                                 const int4_awq_proj_t *q_proj, const int4_awq_proj_t *k_proj,
+                                 const int4_awq_proj_t *v_proj, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    return awq_run("int4_awq_qkv_gemm", x, KVQ_DT_F32, m, k, group_size, q_proj, k_proj, v_proj, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k, uint32_t group_size,
+                                    const int4_awq_proj_t *q_proj, const int4_awq_proj_t *k_proj,
+                                    const int4_awq_proj_t *v_proj, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+    return awq_run("int4_awq_qkv_gemm_dt", x, x_dtype, m, k, group_size, q_proj, k_proj, v_proj, workspace,
+                   workspace_bytes, stream);
 }

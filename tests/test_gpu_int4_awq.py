@@ -127,3 +127,49 @@ def test_degenerate_scales_zeros():
     p.zeros = np.zeros_like(p.zeros)
     got = _run(xi, [p], 64)
     np.testing.assert_array_equal(got[0], (xi.astype(np.int64) @ codes.astype(np.int64)).astype(np.float32))
+
+
+# ------------------------------------------- M = 2..15 and 16-bit activations --
+
+_qkv = {}
+
+
+def _qkv_inputs():
+    if not _qkv:
+        x5, projs = synth.int4_qkv(seed=5)
+        _qkv.update(x=x5, projs=projs)
+    return _qkv["x"], _qkv["projs"]
+
+
+@pytest.mark.parametrize("m", [2, 3, 4, 7, 8, 12, 15])
+def test_fused_qkv_small_m(m):
+    """The fused QKV workload between the M=1 and M=16 configurations."""
+    print_case("int4 qkv small m", m)
+    x5, projs = _qkv_inputs()
+    x = x5[:m]
+    _check(x, projs, 128, _run(x, projs, 128), f"qkv M={m}")
+
+
+def _run16(x16_bits, dt, projs, gs):
+    tdt = {1: torch.float16, 2: torch.bfloat16}[dt]
+    xd = torch.from_numpy(np.ascontiguousarray(x16_bits).view(np.int16)).cuda().view(tdt)
+    outs = api.int4_awq_qkv(xd, [(dev(p.qweight), dev(p.scales), dev(p.zeros)) for p in projs], gs)
+    torch.cuda.synchronize()
+    return [host(o) for o in outs]
+
+
+@pytest.mark.parametrize("dt", [1, 2])
+@pytest.mark.parametrize("m", [1, 5, 16, 40, 128])
+def test_16bit_activations(dt, m):
+    """fp16/bf16 x: within the bound of the oracle on the exact (widened)
+    values, and bit-identical to the fp32 call on those values (both reach
+    the matrix cores as the same fp16 operands)."""
+    print_case("int4 16-bit x", dt, m)
+    x5, projs = _qkv_inputs()
+    xb = _oracle.narrow16(x5[:m], dt)
+    xw = _oracle.widen16(xb, dt)
+    got16 = _run16(xb, dt, projs, 128)
+    _check(xw, projs, 128, got16, f"qkv M={m} dt={dt}")
+    got32 = _run(xw, projs, 128)
+    for a, b in zip(got16, got32):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
