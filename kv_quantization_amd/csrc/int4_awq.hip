@@ -333,9 +333,21 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const void *__restrict__ x, u
         const uint32_t m = c * MR + row;
         const uint32_t lwo = tp * 16 + (col4 >> 1);
         if (m >= M || lwo >= wp) continue;
+        // up to 8 partials in flight, added in slice order (deterministic;
+        // one load at a time paid a memory round trip per slice)
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        for (uint32_t q = 0; q < ks_b; ++q)
-            v += as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rp, ((q * MR + row) * 128 + col4 * 4) * 4, 0, kAuxSc1));
+        for (uint32_t q0 = 0; q0 < ks_b; q0 += 8) {
+            u32x4 t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t q = q0 + u;
+                const uint32_t off = q < ks_b ? ((q * MR + row) * 128 + col4 * 4) * 4 : kOffNone;
+                t[u] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSc1);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < ks_b) v += as_f32x4(t[u]);
+        }
         *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + 8 * lwo + (col4 & 1) * 4) = v;
     }
     if (threadIdx.x == 0) __hip_atomic_store(&counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
