@@ -56,6 +56,34 @@ __device__ __forceinline__ int seg_of(const Segs &S, uint32_t j) {
 // (non-temporal), as the nontemporal global loads below.
 constexpr int kAuxNt = 2;
 
+// Column tile nt (16 output columns) of this workgroup and the lanes (weight
+// rows r16 in [rlo, rhi)) it loads.  Plain: NT consecutive tiles.  Balanced
+// (BAL, NT == 2): a pair of workgroups shares three tiles, the first taking
+// tile 3p and rows 0-7 of tile 3p+1, the second rows 8-15 of tile 3p+1 and
+// tile 3p+2, so 384 tiles make 256 equal workgroups (one per CU) instead of
+// 384 (half the CUs with twice the bytes); the MFMA lanes of the other half
+// tile read zeros.
+template <int NT, bool BAL>
+__device__ __forceinline__ void col_tile(int nt, uint32_t &tile, uint32_t &rlo, uint32_t &rhi) {
+    if (!BAL) {
+        tile = blockIdx.x * NT + nt;
+        rlo = 0;
+        rhi = 16;
+    } else {
+        static_assert(!BAL || NT == 2, "balanced tiling pairs two column tiles");
+        const uint32_t h = blockIdx.x & 1u;
+        tile = 3u * (blockIdx.x >> 1) + h + nt;
+        rlo = (h == 1 && nt == 0) ? 8u : 0u;
+        rhi = (h == 0 && nt == 1) ? 8u : 16u;
+    }
+}
+
+template <int NT, bool BAL>
+inline unsigned col_grid(uint32_t ntotal) {
+    const uint32_t tiles = (ntotal + 15) / 16;
+    return BAL ? 2 * ((tiles + 2) / 3) : (tiles + NT - 1) / NT;
+}
+
 __device__ __forceinline__ i32x8 load_frag(const uint8_t *p) {
     // 16 bytes at p and 16 bytes at p + 64 (see the operand layout above)
     const u32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
@@ -93,7 +121,7 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 // as the other operand; partial sums meet in LDS.  MT 16-row tiles of
 // activations (rows <= 16*MT); KIND 0 per-row, 1 block scales.  NT > 1 reuses
 // each activation fragment for several column tiles.
-template <int MT, int NT, int W, int U, int KIND>
+template <int MT, int NT, int W, int U, int KIND, bool BAL>
 __global__ __launch_bounds__(W * kWave) void w8a8_skinny(const uint8_t *__restrict__ q,
                                                           const float *__restrict__ sa, uint32_t rows, uint32_t K,
                                                           Segs S, uint16_t *__restrict__ out, uint32_t ldc) {
@@ -105,17 +133,20 @@ __global__ __launch_bounds__(W * kWave) void w8a8_skinny(const uint8_t *__restri
     const uint32_t kb0 = wv * nkb / W, kb1 = (wv + 1) * nkb / W;
 
     int sg[NT];
-    uint32_t jloc0[NT], jrow[NT];
+    uint32_t jloc0[NT], jrow[NT], n0s[NT];
     bool jok[NT];
     const uint8_t *wrow[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const uint32_t n0 = (blockIdx.x * NT + nt) * 16u;
+        uint32_t tile, rlo, rhi;
+        col_tile<NT, BAL>(nt, tile, rlo, rhi);
+        const uint32_t n0 = tile * 16u;
+        n0s[nt] = n0;
         const uint32_t nn = n0 < S.ntotal ? n0 : 0;
         sg[nt] = seg_of(S, nn);
         jloc0[nt] = nn - S.start[sg[nt]];
         jrow[nt] = jloc0[nt] + r16;
-        jok[nt] = n0 < S.ntotal && jrow[nt] < S.n[sg[nt]];
+        jok[nt] = n0 < S.ntotal && jrow[nt] < S.n[sg[nt]] && (uint32_t)r16 >= rlo && (uint32_t)r16 < rhi;
         wrow[nt] = S.w[sg[nt]] + (size_t)(jok[nt] ? jrow[nt] : 0) * K + g * 16;
     }
     const uint8_t *arow[MT];
@@ -187,7 +218,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_skinny(const uint8_t *__restri
 #pragma unroll
         for (int w = 1; w < W; ++w) v += red[w][t][lane];
         if (jok[nt]) {
-            const uint32_t j = (blockIdx.x * NT + nt) * 16u + r16;
+            const uint32_t j = n0s[nt] + r16;
             const float sw = KIND == 0 ? S.s[sg[nt]][jrow[nt]] : 1.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -202,14 +233,14 @@ __global__ __launch_bounds__(W * kWave) void w8a8_skinny(const uint8_t *__restri
 }
 
 // launch for rows <= 32
-template <int MT, int NT, int W, int U>
+template <int MT, int NT, int W, int U, bool BAL = false>
 void skinny_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint32_t rows, uint32_t k,
                    const Segs &S, uint16_t *out, uint32_t ldc, hipStream_t s) {
-    const unsigned grid = ((S.ntotal + 15) / 16 + NT - 1) / NT;
+    const unsigned grid = col_grid<NT, BAL>(S.ntotal);
     if (kind == W8A8_ROWSCALE)
-        w8a8_skinny<MT, NT, W, U, 0><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+        w8a8_skinny<MT, NT, W, U, 0, BAL><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
     else
-        w8a8_skinny<MT, NT, W, U, 1><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
+        w8a8_skinny<MT, NT, W, U, 1, BAL><<<grid, W * kWave, 0, s>>>(q, a_scales, rows, k, S, out, ldc);
 }
 
 // --------------------------------------------------------- fused proj ---
@@ -233,7 +264,7 @@ void skinny_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, u
 constexpr uint32_t kFusedRows = 8;
 
 // R: activation rows the kernel is built for (rows <= R); W waves split K.
-template <int NT, int R, int W, int U, int KIND, bool SILU, bool UP>
+template <int NT, int R, int W, int U, int KIND, bool SILU, bool UP, bool BAL>
 __global__ __launch_bounds__(W * kWave) void w8a8_fused(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ up, uint32_t ldx, uint32_t rows, uint32_t K, Segs S,
     uint16_t *__restrict__ out, uint32_t ldc, uint8_t *__restrict__ qout, float *__restrict__ saout) {
@@ -255,18 +286,21 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
     // weights through buffer resources (one per column tile; a tile lies in
     // one segment), activations through one over the rows used
     int sg[NT];
-    uint32_t jloc0[NT], jrow[NT], woff[NT];
+    uint32_t jloc0[NT], jrow[NT], woff[NT], n0s[NT];
     bool jok[NT];
     rsrc_t rw[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const uint32_t n0 = (blockIdx.x * NT + nt) * 16u;
+        uint32_t tile, rlo, rhi;
+        col_tile<NT, BAL>(nt, tile, rlo, rhi);
+        const uint32_t n0 = tile * 16u;
+        n0s[nt] = n0;
         const uint32_t nn = n0 < S.ntotal ? n0 : 0;
         sg[nt] = seg_of(S, nn);
         jloc0[nt] = nn - pick(sg[nt], S.start[0], S.start[1], S.start[2]);
         jrow[nt] = jloc0[nt] + r16;
         const uint32_t segn = pick(sg[nt], S.n[0], S.n[1], S.n[2]);
-        jok[nt] = n0 < S.ntotal && jrow[nt] < segn;
+        jok[nt] = n0 < S.ntotal && jrow[nt] < segn && (uint32_t)r16 >= rlo && (uint32_t)r16 < rhi;
         rw[nt] = make_rsrc(pick(sg[nt], S.w[0], S.w[1], S.w[2]), segn * K);
         woff[nt] = jok[nt] ? jrow[nt] * K + g * 16 : kOffNone;
     }
@@ -412,7 +446,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
 #pragma unroll
         for (int w = 1; w < W; ++w) v += red[w][nt][lane];
         if (jok[nt]) {
-            const uint32_t j = (blockIdx.x * NT + nt) * 16u + r16;
+            const uint32_t j = n0s[nt] + r16;
             const float sw = KIND == 0 ? S.s[sg[nt]][jrow[nt]] : 1.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -441,24 +475,26 @@ bool fused_ok(w8a8_scale_t kind, uint32_t rows, uint32_t k, uint32_t ldx) {
            ((uint64_t)(rows - 1) * ldx + k) * 2 < 0x80000000ull;
 }
 
-template <int NT, int W, int U, int KIND, bool SILU, bool UP>
+template <int NT, int R, int W, int U, bool BAL, int KIND, bool SILU, bool UP>
 void fused_launch3(const uint16_t *x, const uint16_t *up, uint32_t ldx, uint32_t rows, uint32_t k, const Segs &S,
                    uint16_t *out, uint32_t ldc, uint8_t *q, float *a_scales, hipStream_t s) {
     static_assert(W * U == (int)kFusedMaxBlocksRow, "per-row scales: one chunk per wave");
-    const unsigned grid = ((S.ntotal + 15) / 16 + NT - 1) / NT;
-    w8a8_fused<NT, 4 * NT, W, U, KIND, SILU, UP><<<grid, W * kWave, 0, s>>>(x, up, ldx, rows, k, S, out, ldc, q,
-                                                                            a_scales);
+    w8a8_fused<NT, R, W, U, KIND, SILU, UP, BAL><<<col_grid<NT, BAL>(S.ntotal), W * kWave, 0, s>>>(
+        x, up, ldx, rows, k, S, out, ldc, q, a_scales);
 }
 
-template <int NT, int W, int U>
+template <int NT, int R, int W, int U, bool BAL>
 void fused_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t *up, uint32_t ldx, uint32_t rows,
                   uint32_t k, const Segs &S, uint16_t *out, uint32_t ldc, uint8_t *q, float *a_scales,
                   hipStream_t s) {
-#define KVQ_FUSED(KIND)                                                                                               \
-    do {                                                                                                              \
-        if (!silu) fused_launch3<NT, W, U, KIND, false, false>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);    \
-        else if (!up) fused_launch3<NT, W, U, KIND, true, false>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);  \
-        else fused_launch3<NT, W, U, KIND, true, true>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);            \
+#define KVQ_FUSED(KIND)                                                                                        \
+    do {                                                                                                       \
+        if (!silu)                                                                                             \
+            fused_launch3<NT, R, W, U, BAL, KIND, false, false>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s); \
+        else if (!up)                                                                                          \
+            fused_launch3<NT, R, W, U, BAL, KIND, true, false>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);  \
+        else                                                                                                   \
+            fused_launch3<NT, R, W, U, BAL, KIND, true, true>(x, up, ldx, rows, k, S, out, ldc, q, a_scales, s);   \
     } while (0)
     if (kind == W8A8_ROWSCALE) KVQ_FUSED(0);
     else KVQ_FUSED(1);
@@ -887,10 +923,10 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
         // {MT, NT, W, U}: up to 8 rows as the fused projection (see there); up
         // to 16 rows two column tiles per activation fragment (half the
         // activation re-reads), 4 K slices; 32 rows use 8 K slices
-        if (rows <= 4) skinny_launch<1, 1, 4, 8>(kind, q, a_scales, rows, k, S, out, ldc, s);
-        else if (rows <= 8) skinny_launch<1, 2, 8, 4>(kind, q, a_scales, rows, k, S, out, ldc, s);
-        else if (rows <= 16) skinny_launch<1, 2, 4, 8>(kind, q, a_scales, rows, k, S, out, ldc, s);
-        else skinny_launch<2, 2, 8, 2>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        if (rows <= 4) skinny_launch<1, 2, 4, 8, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        else if (rows <= 8) skinny_launch<1, 2, 8, 4, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        else if (rows <= 16) skinny_launch<1, 2, 4, 8, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        else skinny_launch<2, 2, 8, 2, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
         return launch_status("w8a8_gemv");
     }
     WidePlan pl = wide_plan(rows, k, S.ntotal);
@@ -976,8 +1012,10 @@ extern "C" int w8a8_proj(w8a8_scale_t kind, int silu, const uint16_t *x, const u
     if (st) return st;
     if (fused_ok(kind, rows, k, ldx)) {
         // one launch: the GEMV quantizes the activations itself (and fills q, a_scales)
-        if (rows <= 4) fused_launch<1, 4, 8>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
-        else fused_launch<2, 8, 4>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
+        if (rows <= 4)
+            fused_launch<2, 4, 4, 8, true>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
+        else
+            fused_launch<2, 8, 8, 4, true>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
         return launch_status("w8a8_proj");
     }
     st = act_quant_launch(kind, silu, x, up, ldx, rows, k, q, a_scales, as_stream(stream));
