@@ -13,8 +13,9 @@
  *     on the host before any HIP call; on error nothing is launched and
  *     kvq_last_error() describes the first violated condition.  No exception
  *     crosses this boundary.
- *   - Outputs are written in full (no read-modify-write of caller memory),
- *     except where a call documents a workspace that it leaves zero-filled.
+ *   - Outputs are written in full (no read-modify-write of caller memory).
+ *     Workspaces are scratch memory: the calls that use one leave its
+ *     counter area (below) at zero and put partial results behind it.
  *
  * Sources (web pages; each declaration names the section it implements):
  *   [KVQ]  boostr, src/ops/wgpu/shaders/cache/kv_cache_quant.wgsl
@@ -256,11 +257,14 @@ typedef struct {
 
 /* Q, K and V in one launch (the page dispatches three kernels).  k_proj and
  * v_proj are both NULL (a single projection) or both set with equal n.
- * x: fp32 [m][k], m >= 1, k % group_size == 0, group_size % 32 == 0.
- * Activations are rounded to fp16 (round to nearest even) for the matrix
- * cores; codes are exact; accumulation is fp32; |x| must stay below 65504.
+ * x: fp32 [m][k], m >= 1, k % group_size == 0.
+ * group_size is 32, 64, 128 or 256.  Activations are rounded to fp16 (round
+ * to nearest even) for the matrix cores; codes are exact; accumulation is
+ * fp32; |x| must stay below 65504.
  * workspace: NULL, or at least int4_awq_workspace_bytes(), zero-filled before
- * its first use and left zero-filled; concurrent calls must not share it. */
+ * its first use; the call leaves its counter area at zero and writes partial
+ * tiles behind it.  Without it, one workgroup per tile (less parallelism).
+ * Concurrent calls must not share a workspace. */
 int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k,
                       uint32_t group_size, const int4_awq_proj_t *q_proj,
                       const int4_awq_proj_t *k_proj,

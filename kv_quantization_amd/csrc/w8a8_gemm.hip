@@ -14,7 +14,7 @@
 //     one instruction is one 128-wide scale block) and the activation rows
 //     as the other operand; partial sums meet in LDS.
 //   * rows > 32   "wide": all rows x 128 columns per workgroup over a slice
-//     of K, both tiles staged through a 3-stage LDS ring with direct
+//     of K, both tiles staged through a double-buffered LDS ring with direct
 //     global->LDS loads; split-K partials are added by a second kernel.
 //
 // Operand layout: for a 16x16x128 fp8 MFMA, lane l supplies row (l % 16) of
@@ -510,7 +510,7 @@ void fused_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t
 // wave's scaling arithmetic overlaps the other's matrix instructions.  Each
 // 128-wide K step of both tiles (and the activation block scales) travels
 // global -> LDS with direct DMA loads (lane i's 16 bytes land at LDS base +
-// 16*i) through a 3-stage ring, two K steps in flight while the third is
+// 16*i) through a two-stage ring: one K step in flight while the other is
 // multiplied.  Rows are stored with their eight 16-byte chunks XOR-swizzled
 // by (row & 7), which keeps both the load pattern and the MFMA operand reads
 // (ds_read_b128) free of bank conflicts.  The loads are buffer loads from
