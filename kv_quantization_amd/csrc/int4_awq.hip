@@ -45,7 +45,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBlock = 256;
+constexpr int kWaves = 4;            // waves per workgroup (K slices of one tile)
 constexpr int kTargetWaves = 2048;
 constexpr uint32_t kXcds = 8;           // XCDs of an MI355X (workgroups are dealt to them in turn)
 
@@ -126,13 +126,15 @@ __device__ __forceinline__ f16x8 act_f16x8(const u32x4 &lo, const u32x4 &hi) {
 // lane that can hold real outputs (1 when m == 1, else 4).  KSG: 32-wide K
 // steps per quantization group.  U: K steps loaded together (a "piece"; U
 // divides KSG).  PF: prefetch the next piece while computing this one.
-template <int MT, int R, int KSG, int U, bool PF, int XT>
-__global__ __launch_bounds__(kBlock) void awq_gemm(const void *__restrict__ x, uint32_t M, uint32_t K, Projs P,
+// WV: waves per workgroup, each a K slice of the tile, summed in LDS.
+template <int MT, int R, int KSG, int U, bool PF, int XT, int WV>
+__global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ x, uint32_t M, uint32_t K, Projs P,
                                                    uint32_t nchunks, uint32_t ks_b, uint32_t *__restrict__ counters,
                                                    float *__restrict__ partials) {
     constexpr int MR = 16 * MT;
     constexpr uint32_t GS = 32 * KSG;
-    __shared__ f32x4 red[4][16][32];
+    constexpr int NTH = WV * kWave;
+    __shared__ f32x4 red[WV][16][32];
     __shared__ int s_last;
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const void *__restrict__ x, u
 
     // K slice of this wave, in pieces of U steps
     const uint32_t npieces = K / (32 * U);
-    const uint32_t nsplit = ks_b * 4, split = bs * 4 + wv;
+    const uint32_t nsplit = ks_b * WV, split = bs * WV + wv;
     const uint32_t pc0 = (uint32_t)((uint64_t)split * npieces / nsplit);
     const uint32_t pc1 = (uint32_t)((uint64_t)(split + 1) * npieces / nsplit);
 
@@ -298,12 +300,14 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const void *__restrict__ x, u
             red[wv][row][2 * wc + 1] = f32x4{acc[mt][4][i], acc[mt][5][i], acc[mt][6][i], acc[mt][7][i]};
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < 16 * 32; e += kBlock) {
+        for (int e = threadIdx.x; e < 16 * 32; e += NTH) {
             const int row = e >> 5, col4 = e & 31;
             const uint32_t m = c * MR + mt * 16 + row;
             const uint32_t lwo = tp * 16 + (col4 >> 1);
             if (m >= M || lwo >= wp) continue;
-            const f32x4 v = red[0][row][col4] + red[1][row][col4] + red[2][row][col4] + red[3][row][col4];
+            f32x4 v = red[0][row][col4];
+#pragma unroll
+            for (int w = 1; w < WV; ++w) v += red[w][row][col4];
             if (ks_b == 1) {
                 *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + 8 * lwo + (col4 & 1) * 4) = v;
             } else {
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const void *__restrict__ x, u
     }
     __syncthreads();
     if (!s_last) return;
-    for (int e = threadIdx.x; e < MR * 32; e += kBlock) {
+    for (int e = threadIdx.x; e < MR * 32; e += NTH) {
         const int row = e >> 5, col4 = e & 31;
         const uint32_t m = c * MR + row;
         const uint32_t lwo = tp * 16 + (col4 >> 1);
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void awq_gemm(const void *__restrict__ x, u
 // ------------------------------------------------------------------ host --
 
 struct Plan {
-    uint32_t mt, mr, nchunks, ks_b, u;
+    uint32_t mt, mr, nchunks, ks_b, u, wv;
     size_t counter_bytes, partial_bytes;
 };
 
@@ -371,6 +375,10 @@ Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles) {
     pl.mr = 16 * pl.mt;
     pl.nchunks = (m + pl.mr - 1) / pl.mr;
     pl.u = piece_steps(pl.mt, gs / 32);
+    // two 16-row tiles per wave (M > 16): 8 waves split K inside the
+    // workgroup (LDS), which leaves fewer or no slices to exchange between
+    // workgroups (M=128: 28 -> 24 us); one tile: 4 waves measured faster
+    pl.wv = pl.mt == 2 ? 8 : kWaves;
     const uint32_t npieces = k / (32 * pl.u);
     const uint64_t units = (uint64_t)ntiles * pl.nchunks;
     // 2 <= m <= 16 streams the same weights as m = 1 with four times the
@@ -382,7 +390,7 @@ Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles) {
     // slices and holds only that part of the activations (measured at M=16:
     // ks_b 5 -> 4 halves the fetched bytes, 12.1 -> 11.3 us)
     pl.ks_b = 1;
-    while (pl.ks_b * 2 <= waves / 4) pl.ks_b *= 2;
+    while (pl.ks_b * 2 <= waves / pl.wv) pl.ks_b *= 2;
     const size_t tiles = (size_t)ntiles * pl.nchunks;
     if (tiles * 4 > KVQ_WORKSPACE_COUNTER_BYTES) pl.ks_b = 1;   // more tiles than counters: no exchange
     pl.counter_bytes = pl.ks_b > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;
@@ -480,17 +488,22 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
     hipStream_t s = as_stream(stream);
     const uint32_t ksg = group_size / 32;
-#define KVQ_AWQ(MT, R, KSG, U, PF)                                                                               \
-    do {                                                                                                         \
-        if (xt == KVQ_DT_F32)                                                                                    \
-            awq_gemm<MT, R, KSG, U, PF, 0><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b,  \
-                                                                               counters, partials);              \
-        else if (xt == KVQ_DT_F16)                                                                               \
-            awq_gemm<MT, R, KSG, U, PF, 1><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b,  \
-                                                                               counters, partials);              \
-        else                                                                                                     \
-            awq_gemm<MT, R, KSG, U, PF, 2><<<(unsigned)blocks, kBlock, 0, s>>>(x, m, k, P, pl.nchunks, pl.ks_b,  \
-                                                                               counters, partials);              \
+#define KVQ_AWQ3(MT, R, KSG, U, PF, WV)                                                                        \
+    do {                                                                                                       \
+        if (xt == KVQ_DT_F32)                                                                                  \
+            awq_gemm<MT, R, KSG, U, PF, 0, WV><<<(unsigned)blocks, WV * kWave, 0, s>>>(x, m, k, P, pl.nchunks, \
+                                                                                  pl.ks_b, counters, partials); \
+        else if (xt == KVQ_DT_F16)                                                                             \
+            awq_gemm<MT, R, KSG, U, PF, 1, WV><<<(unsigned)blocks, WV * kWave, 0, s>>>(x, m, k, P, pl.nchunks, \
+                                                                                  pl.ks_b, counters, partials); \
+        else                                                                                                   \
+            awq_gemm<MT, R, KSG, U, PF, 2, WV><<<(unsigned)blocks, WV * kWave, 0, s>>>(x, m, k, P, pl.nchunks, \
+                                                                                  pl.ks_b, counters, partials); \
+    } while (0)
+#define KVQ_AWQ(MT, R, KSG, U, PF)                                 \
+    do {                                                           \
+        if (pl.wv == 8) KVQ_AWQ3(MT, R, KSG, U, PF, 8);            \
+        else KVQ_AWQ3(MT, R, KSG, U, PF, kWaves);                  \
     } while (0)
 #define KVQ_AWQ_K(MT, R, CAP, PF)                                   \
     switch (ksg) {                                                  \
@@ -507,6 +520,7 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
     }
 #undef KVQ_AWQ_K
 #undef KVQ_AWQ
+#undef KVQ_AWQ3
     return launch_status(fn);
 }
 
