@@ -365,7 +365,7 @@ struct Plan {
 };
 
 uint32_t piece_steps(uint32_t mt, uint32_t ksg) {
-    const uint32_t cap = mt == 1 ? 4 : 2;
+    const uint32_t cap = mt == 1 ? 4 : 1;   // two 16-row tiles: one K step per piece, prefetched
     return ksg < cap ? ksg : cap;
 }
 
@@ -516,7 +516,7 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
         if (m == 1) KVQ_AWQ_K(1, 1, 4, true)
         else KVQ_AWQ_K(1, 4, 4, true)
     } else {
-        KVQ_AWQ_K(2, 4, 2, false)
+        KVQ_AWQ_K(2, 4, 1, true)
     }
 #undef KVQ_AWQ_K
 #undef KVQ_AWQ
