@@ -922,11 +922,11 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
     if (rows <= 32) {
         // {MT, NT, W, U}: up to 8 rows as the fused projection (see there); up
         // to 16 rows two column tiles per activation fragment (half the
-        // activation re-reads), 4 K slices; 32 rows use 8 K slices
+        // activation re-reads), 4 K slices; 32 rows 8 K slices of 4 blocks
         if (rows <= 4) skinny_launch<1, 2, 4, 8, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
         else if (rows <= 8) skinny_launch<1, 2, 8, 4, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
         else if (rows <= 16) skinny_launch<1, 2, 4, 8, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
-        else skinny_launch<2, 2, 8, 2, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        else skinny_launch<2, 2, 8, 4, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
         return launch_status("w8a8_gemv");
     }
     WidePlan pl = wide_plan(rows, k, S.ntotal);
