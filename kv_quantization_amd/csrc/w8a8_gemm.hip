@@ -462,9 +462,9 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
 
 // Shapes {NT, W, U} shared by the skinny GEMV and the fused projection for
 // the same row counts (same K split, so both forms give the same bits): up
-// to 4 rows one column tile, 4 K slices, 8 K blocks in flight; 5..8 rows two
-// column tiles (each activation fragment serves both) over 8 K slices of 4
-// blocks, which halves each wave's share of the activation encoding.
+// to 8 rows, two column tiles per workgroup in the balanced pairing, 8 K
+// slices of 4 blocks (more waves to hide the loads, and half of each wave's
+// share of the activation encoding compared with 4 slices of 8).
 // W * U is kFusedMaxBlocksRow: with per-row scales K may have that many
 // 128-blocks (one chunk per wave).
 constexpr uint32_t kFusedMaxBlocksRow = 32;
@@ -923,7 +923,7 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
         // {MT, NT, W, U}: up to 8 rows as the fused projection (see there); up
         // to 16 rows two column tiles per activation fragment (half the
         // activation re-reads), 4 K slices; 32 rows 8 K slices of 4 blocks
-        if (rows <= 4) skinny_launch<1, 2, 4, 8, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
+        if (rows <= 4) skinny_launch<1, 2, 8, 4, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
         else if (rows <= 8) skinny_launch<1, 2, 8, 4, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
         else if (rows <= 16) skinny_launch<1, 2, 4, 8, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
         else skinny_launch<2, 2, 8, 4, true>(kind, q, a_scales, rows, k, S, out, ldc, s);
@@ -1013,7 +1013,7 @@ extern "C" int w8a8_proj(w8a8_scale_t kind, int silu, const uint16_t *x, const u
     if (fused_ok(kind, rows, k, ldx)) {
         // one launch: the GEMV quantizes the activations itself (and fills q, a_scales)
         if (rows <= 4)
-            fused_launch<2, 4, 4, 8, true>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
+            fused_launch<2, 4, 8, 4, true>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
         else
             fused_launch<2, 8, 8, 4, true>(kind, silu, x, up, ldx, rows, k, S, out, ldc, q, a_scales, as_stream(stream));
         return launch_status("w8a8_proj");
