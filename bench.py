@@ -80,6 +80,7 @@ def kernel_table():
 
 
 AWQ_EXTRA_MS = (4, 8)
+AWQ_F16X_MS = (1, 16, 128)   # INT4 AWQ with fp16 activations, beside the step
 
 
 def awq_bytes(m, xbytes=4):
@@ -101,7 +102,7 @@ def extra_table():
             ("kv_int4_quant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm"),
             ("kv_int4_dequant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm")]
     rows += [(f"int4_awq_qkv_M{m}", awq_bytes(m), 2 * m * na * AWQ_K, "fp16") for m in AWQ_EXTRA_MS]
-    rows += [(f"int4_awq_qkv_f16x_M{m}", awq_bytes(m, 2), 2 * m * na * AWQ_K, "fp16") for m in (1, 16)]
+    rows += [(f"int4_awq_qkv_f16x_M{m}", awq_bytes(m, 2), 2 * m * na * AWQ_K, "fp16") for m in AWQ_F16X_MS]
     return rows
 
 
@@ -173,7 +174,7 @@ class StepBuffers:
         self.kv16_z4 = e((g,), torch.float32)
         self.kv16_y4 = e((KV_T, KV_D), torch.bfloat16)
         self.awqx_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_EXTRA_MS + (1, 16)}
-        self.awq16_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in (1, 16)}
+        self.awq16_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_F16X_MS}
         self.qkv_weight = api.W8a8Weight(api.ROWSCALE, s["qkv_w"])
         self.down_weight = api.W8a8Weight(api.BLK128, s["down_w"])
         self.qkv_q = {m: e((m, QKV_K), torch.uint8) for m in QKV_MS}
@@ -206,7 +207,7 @@ class StepBuffers:
         for m in AWQ_EXTRA_MS:
             L.append((f"int4_awq_qkv_M{m}", lambda m=m: api.int4_awq_qkv(s["awq_x"][:m], s["awq_p"], AWQ_GS,
                                                                           outs=self.awqx_out[m])))
-        for m in (1, 16):
+        for m in AWQ_F16X_MS:
             L.append((f"int4_awq_qkv_f16x_M{m}", lambda m=m: api.int4_awq_qkv(s["awq_x16"][:m], s["awq_p"], AWQ_GS,
                                                                                outs=self.awq16_out[m])))
         return L
