@@ -49,7 +49,8 @@ int kvq_abi_version(void);
 /* Workspaces (w8a8_gemv, w8a8_proj, int4_awq_qkv_gemm): the first
  * KVQ_WORKSPACE_COUNTER_BYTES bytes hold the counters through which the
  * workgroups of one output tile find the last of them; every call leaves
- * them at zero, and partial sums only ever go behind them.  One zero-filled
+ * them at zero, and partial sums (and the INT4 call's fp16 activation copy)
+ * only ever go behind them, also when a call uses no counters.  One zero-filled
  * buffer can therefore serve calls of all three kinds, in any order, as long
  * as they are ordered on one stream. */
 #define KVQ_WORKSPACE_COUNTER_BYTES 4096u
@@ -263,7 +264,10 @@ typedef struct {
  * fp32; |x| must stay below 65504.
  * workspace: NULL, or at least int4_awq_workspace_bytes(), zero-filled before
  * its first use; the call leaves its counter area at zero and writes partial
- * tiles behind it.  Without it, one workgroup per tile (less parallelism).
+ * tiles behind it, and for m > 16 the fp16-rounded activations behind those
+ * (one extra launch converts them; every column tile then reads half the
+ * bytes).  Without it, one workgroup per tile (less parallelism) and the
+ * rounding happens inside the product kernel: the same fp16 operands.
  * Concurrent calls must not share a workspace. */
 int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k,
                       uint32_t group_size, const int4_awq_proj_t *q_proj,

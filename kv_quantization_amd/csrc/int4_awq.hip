@@ -122,6 +122,17 @@ __device__ __forceinline__ f16x8 act_f16x8(const u32x4 &lo, const u32x4 &hi) {
     return h;
 }
 
+// fp32 activations -> fp16 with the rounding act_f16x8<0> applies (round to
+// nearest even), 8 values per thread.  Above 16 rows every column tile
+// re-reads its rows of the activations from L2 over the whole of K, so
+// reading them at half the width pays for this extra pass (M=128: 23.6 ->
+// 18.9 us in the product kernel).
+__global__ __launch_bounds__(256) void x_to_f16(const f32x4 *__restrict__ x, uint32_t n8, f16x8 *__restrict__ y) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    y[i] = to_f16x8(x[2 * i], x[2 * i + 1]);
+}
+
 // MT: 16-row activation tiles per chunk (1 or 2).  R: accumulator rows per
 // lane that can hold real outputs (1 when m == 1, else 4).  KSG: 32-wide K
 // steps per quantization group.  U: K steps loaded together (a "piece"; U
@@ -362,6 +373,9 @@ __global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ 
 struct Plan {
     uint32_t mt, mr, nchunks, ks_b, u, wv;
     size_t counter_bytes, partial_bytes;
+    size_t x16_bytes;   // fp16 copy of fp32 activations (two 16-row tiles per wave)
+    size_t x16_offset;  // behind the counter area (kept zero for every call) and the partials
+    size_t ws_bytes;    // workspace this plan uses in full
 };
 
 uint32_t piece_steps(uint32_t mt, uint32_t ksg) {
@@ -395,6 +409,9 @@ Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles) {
     if (tiles * 4 > KVQ_WORKSPACE_COUNTER_BYTES) pl.ks_b = 1;   // more tiles than counters: no exchange
     pl.counter_bytes = pl.ks_b > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;
     pl.partial_bytes = pl.ks_b > 1 ? tiles * pl.ks_b * pl.mr * 128 * 4 : 0;
+    pl.x16_bytes = pl.mt == 2 ? ((size_t)m * k * 2 + 255) / 256 * 256 : 0;
+    pl.x16_offset = KVQ_WORKSPACE_COUNTER_BYTES + pl.partial_bytes;
+    pl.ws_bytes = pl.x16_bytes ? pl.x16_offset + pl.x16_bytes : pl.counter_bytes + pl.partial_bytes;
     return pl;
 }
 
@@ -425,8 +442,7 @@ extern "C" int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_s
     // splitting n_total into up to three projections adds at most two tiles
     for (uint32_t extra = 0; extra <= 2; ++extra) {
         const Plan pl = make_plan(m, k, group_size, tiles_of(n_total) + extra);
-        const size_t b = pl.counter_bytes + pl.partial_bytes;
-        if (b > *bytes) *bytes = b;
+        if (pl.ws_bytes > *bytes) *bytes = pl.ws_bytes;
     }
     return KVQ_OK;
 }
@@ -487,6 +503,15 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
     const uint64_t blocks = tile_slots * pl.nchunks * pl.ks_b;
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
     hipStream_t s = as_stream(stream);
+    // fp32 activations with two 16-row tiles per wave: convert once to fp16
+    // behind the partials when the workspace holds it, then read that copy
+    if (xt == KVQ_DT_F32 && pl.x16_bytes && workspace && aligned16(workspace) && workspace_bytes >= pl.ws_bytes) {
+        void *x16 = static_cast<uint8_t *>(workspace) + pl.x16_offset;
+        const uint32_t n8 = (uint32_t)((uint64_t)m * k / 8);
+        x_to_f16<<<(n8 + 255) / 256, 256, 0, s>>>(static_cast<const f32x4 *>(x), n8, static_cast<f16x8 *>(x16));
+        x = x16;
+        xt = KVQ_DT_F16;
+    }
     const uint32_t ksg = group_size / 32;
 #define KVQ_AWQ3(MT, R, KSG, U, PF, WV)                                                                        \
     do {                                                                                                       \

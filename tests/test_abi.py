@@ -149,6 +149,17 @@ def test_workspace_sizes(lib):
     assert b.value > 0          # small M slices K across workgroups
     assert lib.int4_awq_workspace_bytes(1, 512, 128, 512, ctypes.byref(b)) == 0
     assert b.value == 0         # tiny problem: one workgroup per tile
+    # above 16 rows it also holds an fp16 copy of fp32 activations (rounded
+    # to 256 bytes), always behind the counter area, which other calls on the
+    # same workspace expect at zero; at 128 rows x 6144 columns K is not
+    # split: counter area and copy only
+    counters = 4096
+    assert lib.int4_awq_workspace_bytes(128, 4096, 128, 6144, ctypes.byref(b)) == 0
+    assert b.value == counters + 128 * 4096 * 2
+    assert lib.int4_awq_workspace_bytes(17, 96, 32, 8, ctypes.byref(b)) == 0
+    assert b.value == counters + (17 * 96 * 2 + 255) // 256 * 256   # one tile, 3 K steps: no split either
+    assert lib.int4_awq_workspace_bytes(16, 96, 32, 8, ctypes.byref(b)) == 0
+    assert b.value == 0
     assert lib.w8a8_gemv_workspace_bytes(0, 8, 4096, 6144, ctypes.byref(b)) == 0
 
 
