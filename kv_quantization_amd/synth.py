@@ -46,6 +46,20 @@ def kv_cache(num_tokens: int = 32768, head_dim: int = 128, seed: int = 2,
     return x
 
 
+def attn_decode(num_tokens: int = 4096, num_kv_heads: int = 8, num_q_heads: int = 32, head_dim: int = 128,
+                seed: int = 11):
+    """One decode token's queries and the cache it reads: (q fp32 [Hq, D],
+    k fp32 [T, Hkv, D], v fp32 [T, Hkv, D]); K and V rows have the KV cache's
+    value distribution (4096 tokens x 8 heads = the 32768 x 128 cache), q is
+    N(0, 1)."""
+    g = rng(seed)
+    q = g.normal(0.0, 1.0, (num_q_heads, head_dim)).astype(np.float32)
+    rows = num_tokens * num_kv_heads
+    k = kv_cache(rows, head_dim, seed=seed + 1).reshape(num_tokens, num_kv_heads, head_dim)
+    v = kv_cache(rows, head_dim, seed=seed + 2).reshape(num_tokens, num_kv_heads, head_dim)
+    return q, k, v
+
+
 # --------------------------------------------------------------------------
 # W8A8: bf16 activations N(0,1); fp32 weights N(0, 0.02) to be quantized.
 

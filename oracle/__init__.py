@@ -17,6 +17,13 @@ The two matrix products are plain definitions, written here as fp64 sums with
   ``out[m, j] = sum_k x[m,k] * (q[k,j] - z[k/gs, j]) * s[k/gs, j]`` with q
   unpacked in the ``QKV_AWQ_SHIFTS`` nibble order.
 
+* Decode attention over the quantized cache (a reading: the pages define
+  the cache and its dequantization, not the attention that reads it):
+  textbook scaled-dot-product attention for one new token, ``out_h =
+  sum_t softmax_t(scale * q_h . k_t) v_t`` over the dequantized keys and
+  values, query head h reading KV head ``h // (Hq // Hkv)``; the bound is
+  ``sum_t p_t |v_t|``.
+
 Every function returns, next to the reference value, the bound
 ``sum_k |a_k| |w_k|`` of the operands actually multiplied, which the parity
 tests scale by the 1e-3 relative tolerance.
@@ -439,3 +446,58 @@ def int4_awq_gemm(x: np.ndarray, qweight, scales, zeros, group_size: int):
 def int4_awq_qkv(x, projections, group_size: int):
     """Q, K, V (or a single projection): list of (ref, bound) per projection."""
     return [int4_awq_gemm(x, qw, s, z, group_size) for (qw, s, z) in projections]
+
+
+# --------------------------------------------------------------------------
+# Decode attention over the quantized cache.  The pages define the cache and
+# its dequantization but not the attention that reads it; the reading taken
+# is textbook scaled-dot-product attention for one new token per query head,
+# with consecutive query heads sharing a KV head (grouped queries).
+
+def attn_decode(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, softmax_scale: float):
+    """q float32 [Hq, D]; k_hat, v_hat float32 [T, Hkv, D], the cache as the
+    pages' dequantization gives it; Hq a multiple of Hkv, and query head h
+    reads KV head h // (Hq // Hkv).  In fp64: s_t = softmax_scale * (q_h .
+    k_t); p = softmax(s), computed as exp(s - max s) / sum; out_h = sum_t
+    p_t v_t.  Returns (out fp64 [Hq, D], bound fp64 [Hq, D] = sum_t p_t |v_t|),
+    the bound of the weighted sum the parity tests scale by 1e-3."""
+    q64 = _c(q, np.float32).astype(np.float64)
+    k64 = _c(k_hat, np.float32).astype(np.float64)
+    v64 = _c(v_hat, np.float32).astype(np.float64)
+    hq, d = q64.shape
+    t, hkv, dk = k64.shape
+    if dk != d or v64.shape != k64.shape or t < 1 or hkv < 1 or hq % hkv:
+        raise ValueError("attn_decode: shapes do not match")
+    sc = float(np.float32(softmax_scale))      # the fp32 value a caller passes
+    grp = hq // hkv
+    out = np.empty((hq, d))
+    bound = np.empty((hq, d))
+    for h in range(hq):
+        g = h // grp
+        s = sc * np.matmul(k64[:, g, :], q64[h])
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        out[h] = np.matmul(p, v64[:, g, :])
+        bound[h] = np.matmul(p, np.abs(v64[:, g, :]))
+    return out, bound
+
+
+def attn_decode_int8(q, k_codes, k_scales, v_codes, v_scales, softmax_scale: float):
+    """Keys and values as per-token INT8: codes int8 [T, Hkv, D], one scale
+    per (token, head) row, float32 [T, Hkv], dequantized by the INT8 section."""
+    t, hkv, d = np.shape(k_codes)
+    kh = kv_int8_dequant(np.reshape(k_codes, (t * hkv, d)), np.reshape(k_scales, t * hkv)).reshape(t, hkv, d)
+    vh = kv_int8_dequant(np.reshape(v_codes, (t * hkv, d)), np.reshape(v_scales, t * hkv)).reshape(t, hkv, d)
+    return attn_decode(q, kh, vh, softmax_scale)
+
+
+def attn_decode_int4(q, k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros, num_tokens: int,
+                     num_kv_heads: int, head_dim: int, group_size: int, softmax_scale: float):
+    """Keys and values as per-group INT4 over the flattened [T, Hkv, D] cache
+    (group_size divides D, so no group spans two rows), dequantized by the
+    INT4 section."""
+    rows = num_tokens * num_kv_heads
+    kh = kv_int4_dequant(k_packed, k_scales, k_zeros, rows, head_dim, group_size)
+    vh = kv_int4_dequant(v_packed, v_scales, v_zeros, rows, head_dim, group_size)
+    shp = (num_tokens, num_kv_heads, head_dim)
+    return attn_decode(q, kh.reshape(shp), vh.reshape(shp), softmax_scale)

@@ -1,0 +1,114 @@
+"""Pins for the oracle's decode attention over the quantized KV cache.
+
+The pages define the cache and its dequantization, not the attention that
+reads it; the reading is textbook scaled-dot-product attention for one new
+token, query head h reading KV head h // (Hq // Hkv).  The pins tie it to
+things other than itself: a hand-worked example, closed forms (one token,
+equal keys, one dominant key), the head grouping, and torch's own
+scaled_dot_product_attention on the same dequantized values."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_quantization_amd import synth
+
+
+@pytest.fixture(scope="module")
+def orc(oracle_mod):
+    return oracle_mod
+
+
+def test_worked_example(orc):
+    # scores 0 and ln 3 -> p = (1/4, 3/4); out = 1/4 * (4, 0) + 3/4 * (0, 8) = (1, 6)
+    q = np.array([[1.0, 0.0]], np.float32)
+    k = np.array([[[0.0, 5.0]], [[math.log(3.0), -2.0]]], np.float32)
+    v = np.array([[[4.0, 0.0]], [[0.0, 8.0]]], np.float32)
+    out, bound = orc.attn_decode(q, k, v, 1.0)
+    np.testing.assert_allclose(out[0], [1.0, 6.0], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(bound[0], [1.0, 6.0], rtol=0, atol=1e-6)
+
+
+def test_one_token_returns_its_value(orc):
+    q, k, v = synth.attn_decode(1, 2, 6, 64, seed=21)
+    out, _ = orc.attn_decode(q, k, v, 0.125)
+    for h in range(6):
+        np.testing.assert_array_equal(out[h], v[0, h // 3].astype(np.float64))
+
+
+def test_equal_keys_give_the_mean_value(orc):
+    q, k, v = synth.attn_decode(37, 1, 2, 32, seed=22)
+    k[:] = k[0]
+    out, _ = orc.attn_decode(q, k, v, 0.3)
+    np.testing.assert_allclose(out, np.broadcast_to(v[:, 0, :].astype(np.float64).mean(0), out.shape),
+                               rtol=0, atol=1e-12)
+
+
+def test_dominant_key_selects_its_value(orc):
+    q, k, v = synth.attn_decode(50, 1, 1, 16, seed=23)
+    k *= np.float32(0.01)
+    k[17, 0] = q[0] * np.float32(4.0)            # score 4 |q|^2 * scale, far above the rest
+    out, _ = orc.attn_decode(q, k, v, 1.0)
+    s = np.matmul(k[:, 0, :].astype(np.float64), q[0].astype(np.float64))
+    gap = s[17] - np.max(np.delete(s, 17))
+    assert gap > 30
+    np.testing.assert_allclose(out[0], v[17, 0], rtol=0, atol=50 * math.exp(-gap) * np.abs(v).max())
+
+
+def test_head_grouping(orc):
+    # Hq = 6 over Hkv = 3: heads 2h, 2h+1 read KV head h alone
+    q, k, v = synth.attn_decode(40, 3, 6, 32, seed=24)
+    out, _ = orc.attn_decode(q, k, v, 0.2)
+    for h in range(6):
+        g = h // 2
+        one, _ = orc.attn_decode(q[h:h + 1], k[:, g:g + 1], v[:, g:g + 1], 0.2)
+        np.testing.assert_array_equal(out[h], one[0])
+
+
+@pytest.mark.parametrize("t,hkv,hq,d", [(1, 1, 1, 8), (5, 2, 8, 64), (300, 4, 4, 128), (1000, 8, 32, 128)])
+def test_matches_torch_sdpa(orc, t, hkv, hq, d):
+    q, k, v = synth.attn_decode(t, hkv, hq, d, seed=25 + t)
+    scale = 1.0 / math.sqrt(d)
+    out, bound = orc.attn_decode(q, k, v, scale)
+    grp = hq // hkv
+    kt = torch.from_numpy(k).double().permute(1, 0, 2).repeat_interleave(grp, 0)[None]   # [1, Hq, T, D]
+    vt = torch.from_numpy(v).double().permute(1, 0, 2).repeat_interleave(grp, 0)[None]
+    qt = torch.from_numpy(q).double()[None, :, None, :]                                     # [1, Hq, 1, D]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=float(np.float32(scale)))
+    np.testing.assert_allclose(out, ref[0, :, 0, :].numpy(), rtol=0, atol=1e-12 * max(1.0, float(bound.max())))
+    assert np.all(np.abs(out) <= bound * (1 + 1e-12))
+
+
+def test_int8_cache_on_exact_codes(orc):
+    # scales of 1 make the dequantized cache the codes themselves
+    t, hkv, hq, d = 64, 2, 4, 32
+    g = np.random.default_rng(26)
+    kc = g.integers(-128, 128, (t, hkv, d), dtype=np.int8)
+    vc = g.integers(-128, 128, (t, hkv, d), dtype=np.int8)
+    q = (g.normal(0, 0.01, (hq, d))).astype(np.float32)
+    ones = np.ones((t, hkv), np.float32)
+    got, _ = orc.attn_decode_int8(q, kc, ones, vc, ones, 0.5)
+    ref, _ = orc.attn_decode(q, kc.astype(np.float32), vc.astype(np.float32), 0.5)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_int8_and_int4_caches_dequantize_by_their_sections(orc):
+    t, hkv, hq, d, gs = 20, 2, 4, 64, 32
+    q, k, v = synth.attn_decode(t, hkv, hq, d, seed=27)
+    kc, ks = orc.kv_int8_quant(k.reshape(t * hkv, d))
+    vc, vs = orc.kv_int8_quant(v.reshape(t * hkv, d))
+    got, _ = orc.attn_decode_int8(q, kc.reshape(t, hkv, d), ks.reshape(t, hkv), vc.reshape(t, hkv, d),
+                                  vs.reshape(t, hkv), 0.1)
+    ref, _ = orc.attn_decode(q, (kc.astype(np.float32) * ks[:, None]).reshape(t, hkv, d),
+                             (vc.astype(np.float32) * vs[:, None]).reshape(t, hkv, d), 0.1)
+    np.testing.assert_array_equal(got, ref)
+    kp, k4s, k4z = orc.kv_int4_quant(k.reshape(t * hkv, d), gs)
+    vp, v4s, v4z = orc.kv_int4_quant(v.reshape(t * hkv, d), gs)
+    got4, _ = orc.attn_decode_int4(q, kp, k4s, k4z, vp, v4s, v4z, t, hkv, d, gs, 0.1)
+    kd = orc.kv_int4_dequant(kp, k4s, k4z, t * hkv, d, gs).reshape(t, hkv, d)
+    vd = orc.kv_int4_dequant(vp, v4s, v4z, t * hkv, d, gs).reshape(t, hkv, d)
+    np.testing.assert_array_equal(got4, orc.attn_decode(q, kd, vd, 0.1)[0])
+    # quantization error of the cache moves the output only a little
+    exact, bound = orc.attn_decode(q, k, v, 0.1)
+    assert np.max(np.abs(got - exact) / bound.max()) < 0.05
