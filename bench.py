@@ -81,6 +81,14 @@ def kernel_table():
 
 AWQ_EXTRA_MS = (4, 8)
 AWQ_F16X_MS = (1, 16, 128)   # INT4 AWQ with fp16 activations, beside the step
+# decode attention over the INT8 cache, beside the step: 4096 tokens x 8 KV
+# heads x 128 (the 32768 x 128 cache), 32 query heads
+ATTN_T, ATTN_HKV, ATTN_HQ, ATTN_D = 4096, 8, 32, 128
+
+
+def attn_bytes():
+    rows = ATTN_T * ATTN_HKV
+    return 2 * rows * ATTN_D + 2 * rows * 4 + 2 * ATTN_HQ * ATTN_D * 4
 
 
 def awq_bytes(m, xbytes=4):
@@ -91,7 +99,8 @@ def awq_bytes(m, xbytes=4):
 def extra_table():
     """Kernels timed beside the step but not part of it (widenings of the
     path: per-tensor KV mode, bf16 KV caches, INT4 at M between the
-    configurations and with fp16 activations): (name, bytes, flops, kind)."""
+    configurations and with fp16 activations, decode attention over the INT8
+    cache): (name, bytes, flops, kind)."""
     kv = KV_T * KV_D * 4 + KV_T * KV_D + 4
     n = KV_T * KV_D
     g = n // KV_GS
@@ -103,6 +112,7 @@ def extra_table():
             ("kv_int4_dequant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm")]
     rows += [(f"int4_awq_qkv_M{m}", awq_bytes(m), 2 * m * na * AWQ_K, "fp16") for m in AWQ_EXTRA_MS]
     rows += [(f"int4_awq_qkv_f16x_M{m}", awq_bytes(m, 2), 2 * m * na * AWQ_K, "fp16") for m in AWQ_F16X_MS]
+    rows += [(f"attn_decode_int8_T{ATTN_T}", attn_bytes(), 0, "hbm")]   # HBM-bound: vector ALU products
     return rows
 
 
@@ -135,6 +145,13 @@ def make_inputs(torch, api, synth):
     s["awq_x16"] = s["awq_x"].to(torch.float16)
     s["kv_x16"] = s["kv_x"].to(torch.bfloat16)
     s["awq_p"] = [(dev(p.qweight.view(np.int32)), dev(p.scales), dev(p.zeros)) for p in projs]
+    aq, ak, av = synth.attn_decode(ATTN_T, ATTN_HKV, ATTN_HQ, ATTN_D, seed=11)
+    s["attn_q"] = dev(aq)
+    rows = ATTN_T * ATTN_HKV
+    for name, a in (("k", ak), ("v", av)):
+        codes, scales = api.quant_int8_token(dev(a.reshape(rows, ATTN_D)))
+        s[f"attn_{name}c"] = codes.view(ATTN_T, ATTN_HKV, ATTN_D)
+        s[f"attn_{name}s"] = scales.view(ATTN_T, ATTN_HKV)
     torch.cuda.synchronize()
     return s, (qkv, down, x5, projs)
 
@@ -175,6 +192,7 @@ class StepBuffers:
         self.kv16_y4 = e((KV_T, KV_D), torch.bfloat16)
         self.awqx_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_EXTRA_MS + (1, 16)}
         self.awq16_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_F16X_MS}
+        self.attn_out = e((ATTN_HQ, ATTN_D), torch.float32)
         self.qkv_weight = api.W8a8Weight(api.ROWSCALE, s["qkv_w"])
         self.down_weight = api.W8a8Weight(api.BLK128, s["down_w"])
         self.qkv_q = {m: e((m, QKV_K), torch.uint8) for m in QKV_MS}
@@ -210,6 +228,9 @@ class StepBuffers:
         for m in AWQ_F16X_MS:
             L.append((f"int4_awq_qkv_f16x_M{m}", lambda m=m: api.int4_awq_qkv(s["awq_x16"][:m], s["awq_p"], AWQ_GS,
                                                                                outs=self.awq16_out[m])))
+        L.append((f"attn_decode_int8_T{ATTN_T}", lambda: api.attn_decode_int8(s["attn_q"], s["attn_kc"], s["attn_ks"],
+                                                                             s["attn_vc"], s["attn_vs"],
+                                                                             out=self.attn_out)))
         return L
 
     # each launcher issues exactly one call

@@ -290,6 +290,43 @@ int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k,
                          size_t workspace_bytes, void *stream);
 
 /* ======================================================================== */
+/* Decode attention over the INT8 per-token cache                           */
+/* The consumer of the [KVQ] "INT8 Per-Token Quantization" cache.  The pages
+ * define the cache and its dequantization (value = code * scale) but no
+ * attention; this is textbook scaled-dot-product attention for one new token
+ * per query head, query head h reading KV head h / (num_q_heads /
+ * num_kv_heads):
+ *   s_t = softmax_scale * (q_h . k_t),  p = softmax(s),  out_h = sum_t p_t v_t
+ * with k_t, v_t the dequantized cache rows.  Arithmetic is fp32: the scales
+ * multiply the integer dot products and the softmax weights; within
+ * 1e-3 * sum_t p_t |v_t| of the exact result for moderate scores.
+ *   q:        fp32 [num_q_heads][head_dim]
+ *   k_codes, v_codes: int8 [num_tokens][num_kv_heads][head_dim] (the
+ *             per-token quantizer's output for num_tokens*num_kv_heads rows)
+ *   k_scales, v_scales: fp32 [num_tokens][num_kv_heads]
+ *   out:      fp32 [num_q_heads][head_dim]
+ * head_dim is 128; num_q_heads is 1..8 times num_kv_heads; num_tokens >= 1.
+ * All pointers are device memory, 16-byte aligned, owned by the caller.
+ * workspace: NULL, or at least kvq_attn_decode_workspace_bytes(), zero-
+ * filled before first use (the shared workspace of the calls above: the
+ * per-head counters sit in its counter area, which the call leaves at zero,
+ * and the per-chunk partial results behind it).  Without it one workgroup
+ * walks each KV head's tokens (less parallelism, same definition).
+ * Concurrent calls must not share a workspace.  Errors: KVQ_E_INVALID for
+ * shapes, null or misaligned pointers, a non-finite softmax_scale. */
+int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads,
+                         uint32_t num_kv_heads, uint32_t num_tokens,
+                         uint32_t head_dim, const int8_t *k_codes,
+                         const float *k_scales, const int8_t *v_codes,
+                         const float *v_scales, float softmax_scale,
+                         float *out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+int kvq_attn_decode_workspace_bytes(uint32_t num_q_heads, uint32_t num_kv_heads,
+                                    uint32_t num_tokens, uint32_t head_dim,
+                                    size_t *bytes);
+
+/* ======================================================================== */
 /* Measurement helper (not part of the method)                              */
 /* kvq_stream_read: reads `bytes` (a positive multiple of 16) at `src` (16-
  * byte aligned device memory) with 16-byte loads across the whole GPU and

@@ -58,6 +58,8 @@ SIGNATURES = {
     "int4_awq_qkv_gemm_dt": [_p, _i, _u32, _u32, _u32, ctypes.POINTER(Int4AwqProj), ctypes.POINTER(Int4AwqProj),
                              ctypes.POINTER(Int4AwqProj), _p, _sz, _p],
     "kvq_stream_read": [_p, _sz, _p, _p],
+    "kvq_attn_decode_int8": [_p, _u32, _u32, _u32, _u32, _p, _p, _p, _p, ctypes.c_float, _p, _p, _sz, _p],
+    "kvq_attn_decode_workspace_bytes": [_u32, _u32, _u32, _u32, _psz],
 }
 
 # include/kvq.h: KVQ_INT8_TENSOR_WORKSPACE_BYTES (counter area + 512 partials)

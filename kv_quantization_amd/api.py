@@ -8,6 +8,7 @@ each function states.
 from __future__ import annotations
 
 import ctypes
+import math
 from dataclasses import dataclass
 
 import torch
@@ -312,6 +313,40 @@ def int4_awq_qkv(x: torch.Tensor, projections, group_size: int, outs=None, use_w
         _lib.call("int4_awq_qkv_gemm_dt", _dev(x, x.dtype, "x"), xdt, m, k, group_size, ctypes.byref(structs[0]),
                   kp, vp, ws_ptr, ws_bytes, stream)
     return res
+
+
+# ---------------------------------------------------- decode attention ----
+
+def attn_decode_workspace_bytes(num_q_heads: int, num_kv_heads: int, num_tokens: int, head_dim: int) -> int:
+    b = ctypes.c_size_t()
+    _lib.call("kvq_attn_decode_workspace_bytes", num_q_heads, num_kv_heads, num_tokens, head_dim, ctypes.byref(b))
+    return b.value
+
+
+def attn_decode_int8(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                     v_scales: torch.Tensor, softmax_scale: float = None, out: torch.Tensor = None,
+                     use_workspace: bool = True) -> torch.Tensor:
+    """q fp32 [Hq, D]; k/v codes int8 [T, Hkv, D]; k/v scales fp32 [T, Hkv]
+    -> out fp32 [Hq, D] (softmax_scale defaults to 1/sqrt(D))."""
+    hq, d = q.shape
+    t, hkv, dk = k_codes.shape
+    if dk != d or tuple(v_codes.shape) != (t, hkv, d):
+        raise ValueError("q, k_codes and v_codes shapes do not match")
+    if tuple(k_scales.shape) != (t, hkv) or tuple(v_scales.shape) != (t, hkv):
+        raise ValueError("scales must be [T, Hkv]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = _empty((hq, d), torch.float32, q) if out is None else out
+    stream = _stream(q)
+    ws_ptr, ws_bytes = 0, 0
+    if use_workspace:
+        ws_bytes = attn_decode_workspace_bytes(hq, hkv, t, d)
+        if ws_bytes:
+            ws_ptr = workspace(q.device, ws_bytes, stream).data_ptr()
+    _lib.call("kvq_attn_decode_int8", _dev(q, torch.float32, "q"), hq, hkv, t, d,
+              _dev(k_codes, torch.int8, "k_codes"), _dev(k_scales, torch.float32, "k_scales"),
+              _dev(v_codes, torch.int8, "v_codes"), _dev(v_scales, torch.float32, "v_scales"), scale,
+              _dev(o, torch.float32, "out"), ws_ptr, ws_bytes, stream)
+    return o
 
 
 # ---------------------------------------------------------- measurement ----

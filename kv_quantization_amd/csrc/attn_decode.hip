@@ -1,0 +1,422 @@
+// Decode attention over the quantized KV cache: one new token per query head.
+//
+// The pages define the cache (INT8 with one scale per token row) and its
+// dequantization, not the attention that reads it; this is that consumer,
+// textbook scaled-dot-product attention with grouped queries.  Query head h
+// reads KV head h / G (G = Hq / Hkv consecutive query heads per KV head):
+//
+//   s_t = scale * (q_h . k_t),  k_t = code_k[t] * k_scale[t]
+//   p   = softmax(s)            (running max subtracted)
+//   o_h = sum_t p_t v_t,        v_t = code_v[t] * v_scale[t]
+//
+// The scales multiply the integer dot products and the softmax weights; no
+// dequantized copy of the cache is made, and each cache byte is read once.
+//
+// Work: one workgroup per (KV head, chunk of tokens).  256 threads walk the
+// chunk in blocks of 128 tokens with an online softmax (running max and
+// sum; the partial output is rescaled when the max grows).  Per block:
+//   1. scores: 8 lanes per token, each with 16 dims of the key row (one
+//      16-byte load) and the same 16 dims of the G query rows in registers;
+//      the 8 partial dot products are summed with DPP lane moves (all 8
+//      lanes end with the same bits) and go to LDS;
+//   2. softmax: per head the block max and sum over 128 tokens (two waves,
+//      DPP then LDS), the new running max and rescale factor, and
+//      p * v_scale to LDS;
+//   3. values: thread (group of 16 tokens, 4 dims) adds p * v_scale * code
+//      over its tokens into registers (4-byte loads of value codes, issued
+//      with the key loads when the block starts).
+// At the end the 8 token groups are added in LDS in a fixed order.  With
+// several chunks per head, each workgroup writes (max, sum, output) of its
+// chunk behind the workspace's counter area; the last workgroup of a head
+// (agent-scope counter) merges the chunks in chunk order with the same
+// online rule and resets the counter.
+#include "kvq_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kAttnD = 128;       // head_dim
+constexpr int kAttnBlk = 128;     // tokens per block: 4 waves x 32
+constexpr int kAttnThreads = 256;
+constexpr uint32_t kAttnTargetWgs = 256;
+constexpr uint32_t kAttnMaxChunks = 256;   // chunks per KV head (kAttnTargetWgs / 1)
+constexpr int kAuxSc1 = 16;       // device-scope (sc1) buffer access: bypasses the per-XCD L2
+
+template <int GM>
+__global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
+    const float *__restrict__ q, uint32_t G, uint32_t hkv, uint32_t T, const int8_t *__restrict__ kc,
+    const float *__restrict__ ks, const int8_t *__restrict__ vc, const float *__restrict__ vs, float sm_scale,
+    uint32_t nchunks, uint32_t bpc, float *__restrict__ out, uint32_t *__restrict__ counters,
+    float *__restrict__ partials) {
+    constexpr int D = kAttnD;
+    __shared__ float s_w[kAttnBlk][GM];   // scores, then p * v_scale
+    __shared__ float s_red[2][GM][2];     // per wave of a head parity: block max, block sum
+    __shared__ float s_o[8][GM][D];       // the 8 token groups' outputs
+    __shared__ int s_last;
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint32_t g = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const uint32_t nblk = (T + kAttnBlk - 1) / kAttnBlk;
+    const uint32_t blk0 = c * bpc, blk1 = blk0 + bpc < nblk ? blk0 + bpc : nblk;
+
+    // query rows of this head group, the 16 dims of this lane's key slice
+    const uint32_t l8 = lane & 7, tk = lane >> 3;
+    float qr[GM][16];
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        const bool live = (uint32_t)j < G;
+        const f32x4 *qp = reinterpret_cast<const f32x4 *>(q + (size_t)(g * G + (live ? j : 0)) * D + 16 * l8);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const f32x4 v = live ? qp[e4] : f32x4{0.f, 0.f, 0.f, 0.f};
+            qr[j][4 * e4] = v.x; qr[j][4 * e4 + 1] = v.y; qr[j][4 * e4 + 2] = v.z; qr[j][4 * e4 + 3] = v.w;
+        }
+    }
+
+    const uint32_t rows = T * hkv;
+    const rsrc_t rk = make_rsrc(kc, rows * D), rv = make_rsrc(vc, rows * D);
+    const rsrc_t rks = make_rsrc(ks, rows * 4), rvs = make_rsrc(vs, rows * 4);
+    const uint32_t tg = tid >> 5, e4 = tid & 31;          // values: token group, 4-dim slice
+    const uint32_t tt = tid & (kAttnBlk - 1), hp = tid >> 7;   // softmax: token, head parity
+
+    float o[GM][4];
+    float m_run[GM], l_run[GM];
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        m_run[j] = -__builtin_inff();
+        l_run[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[j][e] = 0.f;
+    }
+
+    for (uint32_t blk = blk0; blk < blk1; ++blk) {
+        const uint32_t t0 = blk * kAttnBlk;
+        // -- loads of the block (out-of-range tokens read zeros)
+        u32x4 kraw[4];
+        float ksc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t t = t0 + wv * 32 + i * 8 + tk;
+            const uint32_t row = t * hkv + g;
+            kraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, t < T ? row * D + 16 * l8 : kOffNone, 0, 0);
+            ksc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, t < T ? row * 4 : kOffNone, 0, 0));
+        }
+        uint32_t vraw[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const uint32_t t = t0 + tg * 16 + u;
+            vraw[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, t < T ? (t * hkv + g) * D + 4 * e4 : kOffNone, 0, 0);
+        }
+        const uint32_t tv = t0 + tt;
+        const float vsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, tv < T ? (tv * hkv + g) * 4 : kOffNone, 0, 0));
+
+        // -- 1. scores
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x[16];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) x[4 * w + b] = (float)(int8_t)(kraw[i][w] >> (8 * b));
+            const uint32_t lt = wv * 32 + i * 8 + tk;
+            const bool valid = t0 + lt < T;
+#pragma unroll
+            for (int j = 0; j < GM; ++j) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) d = __builtin_fmaf(qr[j][e], x[e], d);
+                d = team_sum<8>(d);
+                const float s = valid ? (d * ksc[i]) * sm_scale : -__builtin_inff();
+                if (l8 == 0) s_w[lt][j] = s;
+            }
+        }
+        __syncthreads();
+
+        // -- 2. softmax of the block: thread (token tt, head parity hp) owns heads hp, hp + 2, ...
+        const uint32_t half = (tid >> 6) & 1;
+#pragma unroll
+        for (int j = 0; j < GM; ++j) {
+            if ((uint32_t)(j & 1) != hp && GM > 1) continue;
+            if (GM == 1 && hp) continue;
+            const float bm = team_max<64>(s_w[tt][j]);
+            if (lane == 0) s_red[half][j][0] = bm;
+        }
+        __syncthreads();
+        float alpha[GM];
+#pragma unroll
+        for (int j = 0; j < GM; ++j) {
+            const float bm = fmaxf(s_red[0][j][0], s_red[1][j][0]);
+            const float mn = fmaxf(m_run[j], bm);
+            alpha[j] = expf(m_run[j] - mn);   // 0 for the first block (m_run = -inf)
+            m_run[j] = mn;
+        }
+#pragma unroll
+        for (int j = 0; j < GM; ++j) {
+            if ((uint32_t)(j & 1) != hp && GM > 1) continue;
+            if (GM == 1 && hp) continue;
+            const float p = expf(s_w[tt][j] - m_run[j]);   // 0 for tokens past the end
+            s_w[tt][j] = p * vsc;
+            const float bs = team_sum<64>(p);
+            if (lane == 0) s_red[half][j][1] = bs;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < GM; ++j) l_run[j] = l_run[j] * alpha[j] + (s_red[0][j][1] + s_red[1][j][1]);
+
+        // -- 3. values
+#pragma unroll
+        for (int j = 0; j < GM; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[j][e] *= alpha[j];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            float cv[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) cv[b] = (float)(int8_t)(vraw[u] >> (8 * b));
+#pragma unroll
+            for (int j = 0; j < GM; ++j) {
+                const float w = s_w[tg * 16 + u][j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[j][e] = __builtin_fmaf(w, cv[e], o[j][e]);
+            }
+        }
+        __syncthreads();   // s_w and s_red are rewritten by the next block
+    }
+
+    // -- the 8 token groups, added in order
+#pragma unroll
+    for (int j = 0; j < GM; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_o[tg][j][4 * e4 + e] = o[j][e];
+    __syncthreads();
+    constexpr int kOut = GM * D;   // outputs of the head group
+    float ov[(kOut + kAttnThreads - 1) / kAttnThreads];
+#pragma unroll
+    for (int r = 0; r * kAttnThreads < kOut; ++r) {
+        const uint32_t idx = tid + r * kAttnThreads;
+        float a = 0.f;
+        if (idx < (uint32_t)kOut) {
+            const uint32_t j = idx / D, d = idx % D;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) a += s_o[x][j][d];
+        }
+        ov[r] = a;
+    }
+
+    if (nchunks == 1) {
+#pragma unroll
+        for (int r = 0; r * kAttnThreads < kOut; ++r) {
+            const uint32_t idx = tid + r * kAttnThreads;
+            const uint32_t j = idx / D, d = idx % D;
+            if (idx < (uint32_t)kOut && j < G) {
+                float l = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < GM; ++jj) l = (uint32_t)jj == j ? l_run[jj] : l;
+                out[(size_t)(g * G + j) * D + d] = ov[r] / l;
+            }
+        }
+        return;
+    }
+
+    // -- several chunks: (output, max, sum) of this chunk behind the counter
+    // area as [head][chunk][GM][D + 2], device-scope stores; the last
+    // workgroup of the head merges them in chunk order
+    constexpr uint32_t kRec = GM * (D + 2);
+    const rsrc_t rp = make_rsrc(partials + (size_t)g * nchunks * kRec, nchunks * kRec * 4);
+#pragma unroll
+    for (int r = 0; r * kAttnThreads < kOut; ++r) {
+        const uint32_t idx = tid + r * kAttnThreads;
+        if (idx < (uint32_t)kOut) {
+            const uint32_t j = idx / D, d = idx % D;
+            const uint32_t base = (c * GM + j) * (D + 2);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[r]), rp, (base + d) * 4, 0, kAuxSc1);
+            if (d == 0) {
+                float m = 0.f, l = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < GM; ++jj) {
+                    m = (uint32_t)jj == j ? m_run[jj] : m;
+                    l = (uint32_t)jj == j ? l_run[jj] : l;
+                }
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rp, (base + D) * 4, 0, kAuxSc1);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rp, (base + D + 1) * 4, 0, kAuxSc1);
+            }
+        }
+    }
+    // every thread's device-scope stores complete before the barrier, so they
+    // are visible at the coherence point before the counter moves
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&counters[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == nchunks - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    // Merge, in two batches of loads.  (1) Every chunk's max and sum to LDS
+    // (the token-group area is free again: this thread's outputs are in ov).
+    float *s_cm = &s_o[0][0][0];               // [chunk][GM]: max, then weight exp(m_c - M)
+    float *s_cl = s_cm + kAttnMaxChunks * GM;  // [chunk][GM]: sum
+    constexpr int kMl = kAttnMaxChunks * GM / kAttnThreads;
+    {
+        uint32_t mm[kMl], ll[kMl];
+#pragma unroll
+        for (int r = 0; r < kMl; ++r) {
+            const uint32_t idx = tid + r * kAttnThreads, cc = idx / GM, j = idx % GM;
+            const uint32_t base = (cc * GM + j) * (D + 2);
+            const bool in = cc < nchunks;
+            mm[r] = __builtin_amdgcn_raw_buffer_load_b32(rp, in ? (base + D) * 4 : kOffNone, 0, kAuxSc1);
+            ll[r] = __builtin_amdgcn_raw_buffer_load_b32(rp, in ? (base + D + 1) * 4 : kOffNone, 0, kAuxSc1);
+        }
+#pragma unroll
+        for (int r = 0; r < kMl; ++r) {
+            const uint32_t idx = tid + r * kAttnThreads;
+            s_cm[idx] = __uint_as_float(mm[r]);
+            s_cl[idx] = __uint_as_float(ll[r]);
+        }
+    }
+    __syncthreads();
+    // (2) per head, one wave: the overall max, each chunk's weight, and the
+    // weighted sum of the chunk sums (lanes take chunks lane, lane + 64, ...;
+    // fixed-order DPP reductions)
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        if ((uint32_t)j % 4 != wv) continue;
+        float mx = -__builtin_inff();
+        for (uint32_t cc = lane; cc < nchunks; cc += 64) mx = fmaxf(mx, s_cm[cc * GM + j]);
+        const float M = team_max<64>(mx);
+        float lsum = 0.f;
+        for (uint32_t cc = lane; cc < nchunks; cc += 64) {
+            const float bw = expf(s_cm[cc * GM + j] - M);
+            s_cm[cc * GM + j] = bw;
+            lsum = __builtin_fmaf(bw, s_cl[cc * GM + j], lsum);
+        }
+        lsum = team_sum<64>(lsum);
+        if (lane == 0) s_red[0][j][1] = lsum;
+    }
+    __syncthreads();
+    // (3) outputs: every chunk's value, 16 chunks of loads in flight per output
+    float acc[(kOut + kAttnThreads - 1) / kAttnThreads];
+#pragma unroll
+    for (int r = 0; r * kAttnThreads < kOut; ++r) acc[r] = 0.f;
+    for (uint32_t c0 = 0; c0 < nchunks; c0 += 16) {
+        uint32_t ov16[(kOut + kAttnThreads - 1) / kAttnThreads][16];
+#pragma unroll
+        for (int r = 0; r * kAttnThreads < kOut; ++r) {
+            const uint32_t idx = tid + r * kAttnThreads, j = idx / D, d = idx % D;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const uint32_t cc = c0 + u;
+                const bool in = cc < nchunks && idx < (uint32_t)kOut;
+                ov16[r][u] = __builtin_amdgcn_raw_buffer_load_b32(rp, in ? ((cc * GM + j) * (D + 2) + d) * 4 : kOffNone,
+                                                                  0, kAuxSc1);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r * kAttnThreads < kOut; ++r) {
+            const uint32_t idx = tid + r * kAttnThreads, j = idx / D;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const uint32_t cc = c0 + u;
+                if (cc < nchunks && idx < (uint32_t)kOut)
+                    acc[r] = __builtin_fmaf(s_cm[cc * GM + j], __uint_as_float(ov16[r][u]), acc[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r * kAttnThreads < kOut; ++r) {
+        const uint32_t idx = tid + r * kAttnThreads, j = idx / D, d = idx % D;
+        if (idx < (uint32_t)kOut && j < G) out[(size_t)(g * G + j) * D + d] = acc[r] / s_red[0][j][1];
+    }
+    if (tid == 0) __hip_atomic_store(&counters[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct AttnPlan {
+    uint32_t gm, nchunks, bpc;
+    size_t ws_bytes;
+};
+
+uint32_t attn_gm(uint32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
+
+// ~256 workgroups: split each head's tokens into chunks of whole 128-token blocks
+AttnPlan attn_plan(uint32_t hq, uint32_t hkv, uint32_t T) {
+    AttnPlan pl;
+    pl.gm = attn_gm(hq / hkv);
+    const uint32_t nblk = (T + kAttnBlk - 1) / kAttnBlk;
+    uint32_t want = kAttnTargetWgs / hkv;
+    if (want < 1) want = 1;
+    if (want > nblk) want = nblk;
+    if (hkv * 4 > KVQ_WORKSPACE_COUNTER_BYTES) want = 1;   // one counter per KV head
+    pl.bpc = (nblk + want - 1) / want;
+    pl.nchunks = (nblk + pl.bpc - 1) / pl.bpc;
+    pl.ws_bytes = pl.nchunks > 1
+                      ? KVQ_WORKSPACE_COUNTER_BYTES + (size_t)hkv * pl.nchunks * pl.gm * (kAttnD + 2) * 4
+                      : 0;
+    return pl;
+}
+
+int check_attn(const char *fn, uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D) {
+    if (hq == 0 || hkv == 0 || T == 0)
+        return fail(KVQ_E_INVALID, "%s: num_q_heads=%u num_kv_heads=%u num_tokens=%u (want all > 0)", fn, hq, hkv, T);
+    if (hq % hkv || hq / hkv > 8)
+        return fail(KVQ_E_INVALID, "%s: num_q_heads=%u is not 1..8 times num_kv_heads=%u", fn, hq, hkv);
+    if (D != kAttnD) return fail(KVQ_E_INVALID, "%s: head_dim=%u (supported: 128)", fn, D);
+    if ((uint64_t)T * hkv * D >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: cache larger than 2 GiB", fn);
+    return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" int kvq_attn_decode_workspace_bytes(uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t num_tokens,
+                                               uint32_t head_dim, size_t *bytes) {
+    if (!bytes) return fail(KVQ_E_INVALID, "kvq_attn_decode_workspace_bytes: null output pointer");
+    *bytes = 0;
+    const int st = check_attn("kvq_attn_decode_workspace_bytes", num_q_heads, num_kv_heads, num_tokens, head_dim);
+    if (st) return st;
+    *bytes = attn_plan(num_q_heads, num_kv_heads, num_tokens).ws_bytes;
+    return KVQ_OK;
+}
+
+extern "C" int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads, uint32_t num_kv_heads,
+                                    uint32_t num_tokens, uint32_t head_dim, const int8_t *k_codes,
+                                    const float *k_scales, const int8_t *v_codes, const float *v_scales,
+                                    float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+    const char *fn = "kvq_attn_decode_int8";
+    int st = check_attn(fn, num_q_heads, num_kv_heads, num_tokens, head_dim);
+    if (st) return st;
+    st = check_ptrs(fn, {q, k_codes, k_scales, v_codes, v_scales, out});
+    if (st) return st;
+    if (!(softmax_scale == softmax_scale) || __builtin_isinf(softmax_scale))
+        return fail(KVQ_E_INVALID, "%s: softmax_scale is not finite", fn);
+    AttnPlan pl = attn_plan(num_q_heads, num_kv_heads, num_tokens);
+    uint32_t *counters = nullptr;
+    float *partials = nullptr;
+    if (pl.nchunks > 1) {
+        if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
+            pl.bpc = (num_tokens + kAttnBlk - 1) / kAttnBlk;   // no workspace: one workgroup per KV head
+            pl.nchunks = 1;
+        } else {
+            counters = static_cast<uint32_t *>(workspace);
+            partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
+        }
+    }
+    const uint32_t G = num_q_heads / num_kv_heads;
+    const unsigned grid = num_kv_heads * pl.nchunks;
+    hipStream_t s = as_stream(stream);
+#define KVQ_ATTN(GM)                                                                                            \
+    attn_decode_i8<GM><<<grid, kAttnThreads, 0, s>>>(q, G, num_kv_heads, num_tokens, k_codes, k_scales, v_codes, \
+                                                     v_scales, softmax_scale, pl.nchunks, pl.bpc, out, counters,   \
+                                                     partials)
+    switch (pl.gm) {
+        case 1: KVQ_ATTN(1); break;
+        case 2: KVQ_ATTN(2); break;
+        case 4: KVQ_ATTN(4); break;
+        default: KVQ_ATTN(8); break;
+    }
+#undef KVQ_ATTN
+    return launch_status(fn);
+}

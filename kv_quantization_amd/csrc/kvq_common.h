@@ -22,6 +22,15 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Every pointer set and 16-byte aligned, else KVQ_E_INVALID naming the call.
+inline int check_ptrs(const char *fn, std::initializer_list<const void *> ps) {
+    for (const void *p : ps) {
+        if (!p) return fail(KVQ_E_INVALID, "%s: null pointer argument", fn);
+        if (!aligned16(p)) return fail(KVQ_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    }
+    return KVQ_OK;
+}
+
 constexpr int kWave = 64;
 
 // Native vector types (usable with the nontemporal load/store builtins).
@@ -83,6 +92,32 @@ template <int W>
 __device__ __forceinline__ float team_min(float v) { return order_float(team_ext<W, false>(float_order(v))); }
 
 // Max of non-negative floats (absolute values).
+// Sum over an aligned team of W lanes with the same lane moves.  Each step
+// adds a lane's value and its partner's, and fp addition is commutative, so
+// every lane of the team ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int W>
+__device__ __forceinline__ float team_sum(float v) {
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "teams of 1..64 lanes");
+    if (W >= 2) v += dpp_move<0xB1>(v);
+    if (W >= 4) v += dpp_move<0x4E>(v);
+    if (W >= 8) v += dpp_move<0x141>(v);
+    if (W >= 16) v += dpp_move<0x140>(v);
+    if (W >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if (W >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return v;
+}
+
 template <int W>
 __device__ __forceinline__ float team_absmax(float v) { return __int_as_float(team_ext<W, true>(__float_as_int(v))); }
 

@@ -175,14 +175,6 @@ __global__ __launch_bounds__(kBlock) void cast_e4m3(const float *__restrict__ x,
 
 // ---------------------------------------------------------------- host ---
 
-int check_ptrs(const char *fn, std::initializer_list<const void *> ps) {
-    for (const void *p : ps) {
-        if (!p) return fail(KVQ_E_INVALID, "%s: null pointer argument", fn);
-        if (!aligned16(p)) return fail(KVQ_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
-    }
-    return KVQ_OK;
-}
-
 }  // namespace
 
 int act_quant_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t *up, uint32_t ldx,

@@ -203,3 +203,42 @@ def test_kv_dtype_calls_share_the_fp32_checks(lib):
     assert st == _lib.KVQ_E_INVALID and "num_tokens=0" in msg
     st, msg = _err(lib, "kvq_quant_int4_group_dt", FAKE, 2, FAKE, FAKE, FAKE, 4, 8, 3, None)
     assert st == _lib.KVQ_E_INVALID and "group_size" in msg
+
+
+# decode attention: q, Hq, Hkv, T, D, k codes, k scales, v codes, v scales, scale, out, ws, ws bytes, stream
+def _attn(hq=32, hkv=8, t=4096, d=128, q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, scale=0.088, out=FAKE):
+    return (q, hq, hkv, t, d, kc, ks, vc, vs, ctypes.c_float(scale), out, None, 0, None)
+
+
+@pytest.mark.parametrize("args,frag", [
+    (_attn(hq=0), "num_q_heads=0"),
+    (_attn(hkv=0), "num_kv_heads=0"),
+    (_attn(t=0), "num_tokens=0"),
+    (_attn(hq=12, hkv=8), "not 1..8 times"),
+    (_attn(hq=72, hkv=8), "not 1..8 times"),
+    (_attn(d=64), "head_dim=64"),
+    (_attn(t=1 << 21, hkv=8), "2 GiB"),
+    (_attn(q=0), "null"),
+    (_attn(vs=0), "null"),
+    (_attn(kc=MISALIGNED), "aligned"),
+    (_attn(scale=float("inf")), "softmax_scale"),
+    (_attn(scale=float("nan")), "softmax_scale"),
+])
+def test_attn_decode_validation(lib, args, frag):
+    st, msg = _err(lib, "kvq_attn_decode_int8", *args)
+    assert st == _lib.KVQ_E_INVALID and frag in msg, msg
+
+
+def test_attn_decode_workspace_sizes(lib):
+    b = ctypes.c_size_t()
+    # 4096 tokens, 8 KV heads: 32 blocks of 128 tokens per head, one chunk
+    # each (256 workgroups), records of 4 heads x (128 outputs + max + sum)
+    assert lib.kvq_attn_decode_workspace_bytes(32, 8, 4096, 128, ctypes.byref(b)) == 0
+    assert b.value == 4096 + 8 * 32 * 4 * 130 * 4
+    # one block per head: no chunks to merge, no workspace
+    assert lib.kvq_attn_decode_workspace_bytes(32, 8, 128, 128, ctypes.byref(b)) == 0
+    assert b.value == 0
+    # 6 query heads per KV head are padded to 8 in the records
+    assert lib.kvq_attn_decode_workspace_bytes(48, 8, 1000, 128, ctypes.byref(b)) == 0
+    assert b.value == 4096 + 8 * 8 * 8 * 130 * 4
+    assert lib.kvq_attn_decode_workspace_bytes(32, 8, 0, 128, ctypes.byref(b)) == _lib.KVQ_E_INVALID

@@ -1,0 +1,110 @@
+"""GPU parity: decode attention over the INT8 per-token KV cache vs the
+oracle's fp64 definition, |gpu - ref| <= 1e-3 * sum_t p_t |v_t| per output,
+through the C ABI.  The caches are quantized on the CPU by the oracle's
+per-token quantizer (the same bytes the GPU quantizer writes)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import print_case
+from gpu_util import dev, host
+from kv_quantization_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-3
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _bind_oracle(oracle_mod):
+    global _oracle
+    _oracle = oracle_mod
+
+
+def _cache(t, hkv, hq, d, seed, k_gain=1.0):
+    q, k, v = synth.attn_decode(t, hkv, hq, d, seed=seed)
+    k = k * np.float32(k_gain)
+    kc, ks = _oracle.kv_int8_quant(k.reshape(t * hkv, d))
+    vc, vs = _oracle.kv_int8_quant(v.reshape(t * hkv, d))
+    return q, kc.reshape(t, hkv, d), ks.reshape(t, hkv), vc.reshape(t, hkv, d), vs.reshape(t, hkv)
+
+
+def _run(q, kc, ks, vc, vs, scale, use_workspace=True):
+    out = api.attn_decode_int8(dev(q), dev(kc), dev(ks), dev(vc), dev(vs), scale, use_workspace=use_workspace)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def _check(inputs, scale, got, what):
+    ref, bound = _oracle.attn_decode_int8(*inputs, scale)
+    ratio = np.abs(got.astype(np.float64) - ref) / np.maximum(bound, 1e-30)
+    worst = float(ratio.max())
+    print(f"{what}: max |err|/sum p|v| = {worst:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), what
+    assert worst <= RTOL, what
+
+
+def test_decode_workload():
+    """4096 tokens x 8 KV heads x 128 (the 32768 x 128 cache), 32 query heads."""
+    print_case("attn int8 4096x8 hq32")
+    inp = _cache(4096, 8, 32, 128, seed=11)
+    scale = 1.0 / math.sqrt(128)
+    a = _run(*inp, scale)
+    _check(inp, scale, a, "decode 4096x8x128 Hq=32")
+    b = _run(*inp, scale)
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))   # same bits every call
+    c = _run(*inp, scale, use_workspace=False)
+    _check(inp, scale, c, "decode, no workspace")
+
+
+@pytest.mark.parametrize("t", [1, 2, 5, 127, 128, 129, 255, 1000, 4095])
+@pytest.mark.parametrize("hkv,hq", [(1, 1), (2, 4), (8, 32)])
+def test_token_counts(t, hkv, hq):
+    print_case("attn int8 tokens", t, hkv, hq)
+    inp = _cache(t, hkv, hq, 128, seed=100 + t + hq)
+    _check(inp, 0.0884, _run(*inp, 0.0884), f"T={t} Hkv={hkv} Hq={hq}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_query_heads_per_kv_head(g):
+    print_case("attn int8 group", g)
+    inp = _cache(700, 3, 3 * g, 128, seed=200 + g)
+    _check(inp, 0.0884, _run(*inp, 0.0884), f"G={g}")
+
+
+@pytest.mark.parametrize("t,hkv", [(32768, 1), (65536, 1), (20000, 2)])
+def test_long_caches(t, hkv):
+    """One KV head over 32768 tokens (256 chunks to merge), 65536 tokens
+    (two blocks per chunk: the online softmax inside a workgroup), and the
+    same without a workspace (one workgroup walks every block)."""
+    print_case("attn int8 long", t, hkv)
+    inp = _cache(t, hkv, 4 * hkv, 128, seed=300 + t)
+    _check(inp, 0.0884, _run(*inp, 0.0884), f"T={t} Hkv={hkv}")
+    if t == 65536:
+        _check(inp, 0.0884, _run(*inp, 0.0884, use_workspace=False), f"T={t} no workspace")
+
+
+@pytest.mark.parametrize("gain,scale", [(1.0, 1.0), (8.0, 0.5), (0.0, 0.0884), (1.0, 0.0), (1.0, -0.2)])
+def test_score_ranges(gain, scale):
+    """Sharp softmax (scores in the hundreds: nearly one token per head), flat
+    keys (all scores equal), a zero and a negative scale."""
+    print_case("attn int8 scores", gain, scale)
+    inp = _cache(1500, 2, 8, 128, seed=400, k_gain=gain)
+    _check(inp, scale, _run(*inp, scale), f"gain={gain} scale={scale}")
+
+
+def test_workspace_shared_with_split_k_calls():
+    """The attention call leaves the counter area at zero for the next call of
+    another kind on the same workspace (INT4 M=1 exchanges K slices through
+    it), and the reverse."""
+    print_case("attn int8 shared workspace")
+    inp = _cache(3000, 4, 16, 128, seed=500)
+    _check(inp, 0.0884, _run(*inp, 0.0884), "attn first")
+    x, projs = synth.int4_awq(1, 512, (136, 24, 24), 32, seed=501)
+    outs = api.int4_awq_qkv(dev(x), [(dev(p.qweight), dev(p.scales), dev(p.zeros)) for p in projs], 32)
+    torch.cuda.synchronize()
+    refs = _oracle.int4_awq_qkv(x, [(p.qweight, p.scales, p.zeros) for p in projs], 32)
+    for o, (ref, bound) in zip(outs, refs):
+        assert np.max(np.abs(host(o).astype(np.float64) - ref) / np.maximum(bound, 1e-300)) <= RTOL
+    _check(inp, 0.0884, _run(*inp, 0.0884), "attn after int4")
