@@ -307,11 +307,11 @@ int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k,
  *   out:      fp32 [num_q_heads][head_dim]
  * head_dim is 128; num_q_heads is 1..8 times num_kv_heads; num_tokens >= 1.
  * All pointers are device memory, 16-byte aligned, owned by the caller.
- * workspace: NULL, or at least kvq_attn_decode_workspace_bytes(), zero-
- * filled before first use (the shared workspace of the calls above: the
- * per-head counters sit in its counter area, which the call leaves at zero,
- * and the per-chunk partial results behind it).  Without it one workgroup
- * walks each KV head's tokens (less parallelism, same definition).
+ * workspace: NULL, or at least kvq_attn_decode_workspace_bytes() (the
+ * shared workspace of the calls above: the per-chunk partial results go
+ * behind its counter area, which this call does not touch; a second kernel
+ * on the stream merges them).  Without it one workgroup walks each KV
+ * head's tokens (less parallelism, same definition).
  * Concurrent calls must not share a workspace.  Errors: KVQ_E_INVALID for
  * shapes, null or misaligned pointers, a non-finite softmax_scale. */
 int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads,

@@ -26,10 +26,11 @@
 //      over its tokens into registers (4-byte loads of value codes, issued
 //      with the key loads when the block starts).
 // At the end the 8 token groups are added in LDS in a fixed order.  With
-// several chunks per head, each workgroup writes (max, sum, output) of its
-// chunk behind the workspace's counter area; the last workgroup of a head
-// (agent-scope counter) merges the chunks in chunk order with the same
-// online rule and resets the counter.
+// several chunks per head, each workgroup writes (output, max, sum) of its
+// chunk behind the workspace's counter area and a second kernel merges the
+// chunks in chunk order (measured: merging inside the attention kernel by
+// the last workgroup of a head, after device-scope stores and a counter,
+// cost 8 us of a 14 us call; the kernel boundary is cheaper).
 #include "kvq_common.h"
 
 namespace kvq {
@@ -39,20 +40,16 @@ constexpr int kAttnD = 128;       // head_dim
 constexpr int kAttnBlk = 128;     // tokens per block: 4 waves x 32
 constexpr int kAttnThreads = 256;
 constexpr uint32_t kAttnTargetWgs = 256;
-constexpr uint32_t kAttnMaxChunks = 256;   // chunks per KV head (kAttnTargetWgs / 1)
-constexpr int kAuxSc1 = 16;       // device-scope (sc1) buffer access: bypasses the per-XCD L2
 
 template <int GM>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
     const float *__restrict__ q, uint32_t G, uint32_t hkv, uint32_t T, const int8_t *__restrict__ kc,
     const float *__restrict__ ks, const int8_t *__restrict__ vc, const float *__restrict__ vs, float sm_scale,
-    uint32_t nchunks, uint32_t bpc, float *__restrict__ out, uint32_t *__restrict__ counters,
-    float *__restrict__ partials) {
+    uint32_t nchunks, uint32_t bpc, float *__restrict__ out, float *__restrict__ partials) {
     constexpr int D = kAttnD;
     __shared__ float s_w[kAttnBlk][GM];   // scores, then p * v_scale
     __shared__ float s_red[2][GM][2];     // per wave of a head parity: block max, block sum
     __shared__ float s_o[8][GM][D];       // the 8 token groups' outputs
-    __shared__ int s_last;
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint32_t g = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
@@ -218,18 +215,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
         return;
     }
 
-    // -- several chunks: (output, max, sum) of this chunk behind the counter
-    // area as [head][chunk][GM][D + 2], device-scope stores; the last
-    // workgroup of the head merges them in chunk order
-    constexpr uint32_t kRec = GM * (D + 2);
-    const rsrc_t rp = make_rsrc(partials + (size_t)g * nchunks * kRec, nchunks * kRec * 4);
+    // -- several chunks: (output, max, sum, 2 pad) of this chunk as a record
+    // [head][chunk][GM][D + 4] behind the workspace's counter area; the
+    // merge kernel that follows on the stream combines them
+    constexpr uint32_t kRecD = D + 4;
+    float *rec = partials + ((size_t)g * nchunks + c) * GM * kRecD;
 #pragma unroll
     for (int r = 0; r * kAttnThreads < kOut; ++r) {
         const uint32_t idx = tid + r * kAttnThreads;
         if (idx < (uint32_t)kOut) {
             const uint32_t j = idx / D, d = idx % D;
-            const uint32_t base = (c * GM + j) * (D + 2);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[r]), rp, (base + d) * 4, 0, kAuxSc1);
+            rec[j * kRecD + d] = ov[r];
             if (d == 0) {
                 float m = 0.f, l = 0.f;
 #pragma unroll
@@ -237,98 +233,46 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
                     m = (uint32_t)jj == j ? m_run[jj] : m;
                     l = (uint32_t)jj == j ? l_run[jj] : l;
                 }
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rp, (base + D) * 4, 0, kAuxSc1);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rp, (base + D + 1) * 4, 0, kAuxSc1);
+                rec[j * kRecD + D] = m;
+                rec[j * kRecD + D + 1] = l;
             }
         }
     }
-    // every thread's device-scope stores complete before the barrier, so they
-    // are visible at the coherence point before the counter moves
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&counters[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == nchunks - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
+}
 
-    // Merge, in two batches of loads.  (1) Every chunk's max and sum to LDS
-    // (the token-group area is free again: this thread's outputs are in ov).
-    float *s_cm = &s_o[0][0][0];               // [chunk][GM]: max, then weight exp(m_c - M)
-    float *s_cl = s_cm + kAttnMaxChunks * GM;  // [chunk][GM]: sum
-    constexpr int kMl = kAttnMaxChunks * GM / kAttnThreads;
-    {
-        uint32_t mm[kMl], ll[kMl];
+// Merge of the chunk records: one workgroup per query head (KV head g, head
+// j of its group), one thread per output dim.  All output values of a batch
+// of 64 chunks are loaded at once; lane u of each wave takes chunk u's max
+// and sum, and fixed-order DPP reductions give the batch max, the chunk
+// weights exp(m_c - M) and the weighted sum of the sums, so the chunks are
+// added in order and the result does not depend on launch timing.
+template <int GM>
+__global__ __launch_bounds__(kAttnD) void attn_merge(const float *__restrict__ partials, uint32_t G,
+                                                     uint32_t nchunks, float *__restrict__ out) {
+    constexpr int D = kAttnD;
+    constexpr uint32_t kRecD = D + 4;
+    const uint32_t g = blockIdx.x / G, j = blockIdx.x % G, d = threadIdx.x, lane = d & 63;
+    const size_t rec0 = (size_t)g * nchunks * GM + j;   // record of chunk c: (rec0 + c * GM) * kRecD
+    float M = -__builtin_inff(), L = 0.f, O = 0.f;
+    for (uint32_t c0 = 0; c0 < nchunks; c0 += 64) {
+        float ov[64];
 #pragma unroll
-        for (int r = 0; r < kMl; ++r) {
-            const uint32_t idx = tid + r * kAttnThreads, cc = idx / GM, j = idx % GM;
-            const uint32_t base = (cc * GM + j) * (D + 2);
-            const bool in = cc < nchunks;
-            mm[r] = __builtin_amdgcn_raw_buffer_load_b32(rp, in ? (base + D) * 4 : kOffNone, 0, kAuxSc1);
-            ll[r] = __builtin_amdgcn_raw_buffer_load_b32(rp, in ? (base + D + 1) * 4 : kOffNone, 0, kAuxSc1);
-        }
+        for (int u = 0; u < 64; ++u)
+            ov[u] = c0 + u < nchunks ? partials[(rec0 + (size_t)(c0 + u) * GM) * kRecD + d] : 0.f;
+        const bool in = c0 + lane < nchunks;
+        const float *rl = partials + (rec0 + (size_t)(c0 + (in ? lane : 0)) * GM) * kRecD;
+        const float mc = in ? rl[D] : -__builtin_inff();
+        const float lc = in ? rl[D + 1] : 0.f;
+        const float mn = fmaxf(M, team_max<64>(mc));
+        const float a = expf(M - mn);   // rescales earlier batches (0 for the first)
+        const float bw = in ? expf(mc - mn) : 0.f;
+        L = L * a + team_sum<64>(bw * lc);
+        O *= a;
 #pragma unroll
-        for (int r = 0; r < kMl; ++r) {
-            const uint32_t idx = tid + r * kAttnThreads;
-            s_cm[idx] = __uint_as_float(mm[r]);
-            s_cl[idx] = __uint_as_float(ll[r]);
-        }
+        for (int u = 0; u < 64; ++u) O = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bw), u)), ov[u], O);
+        M = mn;
     }
-    __syncthreads();
-    // (2) per head, one wave: the overall max, each chunk's weight, and the
-    // weighted sum of the chunk sums (lanes take chunks lane, lane + 64, ...;
-    // fixed-order DPP reductions)
-#pragma unroll
-    for (int j = 0; j < GM; ++j) {
-        if ((uint32_t)j % 4 != wv) continue;
-        float mx = -__builtin_inff();
-        for (uint32_t cc = lane; cc < nchunks; cc += 64) mx = fmaxf(mx, s_cm[cc * GM + j]);
-        const float M = team_max<64>(mx);
-        float lsum = 0.f;
-        for (uint32_t cc = lane; cc < nchunks; cc += 64) {
-            const float bw = expf(s_cm[cc * GM + j] - M);
-            s_cm[cc * GM + j] = bw;
-            lsum = __builtin_fmaf(bw, s_cl[cc * GM + j], lsum);
-        }
-        lsum = team_sum<64>(lsum);
-        if (lane == 0) s_red[0][j][1] = lsum;
-    }
-    __syncthreads();
-    // (3) outputs: every chunk's value, 16 chunks of loads in flight per output
-    float acc[(kOut + kAttnThreads - 1) / kAttnThreads];
-#pragma unroll
-    for (int r = 0; r * kAttnThreads < kOut; ++r) acc[r] = 0.f;
-    for (uint32_t c0 = 0; c0 < nchunks; c0 += 16) {
-        uint32_t ov16[(kOut + kAttnThreads - 1) / kAttnThreads][16];
-#pragma unroll
-        for (int r = 0; r * kAttnThreads < kOut; ++r) {
-            const uint32_t idx = tid + r * kAttnThreads, j = idx / D, d = idx % D;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const uint32_t cc = c0 + u;
-                const bool in = cc < nchunks && idx < (uint32_t)kOut;
-                ov16[r][u] = __builtin_amdgcn_raw_buffer_load_b32(rp, in ? ((cc * GM + j) * (D + 2) + d) * 4 : kOffNone,
-                                                                  0, kAuxSc1);
-            }
-        }
-#pragma unroll
-        for (int r = 0; r * kAttnThreads < kOut; ++r) {
-            const uint32_t idx = tid + r * kAttnThreads, j = idx / D;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const uint32_t cc = c0 + u;
-                if (cc < nchunks && idx < (uint32_t)kOut)
-                    acc[r] = __builtin_fmaf(s_cm[cc * GM + j], __uint_as_float(ov16[r][u]), acc[r]);
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r * kAttnThreads < kOut; ++r) {
-        const uint32_t idx = tid + r * kAttnThreads, j = idx / D, d = idx % D;
-        if (idx < (uint32_t)kOut && j < G) out[(size_t)(g * G + j) * D + d] = acc[r] / s_red[0][j][1];
-    }
-    if (tid == 0) __hip_atomic_store(&counters[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    out[((size_t)g * G + j) * D + d] = O / L;
 }
 
 struct AttnPlan {
@@ -346,11 +290,10 @@ AttnPlan attn_plan(uint32_t hq, uint32_t hkv, uint32_t T) {
     uint32_t want = kAttnTargetWgs / hkv;
     if (want < 1) want = 1;
     if (want > nblk) want = nblk;
-    if (hkv * 4 > KVQ_WORKSPACE_COUNTER_BYTES) want = 1;   // one counter per KV head
     pl.bpc = (nblk + want - 1) / want;
     pl.nchunks = (nblk + pl.bpc - 1) / pl.bpc;
     pl.ws_bytes = pl.nchunks > 1
-                      ? KVQ_WORKSPACE_COUNTER_BYTES + (size_t)hkv * pl.nchunks * pl.gm * (kAttnD + 2) * 4
+                      ? KVQ_WORKSPACE_COUNTER_BYTES + (size_t)hkv * pl.nchunks * pl.gm * (kAttnD + 4) * 4
                       : 0;
     return pl;
 }
@@ -393,24 +336,25 @@ extern "C" int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads, uint32
     if (!(softmax_scale == softmax_scale) || __builtin_isinf(softmax_scale))
         return fail(KVQ_E_INVALID, "%s: softmax_scale is not finite", fn);
     AttnPlan pl = attn_plan(num_q_heads, num_kv_heads, num_tokens);
-    uint32_t *counters = nullptr;
     float *partials = nullptr;
     if (pl.nchunks > 1) {
         if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
             pl.bpc = (num_tokens + kAttnBlk - 1) / kAttnBlk;   // no workspace: one workgroup per KV head
             pl.nchunks = 1;
         } else {
-            counters = static_cast<uint32_t *>(workspace);
             partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
         }
     }
     const uint32_t G = num_q_heads / num_kv_heads;
     const unsigned grid = num_kv_heads * pl.nchunks;
     hipStream_t s = as_stream(stream);
-#define KVQ_ATTN(GM)                                                                                            \
-    attn_decode_i8<GM><<<grid, kAttnThreads, 0, s>>>(q, G, num_kv_heads, num_tokens, k_codes, k_scales, v_codes, \
-                                                     v_scales, softmax_scale, pl.nchunks, pl.bpc, out, counters,   \
-                                                     partials)
+#define KVQ_ATTN(GM)                                                                                              \
+    do {                                                                                                          \
+        attn_decode_i8<GM><<<grid, kAttnThreads, 0, s>>>(q, G, num_kv_heads, num_tokens, k_codes, k_scales,       \
+                                                         v_codes, v_scales, softmax_scale, pl.nchunks, pl.bpc, out, \
+                                                         partials);                                               \
+        if (pl.nchunks > 1) attn_merge<GM><<<num_kv_heads * G, kAttnD, 0, s>>>(partials, G, pl.nchunks, out);    \
+    } while (0)
     switch (pl.gm) {
         case 1: KVQ_ATTN(1); break;
         case 2: KVQ_ATTN(2); break;

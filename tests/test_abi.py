@@ -232,13 +232,13 @@ def test_attn_decode_validation(lib, args, frag):
 def test_attn_decode_workspace_sizes(lib):
     b = ctypes.c_size_t()
     # 4096 tokens, 8 KV heads: 32 blocks of 128 tokens per head, one chunk
-    # each (256 workgroups), records of 4 heads x (128 outputs + max + sum)
+    # each (256 workgroups), records of 4 heads x (128 outputs, max, sum, 2 pad)
     assert lib.kvq_attn_decode_workspace_bytes(32, 8, 4096, 128, ctypes.byref(b)) == 0
-    assert b.value == 4096 + 8 * 32 * 4 * 130 * 4
+    assert b.value == 4096 + 8 * 32 * 4 * 132 * 4
     # one block per head: no chunks to merge, no workspace
     assert lib.kvq_attn_decode_workspace_bytes(32, 8, 128, 128, ctypes.byref(b)) == 0
     assert b.value == 0
     # 6 query heads per KV head are padded to 8 in the records
     assert lib.kvq_attn_decode_workspace_bytes(48, 8, 1000, 128, ctypes.byref(b)) == 0
-    assert b.value == 4096 + 8 * 8 * 8 * 130 * 4
+    assert b.value == 4096 + 8 * 8 * 8 * 132 * 4
     assert lib.kvq_attn_decode_workspace_bytes(32, 8, 0, 128, ctypes.byref(b)) == _lib.KVQ_E_INVALID
