@@ -86,9 +86,10 @@ AWQ_F16X_MS = (1, 16, 128)   # INT4 AWQ with fp16 activations, beside the step
 ATTN_T, ATTN_HKV, ATTN_HQ, ATTN_D = 4096, 8, 32, 128
 
 
-def attn_bytes():
+def attn_bytes(int4=False):
     rows = ATTN_T * ATTN_HKV
-    return 2 * rows * ATTN_D + 2 * rows * 4 + 2 * ATTN_HQ * ATTN_D * 4
+    cache = rows * ATTN_D // 2 + rows * (ATTN_D // KV_GS) * 8 if int4 else rows * ATTN_D + rows * 4
+    return 2 * cache + 2 * ATTN_HQ * ATTN_D * 4
 
 
 def awq_bytes(m, xbytes=4):
@@ -112,7 +113,8 @@ def extra_table():
             ("kv_int4_dequant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm")]
     rows += [(f"int4_awq_qkv_M{m}", awq_bytes(m), 2 * m * na * AWQ_K, "fp16") for m in AWQ_EXTRA_MS]
     rows += [(f"int4_awq_qkv_f16x_M{m}", awq_bytes(m, 2), 2 * m * na * AWQ_K, "fp16") for m in AWQ_F16X_MS]
-    rows += [(f"attn_decode_int8_T{ATTN_T}", attn_bytes(), 0, "hbm")]   # HBM-bound: vector ALU products
+    rows += [(f"attn_decode_int8_T{ATTN_T}", attn_bytes(), 0, "hbm"),   # HBM-bound: vector ALU products
+             (f"attn_decode_int4_g{KV_GS}_T{ATTN_T}", attn_bytes(True), 0, "hbm")]
     return rows
 
 
@@ -148,10 +150,15 @@ def make_inputs(torch, api, synth):
     aq, ak, av = synth.attn_decode(ATTN_T, ATTN_HKV, ATTN_HQ, ATTN_D, seed=11)
     s["attn_q"] = dev(aq)
     rows = ATTN_T * ATTN_HKV
+    ng = ATTN_D // KV_GS
     for name, a in (("k", ak), ("v", av)):
         codes, scales = api.quant_int8_token(dev(a.reshape(rows, ATTN_D)))
         s[f"attn_{name}c"] = codes.view(ATTN_T, ATTN_HKV, ATTN_D)
         s[f"attn_{name}s"] = scales.view(ATTN_T, ATTN_HKV)
+        p4, s4, z4 = api.quant_int4_group(dev(a.reshape(rows, ATTN_D)), KV_GS)
+        s[f"attn_{name}p4"] = p4.view(ATTN_T, ATTN_HKV, ATTN_D // 2)
+        s[f"attn_{name}s4"] = s4.view(ATTN_T, ATTN_HKV, ng)
+        s[f"attn_{name}z4"] = z4.view(ATTN_T, ATTN_HKV, ng)
     torch.cuda.synchronize()
     return s, (qkv, down, x5, projs)
 
@@ -231,6 +238,9 @@ class StepBuffers:
         L.append((f"attn_decode_int8_T{ATTN_T}", lambda: api.attn_decode_int8(s["attn_q"], s["attn_kc"], s["attn_ks"],
                                                                              s["attn_vc"], s["attn_vs"],
                                                                              out=self.attn_out)))
+        L.append((f"attn_decode_int4_g{KV_GS}_T{ATTN_T}",
+                  lambda: api.attn_decode_int4(s["attn_q"], KV_GS, s["attn_kp4"], s["attn_ks4"], s["attn_kz4"],
+                                               s["attn_vp4"], s["attn_vs4"], s["attn_vz4"], out=self.attn_out)))
         return L
 
     # each launcher issues exactly one call

@@ -326,6 +326,25 @@ int kvq_attn_decode_workspace_bytes(uint32_t num_q_heads, uint32_t num_kv_heads,
                                     uint32_t num_tokens, uint32_t head_dim,
                                     size_t *bytes);
 
+/* The same attention over the [KVQ] "INT4 Per-Group Quantization" cache:
+ * each (token, KV head) row of head_dim values holds head_dim / group_size
+ * groups (group_size 32, 64 or 128), dequantized as code * scale - zero *
+ * scale.  k_packed, v_packed: uint8 [num_tokens][num_kv_heads][head_dim/2],
+ * two codes per byte, even element in the low nibble (the quantizer's output
+ * for num_tokens*num_kv_heads rows); scales and zeros: fp32
+ * [num_tokens][num_kv_heads][head_dim/group_size].  Per group the scale
+ * multiplies sum q*code - zero * sum q, and the softmax weight times the
+ * scale multiplies the value codes.  Everything else (layout, workspace,
+ * tolerance, errors) as kvq_attn_decode_int8. */
+int kvq_attn_decode_int4(const float *q, uint32_t num_q_heads,
+                         uint32_t num_kv_heads, uint32_t num_tokens,
+                         uint32_t head_dim, uint32_t group_size,
+                         const uint8_t *k_packed, const float *k_scales,
+                         const float *k_zeros, const uint8_t *v_packed,
+                         const float *v_scales, const float *v_zeros,
+                         float softmax_scale, float *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* ======================================================================== */
 /* Measurement helper (not part of the method)                              */
 /* kvq_stream_read: reads `bytes` (a positive multiple of 16) at `src` (16-

@@ -349,6 +349,35 @@ def attn_decode_int8(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Ten
     return o
 
 
+def attn_decode_int4(q: torch.Tensor, group_size: int, k_packed: torch.Tensor, k_scales: torch.Tensor,
+                     k_zeros: torch.Tensor, v_packed: torch.Tensor, v_scales: torch.Tensor, v_zeros: torch.Tensor,
+                     softmax_scale: float = None, out: torch.Tensor = None, use_workspace: bool = True) -> torch.Tensor:
+    """q fp32 [Hq, D]; k/v packed uint8 [T, Hkv, D/2]; k/v scales and zeros
+    fp32 [T, Hkv, D/group_size] -> out fp32 [Hq, D]."""
+    hq, d = q.shape
+    t, hkv, half = k_packed.shape
+    ng = d // group_size if group_size else 0
+    if half * 2 != d or tuple(v_packed.shape) != (t, hkv, half):
+        raise ValueError("q, k_packed and v_packed shapes do not match")
+    for a in (k_scales, k_zeros, v_scales, v_zeros):
+        if tuple(a.shape) != (t, hkv, ng):
+            raise ValueError("scales and zeros must be [T, Hkv, D/group_size]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = _empty((hq, d), torch.float32, q) if out is None else out
+    stream = _stream(q)
+    ws_ptr, ws_bytes = 0, 0
+    if use_workspace:
+        ws_bytes = attn_decode_workspace_bytes(hq, hkv, t, d)
+        if ws_bytes:
+            ws_ptr = workspace(q.device, ws_bytes, stream).data_ptr()
+    f = lambda a, n: _dev(a, torch.float32, n)
+    _lib.call("kvq_attn_decode_int4", _dev(q, torch.float32, "q"), hq, hkv, t, d, group_size,
+              _dev(k_packed, torch.uint8, "k_packed"), f(k_scales, "k_scales"), f(k_zeros, "k_zeros"),
+              _dev(v_packed, torch.uint8, "v_packed"), f(v_scales, "v_scales"), f(v_zeros, "v_zeros"), scale,
+              _dev(o, torch.float32, "out"), ws_ptr, ws_bytes, stream)
+    return o
+
+
 # ---------------------------------------------------------- measurement ----
 
 def stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor) -> None:

@@ -1,16 +1,19 @@
 // Decode attention over the quantized KV cache: one new token per query head.
 //
-// The pages define the cache (INT8 with one scale per token row) and its
-// dequantization, not the attention that reads it; this is that consumer,
-// textbook scaled-dot-product attention with grouped queries.  Query head h
-// reads KV head h / G (G = Hq / Hkv consecutive query heads per KV head):
+// The pages define the cache (INT8 with one scale per token row, INT4 with a
+// scale and zero per group) and its dequantization, not the attention that
+// reads it; this is that consumer, textbook scaled-dot-product attention
+// with grouped queries.  Query head h reads KV head h / G (G = Hq / Hkv
+// consecutive query heads per KV head):
 //
-//   s_t = scale * (q_h . k_t),  k_t = code_k[t] * k_scale[t]
+//   s_t = scale * (q_h . k_t)   k_t = code * k_scale[t]  (INT8)
+//                               k_t = code * s - z * s   (INT4, per group)
 //   p   = softmax(s)            (running max subtracted)
-//   o_h = sum_t p_t v_t,        v_t = code_v[t] * v_scale[t]
+//   o_h = sum_t p_t v_t         v_t dequantized the same way
 //
-// The scales multiply the integer dot products and the softmax weights; no
-// dequantized copy of the cache is made, and each cache byte is read once.
+// The scales multiply the integer dot products (INT4: s * (sum q c - z sum
+// q) per group) and the softmax weights (INT4: sum_t (p s) c - sum_t (p s
+// z)); no dequantized copy of the cache is made, each cache byte is read once.
 //
 // Work: one workgroup per (KV head, chunk of tokens).  256 threads walk the
 // chunk in blocks of 128 tokens with an online softmax (running max and
@@ -41,15 +44,29 @@ constexpr int kAttnBlk = 128;     // tokens per block: 4 waves x 32
 constexpr int kAttnThreads = 256;
 constexpr uint32_t kAttnTargetWgs = 256;
 
-template <int GM>
-__global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
-    const float *__restrict__ q, uint32_t G, uint32_t hkv, uint32_t T, const int8_t *__restrict__ kc,
-    const float *__restrict__ ks, const int8_t *__restrict__ vc, const float *__restrict__ vs, float sm_scale,
-    uint32_t nchunks, uint32_t bpc, float *__restrict__ out, float *__restrict__ partials) {
+// The cache: INT8 codes [rows][D] with one scale per row (NG == 0), or INT4
+// codes packed two per byte [rows][D/2] (even element in the low nibble)
+// with NG groups of D/NG values per row, a scale and a zero per group
+// (value = code * scale - zero * scale).  rows = T * Hkv, row = t * Hkv + head.
+struct KvCache {
+    const uint8_t *kc, *vc;
+    const float *ks, *vs;   // [rows] (INT8) or [rows][NG] (INT4)
+    const float *kz, *vz;   // INT4 zeros [rows][NG]
+};
+
+template <int GM, int NG>
+__global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restrict__ q, uint32_t G, uint32_t hkv,
+                                                            uint32_t T, KvCache C, float sm_scale, uint32_t nchunks,
+                                                            uint32_t bpc, float *__restrict__ out,
+                                                            float *__restrict__ partials) {
     constexpr int D = kAttnD;
-    __shared__ float s_w[kAttnBlk][GM];   // scores, then p * v_scale
-    __shared__ float s_red[2][GM][2];     // per wave of a head parity: block max, block sum
-    __shared__ float s_o[8][GM][D];       // the 8 token groups' outputs
+    constexpr bool I4 = NG > 0;
+    constexpr int NGS = I4 ? NG : 1;                 // scale slots per row
+    constexpr uint32_t RB = I4 ? D / 2 : D;          // code bytes per row
+    __shared__ float s_w[kAttnBlk][GM];              // scores; INT8: then p * v_scale
+    __shared__ float s_wz[I4 ? kAttnBlk : 1][GM][I4 ? 2 * NGS : 1];   // INT4: p * s, p * s * z per group
+    __shared__ float s_red[2][GM][2];                // per wave of a head parity: block max, block sum
+    __shared__ float s_o[8][GM][D];                  // the 8 token groups' outputs
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint32_t g = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
@@ -57,8 +74,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
     const uint32_t blk0 = c * bpc, blk1 = blk0 + bpc < nblk ? blk0 + bpc : nblk;
 
     // query rows of this head group, the 16 dims of this lane's key slice
+    // (INT4: they lie in group l8 / (16 / (D / NG)) ... one group, since a
+    // group holds a multiple of 16 values)
     const uint32_t l8 = lane & 7, tk = lane >> 3;
-    float qr[GM][16];
+    float qr[GM][16], qsum[GM];
 #pragma unroll
     for (int j = 0; j < GM; ++j) {
         const bool live = (uint32_t)j < G;
@@ -68,20 +87,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
             const f32x4 v = live ? qp[e4] : f32x4{0.f, 0.f, 0.f, 0.f};
             qr[j][4 * e4] = v.x; qr[j][4 * e4 + 1] = v.y; qr[j][4 * e4 + 2] = v.z; qr[j][4 * e4 + 3] = v.w;
         }
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sq += qr[j][e];
+        qsum[j] = sq;
     }
+    const uint32_t kgrp = I4 ? (16 * l8) / (D / NGS) : 0;   // INT4 group of this lane's key dims
 
     const uint32_t rows = T * hkv;
-    const rsrc_t rk = make_rsrc(kc, rows * D), rv = make_rsrc(vc, rows * D);
-    const rsrc_t rks = make_rsrc(ks, rows * 4), rvs = make_rsrc(vs, rows * 4);
+    const rsrc_t rk = make_rsrc(C.kc, rows * RB), rv = make_rsrc(C.vc, rows * RB);
+    const rsrc_t rks = make_rsrc(C.ks, rows * NGS * 4), rvs = make_rsrc(C.vs, rows * NGS * 4);
+    const rsrc_t rkz = make_rsrc(I4 ? C.kz : C.ks, rows * NGS * 4), rvz = make_rsrc(I4 ? C.vz : C.vs, rows * NGS * 4);
     const uint32_t tg = tid >> 5, e4 = tid & 31;          // values: token group, 4-dim slice
+    const uint32_t vgrp = I4 ? (4 * e4) / (D / NGS) : 0;  // INT4 group of this thread's value dims
     const uint32_t tt = tid & (kAttnBlk - 1), hp = tid >> 7;   // softmax: token, head parity
 
-    float o[GM][4];
+    float o[GM][4], oz[GM];
     float m_run[GM], l_run[GM];
 #pragma unroll
     for (int j = 0; j < GM; ++j) {
         m_run[j] = -__builtin_inff();
         l_run[j] = 0.f;
+        oz[j] = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[j][e] = 0.f;
     }
@@ -90,31 +117,58 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
         const uint32_t t0 = blk * kAttnBlk;
         // -- loads of the block (out-of-range tokens read zeros)
         u32x4 kraw[4];
-        float ksc[4];
+        float ksc[4], kzr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t t = t0 + wv * 32 + i * 8 + tk;
             const uint32_t row = t * hkv + g;
-            kraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, t < T ? row * D + 16 * l8 : kOffNone, 0, 0);
-            ksc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, t < T ? row * 4 : kOffNone, 0, 0));
+            if (I4) {
+                const u32x2 w2 = __builtin_amdgcn_raw_buffer_load_b64(rk, t < T ? row * RB + 8 * l8 : kOffNone, 0, 0);
+                kraw[i] = u32x4{w2.x, w2.y, 0u, 0u};
+                const uint32_t so = t < T ? (row * NGS + kgrp) * 4 : kOffNone;
+                ksc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, so, 0, 0));
+                kzr[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkz, so, 0, 0));
+            } else {
+                kraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, t < T ? row * RB + 16 * l8 : kOffNone, 0, 0);
+                ksc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, t < T ? row * 4 : kOffNone, 0, 0));
+                kzr[i] = 0.f;
+            }
         }
         uint32_t vraw[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const uint32_t t = t0 + tg * 16 + u;
-            vraw[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, t < T ? (t * hkv + g) * D + 4 * e4 : kOffNone, 0, 0);
+            const uint32_t row = t * hkv + g;
+            if (I4)
+                vraw[u] = __builtin_amdgcn_raw_buffer_load_b16(rv, t < T ? row * RB + 2 * e4 : kOffNone, 0, 0);
+            else
+                vraw[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, t < T ? row * RB + 4 * e4 : kOffNone, 0, 0);
         }
         const uint32_t tv = t0 + tt;
-        const float vsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, tv < T ? (tv * hkv + g) * 4 : kOffNone, 0, 0));
+        const uint32_t vrow = tv * hkv + g;
+        float vsc[NGS], vzr[NGS];
+#pragma unroll
+        for (int k = 0; k < NGS; ++k) {
+            const uint32_t so = tv < T ? (vrow * NGS + k) * 4 : kOffNone;
+            vsc[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, so, 0, 0));
+            vzr[k] = I4 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvz, so, 0, 0)) : 0.f;
+        }
 
         // -- 1. scores
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float x[16];
+            if (I4) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
+                for (int w = 0; w < 2; ++w)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) x[4 * w + b] = (float)(int8_t)(kraw[i][w] >> (8 * b));
+                    for (int b = 0; b < 8; ++b) x[8 * w + b] = (float)((kraw[i][w] >> (4 * b)) & 0xFu);
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) x[4 * w + b] = (float)(int8_t)(kraw[i][w] >> (8 * b));
+            }
             const uint32_t lt = wv * 32 + i * 8 + tk;
             const bool valid = t0 + lt < T;
 #pragma unroll
@@ -122,8 +176,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) d = __builtin_fmaf(qr[j][e], x[e], d);
+                // INT8: scale the row's integer dot product once after the
+                // sum; INT4: each lane's 16 values share one group
+                if (I4) d = ksc[i] * __builtin_fmaf(-kzr[i], qsum[j], d);
                 d = team_sum<8>(d);
-                const float s = valid ? (d * ksc[i]) * sm_scale : -__builtin_inff();
+                const float s = valid ? (I4 ? d : d * ksc[i]) * sm_scale : -__builtin_inff();
                 if (l8 == 0) s_w[lt][j] = s;
             }
         }
@@ -152,7 +209,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
             if ((uint32_t)(j & 1) != hp && GM > 1) continue;
             if (GM == 1 && hp) continue;
             const float p = expf(s_w[tt][j] - m_run[j]);   // 0 for tokens past the end
-            s_w[tt][j] = p * vsc;
+            if (I4) {
+#pragma unroll
+                for (int k = 0; k < NGS; ++k) {
+                    const float ps = p * vsc[k];
+                    s_wz[I4 ? tt : 0][j][2 * k] = ps;
+                    s_wz[I4 ? tt : 0][j][I4 ? 2 * k + 1 : 0] = ps * vzr[k];
+                }
+            } else {
+                s_w[tt][j] = p * vsc[0];
+            }
             const float bs = team_sum<64>(p);
             if (lane == 0) s_red[half][j][1] = bs;
         }
@@ -160,31 +226,44 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_i8(
 #pragma unroll
         for (int j = 0; j < GM; ++j) l_run[j] = l_run[j] * alpha[j] + (s_red[0][j][1] + s_red[1][j][1]);
 
-        // -- 3. values
+        // -- 3. values: INT8 sum_t (p v_scale) code; INT4 sum_t (p s) code - sum_t (p s z)
 #pragma unroll
-        for (int j = 0; j < GM; ++j)
+        for (int j = 0; j < GM; ++j) {
+            oz[j] *= alpha[j];
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[j][e] *= alpha[j];
+        }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             float cv[4];
+            if (I4) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) cv[b] = (float)(int8_t)(vraw[u] >> (8 * b));
+                for (int b = 0; b < 4; ++b) cv[b] = (float)((vraw[u] >> (4 * b)) & 0xFu);
+            } else {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) cv[b] = (float)(int8_t)(vraw[u] >> (8 * b));
+            }
 #pragma unroll
             for (int j = 0; j < GM; ++j) {
-                const float w = s_w[tg * 16 + u][j];
+                float w;
+                if (I4) {
+                    w = s_wz[I4 ? tg * 16 + u : 0][j][2 * vgrp];
+                    oz[j] += s_wz[I4 ? tg * 16 + u : 0][j][I4 ? 2 * vgrp + 1 : 0];
+                } else {
+                    w = s_w[tg * 16 + u][j];
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[j][e] = __builtin_fmaf(w, cv[e], o[j][e]);
             }
         }
-        __syncthreads();   // s_w and s_red are rewritten by the next block
+        __syncthreads();   // s_w, s_wz and s_red are rewritten by the next block
     }
 
     // -- the 8 token groups, added in order
 #pragma unroll
     for (int j = 0; j < GM; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_o[tg][j][4 * e4 + e] = o[j][e];
+        for (int e = 0; e < 4; ++e) s_o[tg][j][4 * e4 + e] = o[j][e] - oz[j];
     __syncthreads();
     constexpr int kOut = GM * D;   // outputs of the head group
     float ov[(kOut + kAttnThreads - 1) / kAttnThreads];
@@ -323,6 +402,55 @@ extern "C" int kvq_attn_decode_workspace_bytes(uint32_t num_q_heads, uint32_t nu
     return KVQ_OK;
 }
 
+namespace kvq {
+namespace {
+
+// ng == 0: INT8 per-token cache; else INT4 with ng groups per row
+int attn_run(const char *fn, const float *q, uint32_t hq, uint32_t hkv, uint32_t T, int ng,
+             const KvCache &C, float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+             void *stream) {
+    if (!(softmax_scale == softmax_scale) || __builtin_isinf(softmax_scale))
+        return fail(KVQ_E_INVALID, "%s: softmax_scale is not finite", fn);
+    AttnPlan pl = attn_plan(hq, hkv, T);
+    float *partials = nullptr;
+    if (pl.nchunks > 1) {
+        if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
+            pl.bpc = (T + kAttnBlk - 1) / kAttnBlk;   // no workspace: one workgroup per KV head
+            pl.nchunks = 1;
+        } else {
+            partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
+        }
+    }
+    const uint32_t G = hq / hkv;
+    const unsigned grid = hkv * pl.nchunks;
+    hipStream_t s = as_stream(stream);
+#define KVQ_ATTN2(GM, NG)                                                                                     \
+    do {                                                                                                      \
+        attn_decode<GM, NG><<<grid, kAttnThreads, 0, s>>>(q, G, hkv, T, C, softmax_scale, pl.nchunks, pl.bpc, \
+                                                          out, partials);                                     \
+        if (pl.nchunks > 1) attn_merge<GM><<<hkv * G, kAttnD, 0, s>>>(partials, G, pl.nchunks, out);          \
+    } while (0)
+#define KVQ_ATTN(GM)                          \
+    do {                                      \
+        if (ng == 0) KVQ_ATTN2(GM, 0);        \
+        else if (ng == 1) KVQ_ATTN2(GM, 1);   \
+        else if (ng == 2) KVQ_ATTN2(GM, 2);   \
+        else KVQ_ATTN2(GM, 4);                \
+    } while (0)
+    switch (pl.gm) {
+        case 1: KVQ_ATTN(1); break;
+        case 2: KVQ_ATTN(2); break;
+        case 4: KVQ_ATTN(4); break;
+        default: KVQ_ATTN(8); break;
+    }
+#undef KVQ_ATTN
+#undef KVQ_ATTN2
+    return launch_status(fn);
+}
+
+}  // namespace
+}  // namespace kvq
+
 extern "C" int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads, uint32_t num_kv_heads,
                                     uint32_t num_tokens, uint32_t head_dim, const int8_t *k_codes,
                                     const float *k_scales, const int8_t *v_codes, const float *v_scales,
@@ -333,34 +461,32 @@ extern "C" int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads, uint32
     if (st) return st;
     st = check_ptrs(fn, {q, k_codes, k_scales, v_codes, v_scales, out});
     if (st) return st;
-    if (!(softmax_scale == softmax_scale) || __builtin_isinf(softmax_scale))
-        return fail(KVQ_E_INVALID, "%s: softmax_scale is not finite", fn);
-    AttnPlan pl = attn_plan(num_q_heads, num_kv_heads, num_tokens);
-    float *partials = nullptr;
-    if (pl.nchunks > 1) {
-        if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
-            pl.bpc = (num_tokens + kAttnBlk - 1) / kAttnBlk;   // no workspace: one workgroup per KV head
-            pl.nchunks = 1;
-        } else {
-            partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
-        }
-    }
-    const uint32_t G = num_q_heads / num_kv_heads;
-    const unsigned grid = num_kv_heads * pl.nchunks;
-    hipStream_t s = as_stream(stream);
-#define KVQ_ATTN(GM)                                                                                              \
-    do {                                                                                                          \
-        attn_decode_i8<GM><<<grid, kAttnThreads, 0, s>>>(q, G, num_kv_heads, num_tokens, k_codes, k_scales,       \
-                                                         v_codes, v_scales, softmax_scale, pl.nchunks, pl.bpc, out, \
-                                                         partials);                                               \
-        if (pl.nchunks > 1) attn_merge<GM><<<num_kv_heads * G, kAttnD, 0, s>>>(partials, G, pl.nchunks, out);    \
-    } while (0)
-    switch (pl.gm) {
-        case 1: KVQ_ATTN(1); break;
-        case 2: KVQ_ATTN(2); break;
-        case 4: KVQ_ATTN(4); break;
-        default: KVQ_ATTN(8); break;
-    }
-#undef KVQ_ATTN
-    return launch_status(fn);
+    KvCache C;
+    C.kc = reinterpret_cast<const uint8_t *>(k_codes);
+    C.vc = reinterpret_cast<const uint8_t *>(v_codes);
+    C.ks = k_scales; C.vs = v_scales;
+    C.kz = nullptr; C.vz = nullptr;
+    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, 0, C, softmax_scale, out, workspace,
+                    workspace_bytes, stream);
+}
+
+extern "C" int kvq_attn_decode_int4(const float *q, uint32_t num_q_heads, uint32_t num_kv_heads,
+                                    uint32_t num_tokens, uint32_t head_dim, uint32_t group_size,
+                                    const uint8_t *k_packed, const float *k_scales, const float *k_zeros,
+                                    const uint8_t *v_packed, const float *v_scales, const float *v_zeros,
+                                    float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+    const char *fn = "kvq_attn_decode_int4";
+    int st = check_attn(fn, num_q_heads, num_kv_heads, num_tokens, head_dim);
+    if (st) return st;
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(KVQ_E_INVALID, "%s: group_size=%u (supported: 32, 64, 128)", fn, group_size);
+    st = check_ptrs(fn, {q, k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros, out});
+    if (st) return st;
+    KvCache C;
+    C.kc = k_packed; C.vc = v_packed;
+    C.ks = k_scales; C.vs = v_scales;
+    C.kz = k_zeros; C.vz = v_zeros;
+    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, (int)(head_dim / group_size), C,
+                    softmax_scale, out, workspace, workspace_bytes, stream);
 }

@@ -242,3 +242,16 @@ def test_attn_decode_workspace_sizes(lib):
     assert lib.kvq_attn_decode_workspace_bytes(48, 8, 1000, 128, ctypes.byref(b)) == 0
     assert b.value == 4096 + 8 * 8 * 8 * 132 * 4
     assert lib.kvq_attn_decode_workspace_bytes(32, 8, 0, 128, ctypes.byref(b)) == _lib.KVQ_E_INVALID
+
+
+def test_attn_decode_int4_validation(lib):
+    f = ctypes.c_float(0.088)
+    ok = (FAKE, 32, 8, 4096, 128)
+    cache = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for gs in (16, 96, 256):
+        st, msg = _err(lib, "kvq_attn_decode_int4", *ok, gs, *cache, f, FAKE, None, 0, None)
+        assert st == _lib.KVQ_E_INVALID and f"group_size={gs}" in msg, msg
+    st, msg = _err(lib, "kvq_attn_decode_int4", *ok, 32, FAKE, FAKE, 0, FAKE, FAKE, FAKE, f, FAKE, None, 0, None)
+    assert st == _lib.KVQ_E_INVALID and "null" in msg, msg
+    st, msg = _err(lib, "kvq_attn_decode_int4", FAKE, 32, 8, 4096, 64, 32, *cache, f, FAKE, None, 0, None)
+    assert st == _lib.KVQ_E_INVALID and "head_dim=64" in msg, msg

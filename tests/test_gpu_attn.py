@@ -1,7 +1,7 @@
-"""GPU parity: decode attention over the INT8 per-token KV cache vs the
-oracle's fp64 definition, |gpu - ref| <= 1e-3 * sum_t p_t |v_t| per output,
-through the C ABI.  The caches are quantized on the CPU by the oracle's
-per-token quantizer (the same bytes the GPU quantizer writes)."""
+"""GPU parity: decode attention over the INT8 per-token and INT4 per-group
+KV caches vs the oracle's fp64 definition, |gpu - ref| <= 1e-3 * sum_t p_t
+|v_t| per output, through the C ABI.  The caches are quantized on the CPU by
+the oracle's quantizers (the same bytes the GPU quantizers write)."""
 import math
 
 import numpy as np
@@ -108,3 +108,65 @@ def test_workspace_shared_with_split_k_calls():
     for o, (ref, bound) in zip(outs, refs):
         assert np.max(np.abs(host(o).astype(np.float64) - ref) / np.maximum(bound, 1e-300)) <= RTOL
     _check(inp, 0.0884, _run(*inp, 0.0884), "attn after int4")
+
+
+# ---------------------------------------------------------------- INT4 ----
+
+def _cache4(t, hkv, hq, d, gs, seed, k_gain=1.0):
+    q, k, v = synth.attn_decode(t, hkv, hq, d, seed=seed)
+    k = k * np.float32(k_gain)
+    rows, ng = t * hkv, d // gs
+    out = [q]
+    for a in (k, v):
+        p, s, z = _oracle.kv_int4_quant(a.reshape(rows, d), gs)
+        out += [p.reshape(t, hkv, d // 2), s.reshape(t, hkv, ng), z.reshape(t, hkv, ng)]
+    return out
+
+
+def _run4(inp, gs, scale, use_workspace=True):
+    q, kp, ks, kz, vp, vs, vz = inp
+    o = api.attn_decode_int4(dev(q), gs, dev(kp), dev(ks), dev(kz), dev(vp), dev(vs), dev(vz), scale,
+                             use_workspace=use_workspace)
+    torch.cuda.synchronize()
+    return host(o)
+
+
+def _check4(inp, gs, scale, got, what):
+    q, kp, ks, kz, vp, vs, vz = inp
+    t, hkv, half = kp.shape
+    ref, bound = _oracle.attn_decode_int4(q, kp, ks, kz, vp, vs, vz, t, hkv, 2 * half, gs, scale)
+    worst = float((np.abs(got.astype(np.float64) - ref) / np.maximum(bound, 1e-30)).max())
+    print(f"{what}: max |err|/sum p|v| = {worst:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), what
+    assert worst <= RTOL, what
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+def test_int4_decode_workload(gs):
+    print_case("attn int4 4096x8 hq32", gs)
+    inp = _cache4(4096, 8, 32, 128, gs, seed=11)
+    a = _run4(inp, gs, 0.0884)
+    _check4(inp, gs, 0.0884, a, f"int4 gs={gs}")
+    np.testing.assert_array_equal(a.view(np.uint32), _run4(inp, gs, 0.0884).view(np.uint32))
+    _check4(inp, gs, 0.0884, _run4(inp, gs, 0.0884, use_workspace=False), f"int4 gs={gs} no workspace")
+
+
+@pytest.mark.parametrize("t", [1, 3, 128, 129, 1000])
+@pytest.mark.parametrize("g", [1, 3, 8])
+def test_int4_shapes(t, g):
+    print_case("attn int4 shapes", t, g)
+    inp = _cache4(t, 2, 2 * g, 128, 32, seed=600 + t + g)
+    _check4(inp, 32, 0.0884, _run4(inp, 32, 0.0884), f"int4 T={t} G={g}")
+
+
+@pytest.mark.parametrize("gain,scale", [(1.0, 1.0), (8.0, 0.5), (0.0, 0.0884)])
+def test_int4_score_ranges(gain, scale):
+    print_case("attn int4 scores", gain, scale)
+    inp = _cache4(1500, 2, 8, 128, 64, seed=700, k_gain=gain)
+    _check4(inp, 64, scale, _run4(inp, 64, scale), f"int4 gain={gain} scale={scale}")
+
+
+def test_int4_long_cache():
+    print_case("attn int4 long")
+    inp = _cache4(32768, 1, 4, 128, 32, seed=800)
+    _check4(inp, 32, 0.0884, _run4(inp, 32, 0.0884), "int4 T=32768")
