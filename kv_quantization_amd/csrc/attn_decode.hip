@@ -77,14 +77,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     // (INT4: they lie in group l8 / (16 / (D / NG)) ... one group, since a
     // group holds a multiple of 16 values)
     const uint32_t l8 = lane & 7, tk = lane >> 3;
+    // (buffer loads: padding heads read zeros without a branch, so the
+    // cache loads below are issued before the query arrives)
     float qr[GM][16], qsum[GM];
+    const rsrc_t rq = make_rsrc(q, hkv * G * D * 4);
 #pragma unroll
     for (int j = 0; j < GM; ++j) {
-        const bool live = (uint32_t)j < G;
-        const f32x4 *qp = reinterpret_cast<const f32x4 *>(q + (size_t)(g * G + (live ? j : 0)) * D + 16 * l8);
+        const uint32_t qo = (uint32_t)j < G ? ((g * G + j) * D + 16 * l8) * 4 : kOffNone;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-            const f32x4 v = live ? qp[e4] : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 16 * e4, 0));
             qr[j][4 * e4] = v.x; qr[j][4 * e4 + 1] = v.y; qr[j][4 * e4 + 2] = v.z; qr[j][4 * e4 + 3] = v.w;
         }
         float sq = 0.f;
@@ -331,17 +333,21 @@ __global__ __launch_bounds__(kAttnD) void attn_merge(const float *__restrict__ p
     constexpr int D = kAttnD;
     constexpr uint32_t kRecD = D + 4;
     const uint32_t g = blockIdx.x / G, j = blockIdx.x % G, d = threadIdx.x, lane = d & 63;
-    const size_t rec0 = (size_t)g * nchunks * GM + j;   // record of chunk c: (rec0 + c * GM) * kRecD
+    // this head's records: chunk c at (c * GM + j) * kRecD floats (buffer
+    // loads: chunks past the end read zeros without a branch)
+    const rsrc_t rp = make_rsrc(partials + (size_t)g * nchunks * GM * kRecD, nchunks * GM * kRecD * 4);
     float M = -__builtin_inff(), L = 0.f, O = 0.f;
     for (uint32_t c0 = 0; c0 < nchunks; c0 += 64) {
         float ov[64];
 #pragma unroll
-        for (int u = 0; u < 64; ++u)
-            ov[u] = c0 + u < nchunks ? partials[(rec0 + (size_t)(c0 + u) * GM) * kRecD + d] : 0.f;
+        for (int u = 0; u < 64; ++u) {
+            const uint32_t off = c0 + u < nchunks ? (((c0 + u) * GM + j) * kRecD + d) * 4 : kOffNone;
+            ov[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 0));
+        }
         const bool in = c0 + lane < nchunks;
-        const float *rl = partials + (rec0 + (size_t)(c0 + (in ? lane : 0)) * GM) * kRecD;
-        const float mc = in ? rl[D] : -__builtin_inff();
-        const float lc = in ? rl[D + 1] : 0.f;
+        const uint32_t ro = in ? (((c0 + lane) * GM + j) * kRecD + D) * 4 : kOffNone;
+        const float mc = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, ro, 0, 0)) : -__builtin_inff();
+        const float lc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, ro, 4, 0));
         const float mn = fmaxf(M, team_max<64>(mc));
         const float a = expf(M - mn);   // rescales earlier batches (0 for the first)
         const float bw = in ? expf(mc - mn) : 0.f;
