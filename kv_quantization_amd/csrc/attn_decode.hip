@@ -390,6 +390,7 @@ int check_attn(const char *fn, uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D
         return fail(KVQ_E_INVALID, "%s: num_q_heads=%u is not 1..8 times num_kv_heads=%u", fn, hq, hkv);
     if (D != kAttnD) return fail(KVQ_E_INVALID, "%s: head_dim=%u (supported: 128)", fn, D);
     if ((uint64_t)T * hkv * D >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: cache larger than 2 GiB", fn);
+    if ((uint64_t)hq * D * 4 >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: queries larger than 2 GiB", fn);
     return KVQ_OK;
 }
 

@@ -218,6 +218,7 @@ def _attn(hq=32, hkv=8, t=4096, d=128, q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAK
     (_attn(hq=72, hkv=8), "not 1..8 times"),
     (_attn(d=64), "head_dim=64"),
     (_attn(t=1 << 21, hkv=8), "2 GiB"),
+    (_attn(hq=1 << 23, hkv=1 << 20, t=1), "queries larger than 2 GiB"),
     (_attn(q=0), "null"),
     (_attn(vs=0), "null"),
     (_attn(kc=MISALIGNED), "aligned"),
