@@ -40,7 +40,12 @@ namespace kvq {
 namespace {
 
 constexpr int kAttnD = 128;       // head_dim
-constexpr int kAttnBlk = 128;     // tokens per block: 4 waves x 32
+constexpr int kAttnBlk = 128;     // tokens per block
+constexpr int kTpw = kAttnBlk / 4;    // scores: tokens per wave
+constexpr int kSlots = kTpw / 8;      // scores: 8-token load slots per wave
+constexpr int kWpb = kAttnBlk / 64;   // softmax: waves over one head's tokens
+constexpr int kHg = 4 / kWpb;         // softmax: head groups (heads j with j % kHg == group)
+constexpr int kTpg = kAttnBlk / 8;    // values: tokens per thread group
 constexpr int kAttnThreads = 256;
 constexpr uint32_t kAttnTargetWgs = 256;
 
@@ -65,7 +70,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     constexpr uint32_t RB = I4 ? D / 2 : D;          // code bytes per row
     __shared__ float s_w[kAttnBlk][GM];              // scores; INT8: then p * v_scale
     __shared__ float s_wz[I4 ? kAttnBlk : 1][GM][I4 ? 2 * NGS : 1];   // INT4: p * s, p * s * z per group
-    __shared__ float s_red[2][GM][2];                // per wave of a head parity: block max, block sum
+    __shared__ float s_red[kWpb][GM][2];             // per wave of a head group: block max, block sum
     __shared__ float s_o[8][GM][D];                  // the 8 token groups' outputs
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     const rsrc_t rkz = make_rsrc(I4 ? C.kz : C.ks, rows * NGS * 4), rvz = make_rsrc(I4 ? C.vz : C.vs, rows * NGS * 4);
     const uint32_t tg = tid >> 5, e4 = tid & 31;          // values: token group, 4-dim slice
     const uint32_t vgrp = I4 ? (4 * e4) / (D / NGS) : 0;  // INT4 group of this thread's value dims
-    const uint32_t tt = tid & (kAttnBlk - 1), hp = tid >> 7;   // softmax: token, head parity
+    const uint32_t tt = tid % kAttnBlk, hp = tid / kAttnBlk;   // softmax: token, head group
 
     float o[GM][4], oz[GM];
     float m_run[GM], l_run[GM];
@@ -118,11 +123,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     for (uint32_t blk = blk0; blk < blk1; ++blk) {
         const uint32_t t0 = blk * kAttnBlk;
         // -- loads of the block (out-of-range tokens read zeros)
-        u32x4 kraw[4];
-        float ksc[4], kzr[4];
+        u32x4 kraw[kSlots];
+        float ksc[kSlots], kzr[kSlots];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t t = t0 + wv * 32 + i * 8 + tk;
+        for (int i = 0; i < kSlots; ++i) {
+            const uint32_t t = t0 + wv * kTpw + i * 8 + tk;
             const uint32_t row = t * hkv + g;
             if (I4) {
                 const u32x2 w2 = __builtin_amdgcn_raw_buffer_load_b64(rk, t < T ? row * RB + 8 * l8 : kOffNone, 0, 0);
@@ -136,10 +141,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
                 kzr[i] = 0.f;
             }
         }
-        uint32_t vraw[16];
+        uint32_t vraw[kTpg];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const uint32_t t = t0 + tg * 16 + u;
+        for (int u = 0; u < kTpg; ++u) {
+            const uint32_t t = t0 + tg * kTpg + u;
             const uint32_t row = t * hkv + g;
             if (I4)
                 vraw[u] = __builtin_amdgcn_raw_buffer_load_b16(rv, t < T ? row * RB + 2 * e4 : kOffNone, 0, 0);
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 
         // -- 1. scores
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kSlots; ++i) {
             float x[16];
             if (I4) {
 #pragma unroll
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 #pragma unroll
                     for (int b = 0; b < 4; ++b) x[4 * w + b] = (float)(int8_t)(kraw[i][w] >> (8 * b));
             }
-            const uint32_t lt = wv * 32 + i * 8 + tk;
+            const uint32_t lt = wv * kTpw + i * 8 + tk;
             const bool valid = t0 + lt < T;
 #pragma unroll
             for (int j = 0; j < GM; ++j) {
@@ -188,12 +193,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
         }
         __syncthreads();
 
-        // -- 2. softmax of the block: thread (token tt, head parity hp) owns heads hp, hp + 2, ...
-        const uint32_t half = (tid >> 6) & 1;
+        // -- 2. softmax of the block: thread (token tt, head group hp) owns heads hp, hp + kHg, ...
+        const uint32_t half = (tid / 64) % kWpb;
 #pragma unroll
         for (int j = 0; j < GM; ++j) {
-            if ((uint32_t)(j & 1) != hp && GM > 1) continue;
-            if (GM == 1 && hp) continue;
+            if ((uint32_t)(j % kHg) != hp) continue;
             const float bm = team_max<64>(s_w[tt][j]);
             if (lane == 0) s_red[half][j][0] = bm;
         }
@@ -201,15 +205,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
         float alpha[GM];
 #pragma unroll
         for (int j = 0; j < GM; ++j) {
-            const float bm = fmaxf(s_red[0][j][0], s_red[1][j][0]);
+            float bm = s_red[0][j][0];
+#pragma unroll
+            for (int w = 1; w < kWpb; ++w) bm = fmaxf(bm, s_red[w][j][0]);
             const float mn = fmaxf(m_run[j], bm);
             alpha[j] = expf(m_run[j] - mn);   // 0 for the first block (m_run = -inf)
             m_run[j] = mn;
         }
 #pragma unroll
         for (int j = 0; j < GM; ++j) {
-            if ((uint32_t)(j & 1) != hp && GM > 1) continue;
-            if (GM == 1 && hp) continue;
+            if ((uint32_t)(j % kHg) != hp) continue;
             const float p = expf(s_w[tt][j] - m_run[j]);   // 0 for tokens past the end
             if (I4) {
 #pragma unroll
@@ -226,7 +231,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < GM; ++j) l_run[j] = l_run[j] * alpha[j] + (s_red[0][j][1] + s_red[1][j][1]);
+        for (int j = 0; j < GM; ++j) {
+            float bs = s_red[0][j][1];
+#pragma unroll
+            for (int w = 1; w < kWpb; ++w) bs += s_red[w][j][1];
+            l_run[j] = l_run[j] * alpha[j] + bs;
+        }
 
         // -- 3. values: INT8 sum_t (p v_scale) code; INT4 sum_t (p s) code - sum_t (p s z)
 #pragma unroll
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
             for (int e = 0; e < 4; ++e) o[j][e] *= alpha[j];
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < kTpg; ++u) {
             float cv[4];
             if (I4) {
 #pragma unroll
@@ -249,10 +259,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
             for (int j = 0; j < GM; ++j) {
                 float w;
                 if (I4) {
-                    w = s_wz[I4 ? tg * 16 + u : 0][j][2 * vgrp];
-                    oz[j] += s_wz[I4 ? tg * 16 + u : 0][j][I4 ? 2 * vgrp + 1 : 0];
+                    w = s_wz[I4 ? tg * kTpg + u : 0][j][2 * vgrp];
+                    oz[j] += s_wz[I4 ? tg * kTpg + u : 0][j][I4 ? 2 * vgrp + 1 : 0];
                 } else {
-                    w = s_w[tg * 16 + u][j];
+                    w = s_w[tg * kTpg + u][j];
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[j][e] = __builtin_fmaf(w, cv[e], o[j][e]);
