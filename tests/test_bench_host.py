@@ -1,0 +1,62 @@
+"""Host-side checks of bench.py that need no GPU: the workload tables, the
+roofline arithmetic, the guard on the stored traffic figure, and the refusal
+of more than one GPU."""
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+sys.path.insert(0, str(ROOT))
+import bench  # noqa: E402
+
+
+def test_tables_have_unique_names_and_positive_bytes():
+    step, extra = bench.kernel_table(), bench.extra_table()
+    names = [r[0] for r in step + extra]
+    assert len(names) == len(set(names))
+    for name, nbytes, flops, kind in step + extra:
+        assert nbytes > 0 and flops >= 0 and kind in ("hbm", "fp8", "fp16"), name
+        if kind != "hbm":
+            assert flops > 0, name
+
+
+def test_decode_step_bytes():
+    # the KV INT8 quantizer moves x (fp32), its codes and one scale per token
+    row = {r[0]: r for r in bench.kernel_table()}["kv_int8_quant"]
+    assert row[1] == bench.KV_T * bench.KV_D * 5 + bench.KV_T * 4
+    # the attention call reads both caches once (codes and scales) plus q and out
+    a = {r[0]: r for r in bench.extra_table()}[f"attn_decode_int8_T{bench.ATTN_T}"]
+    rows = bench.ATTN_T * bench.ATTN_HKV
+    assert a[1] == 2 * rows * (bench.ATTN_D + 4) + 2 * bench.ATTN_HQ * bench.ATTN_D * 4
+
+
+def test_roofline_picks_the_binding_roof():
+    # 1 GB in 1 ms: 1 TB/s of 8 -> HBM-bound, frac 0.125
+    r = bench.roofline_for("x", 10**9, 0, "hbm", 1e-3)
+    assert r["bound"] == "hbm" and r["achieved"] == 1000.0 and r["frac"] == 0.125
+    # 1 MB and 1e13 flop in 10 ms: far above the FP8 ridge -> MFMA-bound
+    r = bench.roofline_for("y", 10**6, 10**13, "fp8", 1e-2)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["achieved"] == 1000.0
+    assert r["frac"] == round(1000.0 / bench.FP8_PEAK_TFLOPS, 4)
+
+
+def test_stored_traffic_only_for_the_measured_source(tmp_path):
+    assert bench.measured_traffic(bench.TRAFFIC["kernel"]) == bench.TRAFFIC["bytes"]
+    assert bench.measured_traffic("kv_int8_quant") is None
+    # comments do not change the digest, code does
+    src = (ROOT / bench.TRAFFIC["source"]).read_text()
+    assert bench.code_digest(ROOT / bench.TRAFFIC["source"]) == bench.TRAFFIC["sha256"]
+    probe = tmp_path / "probe.hip"
+    probe.write_text(src + "\n// a comment\n")
+    assert bench.code_digest(probe) == bench.TRAFFIC["sha256"]
+    probe.write_text(src + "\nint extra;\n")
+    assert bench.code_digest(probe) != bench.TRAFFIC["sha256"]
+
+
+@pytest.mark.parametrize("n", ["2", "8"])
+def test_more_than_one_gpu_is_refused(n):
+    p = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", n], capture_output=True, text=True,
+                       timeout=120)
+    assert p.returncode == 2 and "one GPU" in p.stderr
