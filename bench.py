@@ -16,9 +16,11 @@ replays K step graphs, rotating over enough input sets (>= 512 MB in total)
 that no step finds its data in the 256 MB MALL.  value = sum of the
 algorithmic bytes of all kernels / step time.  Each kernel is also timed
 alone (a graph of R launches rotating over the sets, HIP events on the launch
-stream) for the per-kernel breakdown and the roofline of the dominant kernel.
+stream, median of 5 replays) for the per-kernel breakdown and the roofline of
+the dominant kernel.
 
-Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 exits: every kernel here runs on
+one GPU.
 """
 from __future__ import annotations
 
@@ -448,17 +450,21 @@ def main():
     reps = max(nsets, args.kernel_reps // nsets * nsets)
     timed = [(name, launch, ki) for ki, name in enumerate(names)]
     timed += [(r[0], xlaunch, ki) for ki, r in enumerate(xtable)]
-    def per_launch(fns):
+    def per_launch(fns, replays=5):
+        """Seconds per launch: one graph of the launches, replayed once to
+        warm up, then the median of `replays` timed replays."""
         g = capture(torch, fns, stream)
         with torch.cuda.stream(stream):
             g.replay()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            g.replay()
-            b.record(stream)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(replays)]
+            for a, b in ev:
+                a.record(stream)
+                g.replay()
+                b.record(stream)
         torch.cuda.synchronize()
         del g
-        return a.elapsed_time(b) / len(fns) / 1e3                 # seconds per launch
+        return sorted(a.elapsed_time(b) for a, b in ev)[replays // 2] / len(fns) / 1e3
 
     for name, lset, ki in timed:
         per_kernel[name] = per_launch([lset[r % nsets][ki][1] for r in range(reps)])
