@@ -305,7 +305,8 @@ int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k,
  *             per-token quantizer's output for num_tokens*num_kv_heads rows)
  *   k_scales, v_scales: fp32 [num_tokens][num_kv_heads]
  *   out:      fp32 [num_q_heads][head_dim]
- * head_dim is 128; num_q_heads is 1..8 times num_kv_heads; num_tokens >= 1.
+ * head_dim is 64, 128 or 256; num_q_heads is 1..8 times num_kv_heads;
+ * num_tokens >= 1.
  * All pointers are device memory, 16-byte aligned, owned by the caller.
  * workspace: NULL, or at least kvq_attn_decode_workspace_bytes() (the
  * shared workspace of the calls above: the per-chunk partial results go
@@ -328,7 +329,8 @@ int kvq_attn_decode_workspace_bytes(uint32_t num_q_heads, uint32_t num_kv_heads,
 
 /* The same attention over the [KVQ] "INT4 Per-Group Quantization" cache:
  * each (token, KV head) row of head_dim values holds head_dim / group_size
- * groups (group_size 32, 64 or 128), dequantized as code * scale - zero *
+ * groups (group_size 32, 64 or 128, at most head_dim), dequantized as
+ * code * scale - zero *
  * scale.  k_packed, v_packed: uint8 [num_tokens][num_kv_heads][head_dim/2],
  * two codes per byte, even element in the low nibble (the quantizer's output
  * for num_tokens*num_kv_heads rows); scales and zeros: fp32

@@ -39,13 +39,11 @@
 namespace kvq {
 namespace {
 
-constexpr int kAttnD = 128;       // head_dim
 constexpr int kAttnBlk = 128;     // tokens per block
 constexpr int kTpw = kAttnBlk / 4;    // scores: tokens per wave
-constexpr int kSlots = kTpw / 8;      // scores: 8-token load slots per wave
 constexpr int kWpb = kAttnBlk / 64;   // softmax: waves over one head's tokens
 constexpr int kHg = 4 / kWpb;         // softmax: head groups (heads j with j % kHg == group)
-constexpr int kTpg = kAttnBlk / 8;    // values: tokens per thread group
+
 constexpr int kAttnThreads = 256;
 constexpr uint32_t kAttnTargetWgs = 256;
 
@@ -59,19 +57,25 @@ struct KvCache {
     const float *kz, *vz;   // INT4 zeros [rows][NG]
 };
 
-template <int GM, int NG>
+template <int D, int GM, int NG>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restrict__ q, uint32_t G, uint32_t hkv,
                                                             uint32_t T, KvCache C, float sm_scale, uint32_t nchunks,
                                                             uint32_t bpc, float *__restrict__ out,
                                                             float *__restrict__ partials) {
-    constexpr int D = kAttnD;
+    constexpr int LPT = D / 16;               // scores: lanes per token (16 dims each)
+    constexpr int TPI = kWave / LPT;          // scores: tokens per wave load
+    constexpr int SLOTS = kTpw / TPI;         // scores: loads per lane per block
+    constexpr int TPR = D / 4;                // values: threads per token row (4 dims each)
+    constexpr int NTG = kAttnThreads / TPR;   // values: token groups
+    constexpr int TPG = kAttnBlk / NTG;       // values: tokens per group
+    static_assert(D == 64 || D == 128 || D == 256, "head_dim");
     constexpr bool I4 = NG > 0;
     constexpr int NGS = I4 ? NG : 1;                 // scale slots per row
     constexpr uint32_t RB = I4 ? D / 2 : D;          // code bytes per row
     __shared__ float s_w[kAttnBlk][GM];              // scores; INT8: then p * v_scale
     __shared__ float s_wz[I4 ? kAttnBlk : 1][GM][I4 ? 2 * NGS : 1];   // INT4: p * s, p * s * z per group
     __shared__ float s_red[kWpb][GM][2];             // per wave of a head group: block max, block sum
-    __shared__ float s_o[8][GM][D];                  // the 8 token groups' outputs
+    __shared__ float s_o[NTG][GM][D];                // the token groups' outputs
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint32_t g = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     // query rows of this head group, the 16 dims of this lane's key slice
     // (INT4: they lie in group l8 / (16 / (D / NG)) ... one group, since a
     // group holds a multiple of 16 values)
-    const uint32_t l8 = lane & 7, tk = lane >> 3;
+    const uint32_t l8 = lane % LPT, tk = lane / LPT;
     // (buffer loads: padding heads read zeros without a branch, so the
     // cache loads below are issued before the query arrives)
     float qr[GM][16], qsum[GM];
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     const rsrc_t rk = make_rsrc(C.kc, rows * RB), rv = make_rsrc(C.vc, rows * RB);
     const rsrc_t rks = make_rsrc(C.ks, rows * NGS * 4), rvs = make_rsrc(C.vs, rows * NGS * 4);
     const rsrc_t rkz = make_rsrc(I4 ? C.kz : C.ks, rows * NGS * 4), rvz = make_rsrc(I4 ? C.vz : C.vs, rows * NGS * 4);
-    const uint32_t tg = tid >> 5, e4 = tid & 31;          // values: token group, 4-dim slice
+    const uint32_t tg = tid / TPR, e4 = tid % TPR;        // values: token group, 4-dim slice
     const uint32_t vgrp = I4 ? (4 * e4) / (D / NGS) : 0;  // INT4 group of this thread's value dims
     const uint32_t tt = tid % kAttnBlk, hp = tid / kAttnBlk;   // softmax: token, head group
 
@@ -123,11 +127,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     for (uint32_t blk = blk0; blk < blk1; ++blk) {
         const uint32_t t0 = blk * kAttnBlk;
         // -- loads of the block (out-of-range tokens read zeros)
-        u32x4 kraw[kSlots];
-        float ksc[kSlots], kzr[kSlots];
+        u32x4 kraw[SLOTS];
+        float ksc[SLOTS], kzr[SLOTS];
 #pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            const uint32_t t = t0 + wv * kTpw + i * 8 + tk;
+        for (int i = 0; i < SLOTS; ++i) {
+            const uint32_t t = t0 + wv * kTpw + i * TPI + tk;
             const uint32_t row = t * hkv + g;
             if (I4) {
                 const u32x2 w2 = __builtin_amdgcn_raw_buffer_load_b64(rk, t < T ? row * RB + 8 * l8 : kOffNone, 0, 0);
@@ -141,10 +145,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
                 kzr[i] = 0.f;
             }
         }
-        uint32_t vraw[kTpg];
+        uint32_t vraw[TPG];
 #pragma unroll
-        for (int u = 0; u < kTpg; ++u) {
-            const uint32_t t = t0 + tg * kTpg + u;
+        for (int u = 0; u < TPG; ++u) {
+            const uint32_t t = t0 + tg * TPG + u;
             const uint32_t row = t * hkv + g;
             if (I4)
                 vraw[u] = __builtin_amdgcn_raw_buffer_load_b16(rv, t < T ? row * RB + 2 * e4 : kOffNone, 0, 0);
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 
         // -- 1. scores
 #pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
+        for (int i = 0; i < SLOTS; ++i) {
             float x[16];
             if (I4) {
 #pragma unroll
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 #pragma unroll
                     for (int b = 0; b < 4; ++b) x[4 * w + b] = (float)(int8_t)(kraw[i][w] >> (8 * b));
             }
-            const uint32_t lt = wv * kTpw + i * 8 + tk;
+            const uint32_t lt = wv * kTpw + i * TPI + tk;
             const bool valid = t0 + lt < T;
 #pragma unroll
             for (int j = 0; j < GM; ++j) {
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
                 // INT8: scale the row's integer dot product once after the
                 // sum; INT4: each lane's 16 values share one group
                 if (I4) d = ksc[i] * __builtin_fmaf(-kzr[i], qsum[j], d);
-                d = team_sum<8>(d);
+                d = team_sum<LPT>(d);
                 const float s = valid ? (I4 ? d : d * ksc[i]) * sm_scale : -__builtin_inff();
                 if (l8 == 0) s_w[lt][j] = s;
             }
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
             for (int e = 0; e < 4; ++e) o[j][e] *= alpha[j];
         }
 #pragma unroll
-        for (int u = 0; u < kTpg; ++u) {
+        for (int u = 0; u < TPG; ++u) {
             float cv[4];
             if (I4) {
 #pragma unroll
@@ -259,10 +263,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
             for (int j = 0; j < GM; ++j) {
                 float w;
                 if (I4) {
-                    w = s_wz[I4 ? tg * kTpg + u : 0][j][2 * vgrp];
-                    oz[j] += s_wz[I4 ? tg * kTpg + u : 0][j][I4 ? 2 * vgrp + 1 : 0];
+                    w = s_wz[I4 ? tg * TPG + u : 0][j][2 * vgrp];
+                    oz[j] += s_wz[I4 ? tg * TPG + u : 0][j][I4 ? 2 * vgrp + 1 : 0];
                 } else {
-                    w = s_w[tg * kTpg + u][j];
+                    w = s_w[tg * TPG + u][j];
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[j][e] = __builtin_fmaf(w, cv[e], o[j][e]);
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
         if (idx < (uint32_t)kOut) {
             const uint32_t j = idx / D, d = idx % D;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) a += s_o[x][j][d];
+            for (int x = 0; x < NTG; ++x) a += s_o[x][j][d];
         }
         ov[r] = a;
     }
@@ -337,10 +341,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 // and sum, and fixed-order DPP reductions give the batch max, the chunk
 // weights exp(m_c - M) and the weighted sum of the sums, so the chunks are
 // added in order and the result does not depend on launch timing.
-template <int GM>
-__global__ __launch_bounds__(kAttnD) void attn_merge(const float *__restrict__ partials, uint32_t G,
-                                                     uint32_t nchunks, float *__restrict__ out) {
-    constexpr int D = kAttnD;
+template <int D, int GM>
+__global__ __launch_bounds__(D) void attn_merge(const float *__restrict__ partials, uint32_t G, uint32_t nchunks,
+                                                float *__restrict__ out) {
     constexpr uint32_t kRecD = D + 4;
     const uint32_t g = blockIdx.x / G, j = blockIdx.x % G, d = threadIdx.x, lane = d & 63;
     // this head's records: chunk c at (c * GM + j) * kRecD floats (buffer
@@ -378,7 +381,7 @@ struct AttnPlan {
 uint32_t attn_gm(uint32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
 // ~256 workgroups: split each head's tokens into chunks of whole 128-token blocks
-AttnPlan attn_plan(uint32_t hq, uint32_t hkv, uint32_t T) {
+AttnPlan attn_plan(uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D) {
     AttnPlan pl;
     pl.gm = attn_gm(hq / hkv);
     const uint32_t nblk = (T + kAttnBlk - 1) / kAttnBlk;
@@ -388,7 +391,7 @@ AttnPlan attn_plan(uint32_t hq, uint32_t hkv, uint32_t T) {
     pl.bpc = (nblk + want - 1) / want;
     pl.nchunks = (nblk + pl.bpc - 1) / pl.bpc;
     pl.ws_bytes = pl.nchunks > 1
-                      ? KVQ_WORKSPACE_COUNTER_BYTES + (size_t)hkv * pl.nchunks * pl.gm * (kAttnD + 4) * 4
+                      ? KVQ_WORKSPACE_COUNTER_BYTES + (size_t)hkv * pl.nchunks * pl.gm * (D + 4) * 4
                       : 0;
     return pl;
 }
@@ -398,7 +401,8 @@ int check_attn(const char *fn, uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D
         return fail(KVQ_E_INVALID, "%s: num_q_heads=%u num_kv_heads=%u num_tokens=%u (want all > 0)", fn, hq, hkv, T);
     if (hq % hkv || hq / hkv > 8)
         return fail(KVQ_E_INVALID, "%s: num_q_heads=%u is not 1..8 times num_kv_heads=%u", fn, hq, hkv);
-    if (D != kAttnD) return fail(KVQ_E_INVALID, "%s: head_dim=%u (supported: 128)", fn, D);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(KVQ_E_INVALID, "%s: head_dim=%u (supported: 64, 128, 256)", fn, D);
     if ((uint64_t)T * hkv * D >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: cache larger than 2 GiB", fn);
     if ((uint64_t)hq * D * 4 >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: queries larger than 2 GiB", fn);
     return KVQ_OK;
@@ -415,20 +419,54 @@ extern "C" int kvq_attn_decode_workspace_bytes(uint32_t num_q_heads, uint32_t nu
     *bytes = 0;
     const int st = check_attn("kvq_attn_decode_workspace_bytes", num_q_heads, num_kv_heads, num_tokens, head_dim);
     if (st) return st;
-    *bytes = attn_plan(num_q_heads, num_kv_heads, num_tokens).ws_bytes;
+    *bytes = attn_plan(num_q_heads, num_kv_heads, num_tokens, head_dim).ws_bytes;
     return KVQ_OK;
 }
 
 namespace kvq {
 namespace {
 
-// ng == 0: INT8 per-token cache; else INT4 with ng groups per row
-int attn_run(const char *fn, const float *q, uint32_t hq, uint32_t hkv, uint32_t T, int ng,
+template <int D, int GM, int NG>
+void attn_launch(unsigned grid, const float *q, uint32_t G, uint32_t hkv, uint32_t T, const KvCache &C, float sc,
+                 const AttnPlan &pl, float *out, float *partials, hipStream_t s) {
+    attn_decode<D, GM, NG><<<grid, kAttnThreads, 0, s>>>(q, G, hkv, T, C, sc, pl.nchunks, pl.bpc, out, partials);
+    if (pl.nchunks > 1) attn_merge<D, GM><<<hkv * G, D, 0, s>>>(partials, G, pl.nchunks, out);
+}
+
+template <int D, int NG>
+void attn_by_group(unsigned grid, const float *q, uint32_t G, uint32_t hkv, uint32_t T, const KvCache &C, float sc,
+                   const AttnPlan &pl, float *out, float *partials, hipStream_t s) {
+    switch (pl.gm) {
+        case 1: attn_launch<D, 1, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
+        case 2: attn_launch<D, 2, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
+        case 4: attn_launch<D, 4, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
+        default: attn_launch<D, 8, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
+    }
+}
+
+// ng == 0: INT8 per-token cache; else INT4 with ng groups of 32..128 values per row
+template <int D>
+void attn_by_format(int ng, unsigned grid, const float *q, uint32_t G, uint32_t hkv, uint32_t T, const KvCache &C,
+                    float sc, const AttnPlan &pl, float *out, float *partials, hipStream_t s) {
+    if (ng == 0) attn_by_group<D, 0>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
+    if constexpr (D <= 128) {
+        if (ng == 1) attn_by_group<D, 1>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
+    }
+    if (ng == 2) attn_by_group<D, 2>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
+    if constexpr (D >= 128) {
+        if (ng == 4) attn_by_group<D, 4>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
+    }
+    if constexpr (D == 256) {
+        if (ng == 8) attn_by_group<D, 8>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
+    }
+}
+
+int attn_run(const char *fn, const float *q, uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D, int ng,
              const KvCache &C, float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
              void *stream) {
     if (!(softmax_scale == softmax_scale) || __builtin_isinf(softmax_scale))
         return fail(KVQ_E_INVALID, "%s: softmax_scale is not finite", fn);
-    AttnPlan pl = attn_plan(hq, hkv, T);
+    AttnPlan pl = attn_plan(hq, hkv, T, D);
     float *partials = nullptr;
     if (pl.nchunks > 1) {
         if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
@@ -441,27 +479,9 @@ int attn_run(const char *fn, const float *q, uint32_t hq, uint32_t hkv, uint32_t
     const uint32_t G = hq / hkv;
     const unsigned grid = hkv * pl.nchunks;
     hipStream_t s = as_stream(stream);
-#define KVQ_ATTN2(GM, NG)                                                                                     \
-    do {                                                                                                      \
-        attn_decode<GM, NG><<<grid, kAttnThreads, 0, s>>>(q, G, hkv, T, C, softmax_scale, pl.nchunks, pl.bpc, \
-                                                          out, partials);                                     \
-        if (pl.nchunks > 1) attn_merge<GM><<<hkv * G, kAttnD, 0, s>>>(partials, G, pl.nchunks, out);          \
-    } while (0)
-#define KVQ_ATTN(GM)                          \
-    do {                                      \
-        if (ng == 0) KVQ_ATTN2(GM, 0);        \
-        else if (ng == 1) KVQ_ATTN2(GM, 1);   \
-        else if (ng == 2) KVQ_ATTN2(GM, 2);   \
-        else KVQ_ATTN2(GM, 4);                \
-    } while (0)
-    switch (pl.gm) {
-        case 1: KVQ_ATTN(1); break;
-        case 2: KVQ_ATTN(2); break;
-        case 4: KVQ_ATTN(4); break;
-        default: KVQ_ATTN(8); break;
-    }
-#undef KVQ_ATTN
-#undef KVQ_ATTN2
+    if (D == 64) attn_by_format<64>(ng, grid, q, G, hkv, T, C, softmax_scale, pl, out, partials, s);
+    else if (D == 128) attn_by_format<128>(ng, grid, q, G, hkv, T, C, softmax_scale, pl, out, partials, s);
+    else attn_by_format<256>(ng, grid, q, G, hkv, T, C, softmax_scale, pl, out, partials, s);
     return launch_status(fn);
 }
 
@@ -483,7 +503,7 @@ extern "C" int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads, uint32
     C.vc = reinterpret_cast<const uint8_t *>(v_codes);
     C.ks = k_scales; C.vs = v_scales;
     C.kz = nullptr; C.vz = nullptr;
-    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, 0, C, softmax_scale, out, workspace,
+    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, head_dim, 0, C, softmax_scale, out, workspace,
                     workspace_bytes, stream);
 }
 
@@ -496,14 +516,14 @@ extern "C" int kvq_attn_decode_int4(const float *q, uint32_t num_q_heads, uint32
     const char *fn = "kvq_attn_decode_int4";
     int st = check_attn(fn, num_q_heads, num_kv_heads, num_tokens, head_dim);
     if (st) return st;
-    if (group_size != 32 && group_size != 64 && group_size != 128)
-        return fail(KVQ_E_INVALID, "%s: group_size=%u (supported: 32, 64, 128)", fn, group_size);
+    if ((group_size != 32 && group_size != 64 && group_size != 128) || group_size > head_dim)
+        return fail(KVQ_E_INVALID, "%s: group_size=%u (supported: 32, 64, 128, at most head_dim)", fn, group_size);
     st = check_ptrs(fn, {q, k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros, out});
     if (st) return st;
     KvCache C;
     C.kc = k_packed; C.vc = v_packed;
     C.ks = k_scales; C.vs = v_scales;
     C.kz = k_zeros; C.vz = v_zeros;
-    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, (int)(head_dim / group_size), C,
+    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, head_dim, (int)(head_dim / group_size), C,
                     softmax_scale, out, workspace, workspace_bytes, stream);
 }

@@ -216,7 +216,8 @@ def _attn(hq=32, hkv=8, t=4096, d=128, q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAK
     (_attn(t=0), "num_tokens=0"),
     (_attn(hq=12, hkv=8), "not 1..8 times"),
     (_attn(hq=72, hkv=8), "not 1..8 times"),
-    (_attn(d=64), "head_dim=64"),
+    (_attn(d=96), "head_dim=96"),
+    (_attn(d=512), "head_dim=512"),
     (_attn(t=1 << 21, hkv=8), "2 GiB"),
     (_attn(hq=1 << 23, hkv=1 << 20, t=1), "queries larger than 2 GiB"),
     (_attn(q=0), "null"),
@@ -243,6 +244,9 @@ def test_attn_decode_workspace_sizes(lib):
     assert lib.kvq_attn_decode_workspace_bytes(48, 8, 1000, 128, ctypes.byref(b)) == 0
     assert b.value == 4096 + 8 * 8 * 8 * 132 * 4
     assert lib.kvq_attn_decode_workspace_bytes(32, 8, 0, 128, ctypes.byref(b)) == _lib.KVQ_E_INVALID
+    # the record holds head_dim outputs, max, sum and two pad floats
+    assert lib.kvq_attn_decode_workspace_bytes(16, 2, 4096, 256, ctypes.byref(b)) == 0
+    assert b.value == 4096 + 2 * 32 * 8 * 260 * 4
 
 
 def test_attn_decode_int4_validation(lib):
@@ -254,5 +258,8 @@ def test_attn_decode_int4_validation(lib):
         assert st == _lib.KVQ_E_INVALID and f"group_size={gs}" in msg, msg
     st, msg = _err(lib, "kvq_attn_decode_int4", *ok, 32, FAKE, FAKE, 0, FAKE, FAKE, FAKE, f, FAKE, None, 0, None)
     assert st == _lib.KVQ_E_INVALID and "null" in msg, msg
-    st, msg = _err(lib, "kvq_attn_decode_int4", FAKE, 32, 8, 4096, 64, 32, *cache, f, FAKE, None, 0, None)
-    assert st == _lib.KVQ_E_INVALID and "head_dim=64" in msg, msg
+    st, msg = _err(lib, "kvq_attn_decode_int4", FAKE, 32, 8, 4096, 32, 32, *cache, f, FAKE, None, 0, None)
+    assert st == _lib.KVQ_E_INVALID and "head_dim=32" in msg, msg
+    # a group may not span two rows
+    st, msg = _err(lib, "kvq_attn_decode_int4", FAKE, 32, 8, 4096, 64, 128, *cache, f, FAKE, None, 0, None)
+    assert st == _lib.KVQ_E_INVALID and "group_size=128" in msg, msg

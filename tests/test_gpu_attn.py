@@ -170,3 +170,23 @@ def test_int4_long_cache():
     print_case("attn int4 long")
     inp = _cache4(32768, 1, 4, 128, 32, seed=800)
     _check4(inp, 32, 0.0884, _run4(inp, 32, 0.0884), "int4 T=32768")
+
+
+# ------------------------------------------------------- other head dims ----
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("t,hkv,g", [(1, 1, 1), (129, 2, 3), (4096, 8, 4), (20000, 1, 8)])
+def test_head_dims_int8(d, t, hkv, g):
+    print_case("attn int8 head_dim", d, t, hkv, g)
+    inp = _cache(t, hkv, hkv * g, d, seed=900 + d + t + g)
+    scale = 1.0 / math.sqrt(d)
+    _check(inp, scale, _run(*inp, scale), f"D={d} T={t} Hkv={hkv} G={g}")
+
+
+@pytest.mark.parametrize("d,gs", [(64, 32), (64, 64), (256, 32), (256, 64), (256, 128)])
+@pytest.mark.parametrize("t,hkv,g", [(3, 1, 2), (1000, 2, 4), (4096, 8, 8)])
+def test_head_dims_int4(d, gs, t, hkv, g):
+    print_case("attn int4 head_dim", d, gs, t, hkv, g)
+    inp = _cache4(t, hkv, hkv * g, d, gs, seed=950 + d + gs + t + g)
+    scale = 1.0 / math.sqrt(d)
+    _check4(inp, gs, scale, _run4(inp, gs, scale), f"D={d} gs={gs} T={t} Hkv={hkv} G={g}")
