@@ -86,6 +86,9 @@ AWQ_F16X_MS = (1, 16, 128)   # INT4 AWQ with fp16 activations, beside the step
 # decode attention over the INT8 cache, beside the step: 4096 tokens x 8 KV
 # heads x 128 (the 32768 x 128 cache), 32 query heads
 ATTN_T, ATTN_HKV, ATTN_HQ, ATTN_D = 4096, 8, 32, 128
+# and a serving batch: 16 sequences of 1024..4096 tokens (seeded), same heads
+ATTN_B = 16
+ATTN_LENS = [int(n) for n in np.random.default_rng(17).integers(1024, 4097, ATTN_B)]
 
 
 def attn_bytes(int4=False):
@@ -117,6 +120,9 @@ def extra_table():
     rows += [(f"int4_awq_qkv_f16x_M{m}", awq_bytes(m, 2), 2 * m * na * AWQ_K, "fp16") for m in AWQ_F16X_MS]
     rows += [(f"attn_decode_int8_T{ATTN_T}", attn_bytes(), 0, "hbm"),   # HBM-bound: vector ALU products
              (f"attn_decode_int4_g{KV_GS}_T{ATTN_T}", attn_bytes(True), 0, "hbm")]
+    vrows = sum(ATTN_LENS) * ATTN_HKV
+    rows += [(f"attn_decode_int8_varlen_B{ATTN_B}", 2 * vrows * (ATTN_D + 4) + 2 * ATTN_B * ATTN_HQ * ATTN_D * 4
+              + (ATTN_B + 1) * 4, 0, "hbm")]
     return rows
 
 
@@ -161,6 +167,14 @@ def make_inputs(torch, api, synth):
         s[f"attn_{name}p4"] = p4.view(ATTN_T, ATTN_HKV, ATTN_D // 2)
         s[f"attn_{name}s4"] = s4.view(ATTN_T, ATTN_HKV, ng)
         s[f"attn_{name}z4"] = z4.view(ATTN_T, ATTN_HKV, ng)
+    ttot = sum(ATTN_LENS)
+    vq, vk, vv = synth.attn_decode(ttot, ATTN_HKV, ATTN_HQ, ATTN_D, seed=19)
+    s["attnv_q"] = dev(np.stack([synth.attn_decode(1, 1, ATTN_HQ, ATTN_D, seed=20 + b)[0] for b in range(ATTN_B)]))
+    s["attnv_start"] = dev(np.concatenate([[0], np.cumsum(ATTN_LENS)]).astype(np.int32))
+    for name, a in (("k", vk), ("v", vv)):
+        codes, scales = api.quant_int8_token(dev(a.reshape(ttot * ATTN_HKV, ATTN_D)))
+        s[f"attnv_{name}c"] = codes.view(ttot, ATTN_HKV, ATTN_D)
+        s[f"attnv_{name}s"] = scales.view(ttot, ATTN_HKV)
     torch.cuda.synchronize()
     return s, (qkv, down, x5, projs)
 
@@ -202,6 +216,7 @@ class StepBuffers:
         self.awqx_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_EXTRA_MS + (1, 16)}
         self.awq16_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_F16X_MS}
         self.attn_out = e((ATTN_HQ, ATTN_D), torch.float32)
+        self.attnv_out = e((ATTN_B, ATTN_HQ, ATTN_D), torch.float32)
         self.qkv_weight = api.W8a8Weight(api.ROWSCALE, s["qkv_w"])
         self.down_weight = api.W8a8Weight(api.BLK128, s["down_w"])
         self.qkv_q = {m: e((m, QKV_K), torch.uint8) for m in QKV_MS}
@@ -243,6 +258,10 @@ class StepBuffers:
         L.append((f"attn_decode_int4_g{KV_GS}_T{ATTN_T}",
                   lambda: api.attn_decode_int4(s["attn_q"], KV_GS, s["attn_kp4"], s["attn_ks4"], s["attn_kz4"],
                                                s["attn_vp4"], s["attn_vs4"], s["attn_vz4"], out=self.attn_out)))
+        L.append((f"attn_decode_int8_varlen_B{ATTN_B}",
+                  lambda: api.attn_decode_int8_varlen(s["attnv_q"], s["attnv_start"], max(ATTN_LENS), s["attnv_kc"],
+                                                      s["attnv_ks"], s["attnv_vc"], s["attnv_vs"],
+                                                      out=self.attnv_out)))
         return L
 
     # each launcher issues exactly one call

@@ -347,6 +347,47 @@ int kvq_attn_decode_int4(const float *q, uint32_t num_q_heads,
                          float softmax_scale, float *out, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/* A batch of sequences of different lengths, one new token each (the same
+ * attention per sequence).
+ *   q, out:    fp32 [batch][num_q_heads][head_dim]
+ *   seq_start: device uint32 [batch + 1]: sequence b's cache rows are tokens
+ *              seq_start[b] .. seq_start[b+1]-1 of the cache (packed:
+ *              [total_tokens][num_kv_heads][...] as in the calls above).
+ *              Non-decreasing, seq_start[batch] <= total_tokens, every
+ *              length <= max_seq_tokens (the host's bound, used to plan the
+ *              work).  The kernels read it on the device: longer sequences
+ *              are cut at max_seq_tokens, rows past total_tokens read as zero
+ *              codes and scales (no fault), a sequence with no tokens gets a
+ *              zero output.
+ * Workspace as above, sized by kvq_attn_decode_varlen_workspace_bytes.
+ * Errors: KVQ_E_INVALID for batch == 0, head shapes as above,
+ * max_seq_tokens > total_tokens, a null or misaligned seq_start. */
+int kvq_attn_decode_int8_varlen(const float *q, uint32_t batch,
+                                uint32_t num_q_heads, uint32_t num_kv_heads,
+                                uint32_t head_dim, const uint32_t *seq_start,
+                                uint32_t total_tokens, uint32_t max_seq_tokens,
+                                const int8_t *k_codes, const float *k_scales,
+                                const int8_t *v_codes, const float *v_scales,
+                                float softmax_scale, float *out,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+int kvq_attn_decode_int4_varlen(const float *q, uint32_t batch,
+                                uint32_t num_q_heads, uint32_t num_kv_heads,
+                                uint32_t head_dim, uint32_t group_size,
+                                const uint32_t *seq_start, uint32_t total_tokens,
+                                uint32_t max_seq_tokens, const uint8_t *k_packed,
+                                const float *k_scales, const float *k_zeros,
+                                const uint8_t *v_packed, const float *v_scales,
+                                const float *v_zeros, float softmax_scale,
+                                float *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+int kvq_attn_decode_varlen_workspace_bytes(uint32_t batch, uint32_t num_q_heads,
+                                           uint32_t num_kv_heads,
+                                           uint32_t max_seq_tokens,
+                                           uint32_t head_dim, size_t *bytes);
+
 /* ======================================================================== */
 /* Measurement helper (not part of the method)                              */
 /* kvq_stream_read: reads `bytes` (a positive multiple of 16) at `src` (16-

@@ -60,6 +60,11 @@ SIGNATURES = {
     "kvq_stream_read": [_p, _sz, _p, _p],
     "kvq_attn_decode_int8": [_p, _u32, _u32, _u32, _u32, _p, _p, _p, _p, ctypes.c_float, _p, _p, _sz, _p],
     "kvq_attn_decode_workspace_bytes": [_u32, _u32, _u32, _u32, _psz],
+    "kvq_attn_decode_varlen_workspace_bytes": [_u32, _u32, _u32, _u32, _u32, _psz],
+    "kvq_attn_decode_int8_varlen": [_p, _u32, _u32, _u32, _u32, _p, _u32, _u32, _p, _p, _p, _p, ctypes.c_float, _p,
+                                    _p, _sz, _p],
+    "kvq_attn_decode_int4_varlen": [_p, _u32, _u32, _u32, _u32, _u32, _p, _u32, _u32, _p, _p, _p, _p, _p, _p,
+                                    ctypes.c_float, _p, _p, _sz, _p],
     "kvq_attn_decode_int4": [_p, _u32, _u32, _u32, _u32, _u32, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _sz,
                              _p],
 }

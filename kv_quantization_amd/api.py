@@ -378,6 +378,69 @@ def attn_decode_int4(q: torch.Tensor, group_size: int, k_packed: torch.Tensor, k
     return o
 
 
+def attn_decode_varlen_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_tokens: int,
+                                       head_dim: int) -> int:
+    b = ctypes.c_size_t()
+    _lib.call("kvq_attn_decode_varlen_workspace_bytes", batch, num_q_heads, num_kv_heads, max_seq_tokens, head_dim,
+              ctypes.byref(b))
+    return b.value
+
+
+def _varlen_common(q, seq_start, softmax_scale, out):
+    bsz, hq, d = q.shape
+    if seq_start.dtype not in (torch.int32, torch.uint32) or tuple(seq_start.shape) != (bsz + 1,):
+        raise ValueError("seq_start must be int32/uint32 [batch + 1]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = _empty((bsz, hq, d), torch.float32, q) if out is None else out
+    return bsz, hq, d, scale, o
+
+
+def attn_decode_int8_varlen(q: torch.Tensor, seq_start: torch.Tensor, max_seq_tokens: int, k_codes: torch.Tensor,
+                            k_scales: torch.Tensor, v_codes: torch.Tensor, v_scales: torch.Tensor,
+                            softmax_scale: float = None, out: torch.Tensor = None,
+                            use_workspace: bool = True) -> torch.Tensor:
+    """q fp32 [B, Hq, D]; seq_start device int32 [B + 1]; k/v codes int8
+    [T_total, Hkv, D], scales fp32 [T_total, Hkv] -> out fp32 [B, Hq, D]."""
+    t, hkv, d = k_codes.shape
+    bsz, hq, d, scale, o = _varlen_common(q, seq_start, softmax_scale, out)
+    stream = _stream(q)
+    ws_ptr, ws_bytes = 0, 0
+    if use_workspace:
+        ws_bytes = attn_decode_varlen_workspace_bytes(bsz, hq, hkv, max_seq_tokens, d)
+        if ws_bytes:
+            ws_ptr = workspace(q.device, ws_bytes, stream).data_ptr()
+    _lib.call("kvq_attn_decode_int8_varlen", _dev(q, torch.float32, "q"), bsz, hq, hkv, d,
+              _dev(seq_start, seq_start.dtype, "seq_start"), t, max_seq_tokens,
+              _dev(k_codes, torch.int8, "k_codes"), _dev(k_scales, torch.float32, "k_scales"),
+              _dev(v_codes, torch.int8, "v_codes"), _dev(v_scales, torch.float32, "v_scales"), scale,
+              _dev(o, torch.float32, "out"), ws_ptr, ws_bytes, stream)
+    return o
+
+
+def attn_decode_int4_varlen(q: torch.Tensor, seq_start: torch.Tensor, max_seq_tokens: int, group_size: int,
+                            k_packed: torch.Tensor, k_scales: torch.Tensor, k_zeros: torch.Tensor,
+                            v_packed: torch.Tensor, v_scales: torch.Tensor, v_zeros: torch.Tensor,
+                            softmax_scale: float = None, out: torch.Tensor = None,
+                            use_workspace: bool = True) -> torch.Tensor:
+    """q fp32 [B, Hq, D]; seq_start device int32 [B + 1]; k/v packed uint8
+    [T_total, Hkv, D/2], scales and zeros fp32 [T_total, Hkv, D/group_size]."""
+    t, hkv, half = k_packed.shape
+    bsz, hq, d, scale, o = _varlen_common(q, seq_start, softmax_scale, out)
+    stream = _stream(q)
+    ws_ptr, ws_bytes = 0, 0
+    if use_workspace:
+        ws_bytes = attn_decode_varlen_workspace_bytes(bsz, hq, hkv, max_seq_tokens, d)
+        if ws_bytes:
+            ws_ptr = workspace(q.device, ws_bytes, stream).data_ptr()
+    f = lambda a, n: _dev(a, torch.float32, n)
+    _lib.call("kvq_attn_decode_int4_varlen", _dev(q, torch.float32, "q"), bsz, hq, hkv, d, group_size,
+              _dev(seq_start, seq_start.dtype, "seq_start"), t, max_seq_tokens,
+              _dev(k_packed, torch.uint8, "k_packed"), f(k_scales, "k_scales"), f(k_zeros, "k_zeros"),
+              _dev(v_packed, torch.uint8, "v_packed"), f(v_scales, "v_scales"), f(v_zeros, "v_zeros"), scale,
+              _dev(o, torch.float32, "out"), ws_ptr, ws_bytes, stream)
+    return o
+
+
 # ---------------------------------------------------------- measurement ----
 
 def stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor) -> None:

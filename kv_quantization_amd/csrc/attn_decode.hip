@@ -46,6 +46,7 @@ constexpr int kHg = 4 / kWpb;         // softmax: head groups (heads j with j % 
 
 constexpr int kAttnThreads = 256;
 constexpr uint32_t kAttnTargetWgs = 256;
+constexpr uint32_t kAttnMaxBpc = 2;         // blocks walked by one workgroup at most (when the workspace allows)
 
 // The cache: INT8 codes [rows][D] with one scale per row (NG == 0), or INT4
 // codes packed two per byte [rows][D/2] (even element in the low nibble)
@@ -57,10 +58,29 @@ struct KvCache {
     const float *kz, *vz;   // INT4 zeros [rows][NG]
 };
 
+// Sequence b of a batch: its first cache token and its token count.  With
+// seq_start NULL (one sequence) that is 0 and T; else seq_start[b] and
+// seq_start[b+1] - seq_start[b], capped at tmax (device data the host never
+// sees: a bad entry only makes the reads leave the cache, and those read
+// zeros).
+struct Seq {
+    uint32_t base, len;
+};
+
+__device__ __forceinline__ Seq seq_of(const uint32_t *seq_start, uint32_t b, uint32_t T, uint32_t tmax) {
+    if (!seq_start) return Seq{0u, T};
+    const uint32_t s0 = seq_start[b], s1 = seq_start[b + 1];
+    const uint32_t n = s1 > s0 ? s1 - s0 : 0u;
+    return Seq{s0, n < tmax ? n : tmax};
+}
+
+// T: tokens in the cache (with a batch, the rows of all sequences); grid:
+// batch x KV head x chunk.
 template <int D, int GM, int NG>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restrict__ q, uint32_t G, uint32_t hkv,
-                                                            uint32_t T, KvCache C, float sm_scale, uint32_t nchunks,
-                                                            uint32_t bpc, float *__restrict__ out,
+                                                            uint32_t T, const uint32_t *__restrict__ seq_start,
+                                                            uint32_t tmax, KvCache C, float sm_scale,
+                                                            uint32_t nchunks, uint32_t bpc, float *__restrict__ out,
                                                             float *__restrict__ partials) {
     constexpr int LPT = D / 16;               // scores: lanes per token (16 dims each)
     constexpr int TPI = kWave / LPT;          // scores: tokens per wave load
@@ -78,9 +98,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     __shared__ float s_o[NTG][GM][D];                // the token groups' outputs
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const uint32_t g = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
-    const uint32_t nblk = (T + kAttnBlk - 1) / kAttnBlk;
+    const uint32_t per_b = hkv * nchunks;
+    const uint32_t b = blockIdx.x / per_b, g = (blockIdx.x % per_b) / nchunks, c = blockIdx.x % nchunks;
+    const Seq sq = seq_of(seq_start, b, T, tmax);
+    const uint32_t hq = hkv * G;
+    q += (size_t)b * hq * D;
+    out += (size_t)b * hq * D;
+    const uint32_t nblk = (sq.len + kAttnBlk - 1) / kAttnBlk;
     const uint32_t blk0 = c * bpc, blk1 = blk0 + bpc < nblk ? blk0 + bpc : nblk;
+    if (blk0 >= nblk) {
+        // no tokens in this chunk: the merge reads only chunks that have
+        // some; an empty sequence without chunks gets zeros
+        if (nchunks == 1)
+            for (uint32_t i = threadIdx.x; i < G * D; i += kAttnThreads) out[(size_t)g * G * D + i] = 0.f;
+        return;
+    }
 
     // query rows of this head group, the 16 dims of this lane's key slice
     // (INT4: they lie in group l8 / (16 / (D / NG)) ... one group, since a
@@ -89,7 +121,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     // (buffer loads: padding heads read zeros without a branch, so the
     // cache loads below are issued before the query arrives)
     float qr[GM][16], qsum[GM];
-    const rsrc_t rq = make_rsrc(q, hkv * G * D * 4);
+    const rsrc_t rq = make_rsrc(q, hq * D * 4);
 #pragma unroll
     for (int j = 0; j < GM; ++j) {
         const uint32_t qo = (uint32_t)j < G ? ((g * G + j) * D + 16 * l8) * 4 : kOffNone;
@@ -132,16 +164,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const uint32_t t = t0 + wv * kTpw + i * TPI + tk;
-            const uint32_t row = t * hkv + g;
+            const uint32_t row = (sq.base + t) * hkv + g;
             if (I4) {
-                const u32x2 w2 = __builtin_amdgcn_raw_buffer_load_b64(rk, t < T ? row * RB + 8 * l8 : kOffNone, 0, 0);
+                const u32x2 w2 = __builtin_amdgcn_raw_buffer_load_b64(rk, t < sq.len ? row * RB + 8 * l8 : kOffNone, 0, 0);
                 kraw[i] = u32x4{w2.x, w2.y, 0u, 0u};
-                const uint32_t so = t < T ? (row * NGS + kgrp) * 4 : kOffNone;
+                const uint32_t so = t < sq.len ? (row * NGS + kgrp) * 4 : kOffNone;
                 ksc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, so, 0, 0));
                 kzr[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkz, so, 0, 0));
             } else {
-                kraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, t < T ? row * RB + 16 * l8 : kOffNone, 0, 0);
-                ksc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, t < T ? row * 4 : kOffNone, 0, 0));
+                kraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, t < sq.len ? row * RB + 16 * l8 : kOffNone, 0, 0);
+                ksc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, t < sq.len ? row * 4 : kOffNone, 0, 0));
                 kzr[i] = 0.f;
             }
         }
@@ -149,18 +181,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 #pragma unroll
         for (int u = 0; u < TPG; ++u) {
             const uint32_t t = t0 + tg * TPG + u;
-            const uint32_t row = t * hkv + g;
+            const uint32_t row = (sq.base + t) * hkv + g;
             if (I4)
-                vraw[u] = __builtin_amdgcn_raw_buffer_load_b16(rv, t < T ? row * RB + 2 * e4 : kOffNone, 0, 0);
+                vraw[u] = __builtin_amdgcn_raw_buffer_load_b16(rv, t < sq.len ? row * RB + 2 * e4 : kOffNone, 0, 0);
             else
-                vraw[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, t < T ? row * RB + 4 * e4 : kOffNone, 0, 0);
+                vraw[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, t < sq.len ? row * RB + 4 * e4 : kOffNone, 0, 0);
         }
         const uint32_t tv = t0 + tt;
-        const uint32_t vrow = tv * hkv + g;
+        const uint32_t vrow = (sq.base + tv) * hkv + g;
         float vsc[NGS], vzr[NGS];
 #pragma unroll
         for (int k = 0; k < NGS; ++k) {
-            const uint32_t so = tv < T ? (vrow * NGS + k) * 4 : kOffNone;
+            const uint32_t so = tv < sq.len ? (vrow * NGS + k) * 4 : kOffNone;
             vsc[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, so, 0, 0));
             vzr[k] = I4 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvz, so, 0, 0)) : 0.f;
         }
@@ -181,7 +213,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
                     for (int b = 0; b < 4; ++b) x[4 * w + b] = (float)(int8_t)(kraw[i][w] >> (8 * b));
             }
             const uint32_t lt = wv * kTpw + i * TPI + tk;
-            const bool valid = t0 + lt < T;
+            const bool valid = t0 + lt < sq.len;
 #pragma unroll
             for (int j = 0; j < GM; ++j) {
                 float d = 0.f;
@@ -311,10 +343,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
     }
 
     // -- several chunks: (output, max, sum, 2 pad) of this chunk as a record
-    // [head][chunk][GM][D + 4] behind the workspace's counter area; the
+    // [sequence][head][chunk][GM][D + 4] behind the workspace's counter area; the
     // merge kernel that follows on the stream combines them
     constexpr uint32_t kRecD = D + 4;
-    float *rec = partials + ((size_t)g * nchunks + c) * GM * kRecD;
+    float *rec = partials + (((size_t)b * hkv + g) * nchunks + c) * GM * kRecD;
 #pragma unroll
     for (int r = 0; r * kAttnThreads < kOut; ++r) {
         const uint32_t idx = tid + r * kAttnThreads;
@@ -342,13 +374,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode(const float *__restr
 // weights exp(m_c - M) and the weighted sum of the sums, so the chunks are
 // added in order and the result does not depend on launch timing.
 template <int D, int GM>
-__global__ __launch_bounds__(D) void attn_merge(const float *__restrict__ partials, uint32_t G, uint32_t nchunks,
-                                                float *__restrict__ out) {
+__global__ __launch_bounds__(D) void attn_merge(const float *__restrict__ partials, uint32_t G, uint32_t hkv,
+                                                uint32_t T, const uint32_t *__restrict__ seq_start, uint32_t tmax,
+                                                uint32_t nchunks_max, uint32_t bpc, float *__restrict__ out) {
     constexpr uint32_t kRecD = D + 4;
-    const uint32_t g = blockIdx.x / G, j = blockIdx.x % G, d = threadIdx.x, lane = d & 63;
+    const uint32_t per_b = hkv * G;
+    const uint32_t b = blockIdx.x / per_b, g = (blockIdx.x % per_b) / G, j = blockIdx.x % G;
+    const uint32_t d = threadIdx.x, lane = d & 63;
+    out += (size_t)b * per_b * D;
+    // the chunks that hold tokens of this sequence
+    const Seq sq = seq_of(seq_start, b, T, tmax);
+    const uint32_t nblk = (sq.len + kAttnBlk - 1) / kAttnBlk;
+    const uint32_t nchunks = (nblk + bpc - 1) / bpc;
+    if (nchunks == 0) {
+        out[((size_t)g * G + j) * D + d] = 0.f;
+        return;
+    }
     // this head's records: chunk c at (c * GM + j) * kRecD floats (buffer
     // loads: chunks past the end read zeros without a branch)
-    const rsrc_t rp = make_rsrc(partials + (size_t)g * nchunks * GM * kRecD, nchunks * GM * kRecD * 4);
+    const rsrc_t rp = make_rsrc(partials + ((size_t)b * hkv + g) * nchunks_max * GM * kRecD,
+                                nchunks * GM * kRecD * 4);
     float M = -__builtin_inff(), L = 0.f, O = 0.f;
     for (uint32_t c0 = 0; c0 < nchunks; c0 += 64) {
         float ov[64];
@@ -380,31 +425,149 @@ struct AttnPlan {
 
 uint32_t attn_gm(uint32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
-// ~256 workgroups: split each head's tokens into chunks of whole 128-token blocks
-AttnPlan attn_plan(uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D) {
+// ~256 workgroups: split each (sequence, KV head)'s tokens, up to tmax, into
+// chunks of whole 128-token blocks
+AttnPlan attn_plan(uint32_t hq, uint32_t hkv, uint32_t B, uint32_t tmax, uint32_t D) {
     AttnPlan pl;
     pl.gm = attn_gm(hq / hkv);
-    const uint32_t nblk = (T + kAttnBlk - 1) / kAttnBlk;
-    uint32_t want = kAttnTargetWgs / hkv;
-    if (want < 1) want = 1;
+    uint32_t nblk = (tmax + kAttnBlk - 1) / kAttnBlk;
+    if (nblk < 1) nblk = 1;
+    const uint64_t units = (uint64_t)B * hkv;
+    uint32_t want = units >= kAttnTargetWgs ? 1u : (uint32_t)(kAttnTargetWgs / units);
+    // a workgroup walks its blocks one after another (each a memory round
+    // trip): with many sequences, more and shorter chunks instead
+    const uint32_t by_len = (nblk + kAttnMaxBpc - 1) / kAttnMaxBpc;
+    if (want < by_len) want = by_len;
     if (want > nblk) want = nblk;
     pl.bpc = (nblk + want - 1) / want;
     pl.nchunks = (nblk + pl.bpc - 1) / pl.bpc;
-    pl.ws_bytes = pl.nchunks > 1
-                      ? KVQ_WORKSPACE_COUNTER_BYTES + (size_t)hkv * pl.nchunks * pl.gm * (D + 4) * 4
-                      : 0;
+    pl.ws_bytes = pl.nchunks > 1 ? KVQ_WORKSPACE_COUNTER_BYTES + units * pl.nchunks * pl.gm * (D + 4) * 4 : 0;
     return pl;
 }
 
-int check_attn(const char *fn, uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D) {
-    if (hq == 0 || hkv == 0 || T == 0)
-        return fail(KVQ_E_INVALID, "%s: num_q_heads=%u num_kv_heads=%u num_tokens=%u (want all > 0)", fn, hq, hkv, T);
+int check_heads(const char *fn, uint32_t hq, uint32_t hkv, uint32_t D) {
+    if (hq == 0 || hkv == 0)
+        return fail(KVQ_E_INVALID, "%s: num_q_heads=%u num_kv_heads=%u (want both > 0)", fn, hq, hkv);
     if (hq % hkv || hq / hkv > 8)
         return fail(KVQ_E_INVALID, "%s: num_q_heads=%u is not 1..8 times num_kv_heads=%u", fn, hq, hkv);
     if (D != 64 && D != 128 && D != 256)
         return fail(KVQ_E_INVALID, "%s: head_dim=%u (supported: 64, 128, 256)", fn, D);
+    return KVQ_OK;
+}
+
+int check_attn(const char *fn, uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D) {
+    if (T == 0) return fail(KVQ_E_INVALID, "%s: num_tokens=0 (want > 0)", fn);
+    const int st = check_heads(fn, hq, hkv, D);
+    if (st) return st;
     if ((uint64_t)T * hkv * D >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: cache larger than 2 GiB", fn);
     if ((uint64_t)hq * D * 4 >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: queries larger than 2 GiB", fn);
+    return KVQ_OK;
+}
+
+int check_varlen(const char *fn, uint32_t B, uint32_t hq, uint32_t hkv, uint32_t total, uint32_t tmax, uint32_t D,
+                 const uint32_t *seq_start) {
+    if (B == 0) return fail(KVQ_E_INVALID, "%s: batch=0 (want > 0)", fn);
+    const int st = check_heads(fn, hq, hkv, D);
+    if (st) return st;
+    if (tmax > total) return fail(KVQ_E_INVALID, "%s: max_seq_tokens=%u exceeds total_tokens=%u", fn, tmax, total);
+    if ((uint64_t)total * hkv * D >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: cache larger than 2 GiB", fn);
+    if ((uint64_t)B * hq * D * 4 >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: queries larger than 2 GiB", fn);
+    if ((uint64_t)B * hkv * hq >= 0x80000000ull) return fail(KVQ_E_INVALID, "%s: batch too large", fn);
+    if (!seq_start || (reinterpret_cast<uintptr_t>(seq_start) & 3u))
+        return fail(KVQ_E_INVALID, "%s: seq_start must be a 4-byte aligned device pointer", fn);
+    return KVQ_OK;
+}
+
+template <int D, int GM, int NG>
+void attn_launch(const float *q, uint32_t B, uint32_t G, uint32_t hkv, uint32_t T, const uint32_t *seq_start,
+                 uint32_t tmax, const KvCache &C, float sc, const AttnPlan &pl, float *out, float *partials,
+                 hipStream_t s) {
+    const unsigned grid = B * hkv * pl.nchunks;
+    attn_decode<D, GM, NG><<<grid, kAttnThreads, 0, s>>>(q, G, hkv, T, seq_start, tmax, C, sc, pl.nchunks, pl.bpc,
+                                                         out, partials);
+    if (pl.nchunks > 1)
+        attn_merge<D, GM><<<B * hkv * G, D, 0, s>>>(partials, G, hkv, T, seq_start, tmax, pl.nchunks, pl.bpc, out);
+}
+
+#define KVQ_ATTN_ARGS q, B, G, hkv, T, seq_start, tmax, C, sc, pl, out, partials, s
+#define KVQ_ATTN_PARAMS                                                                                          \
+    const float *q, uint32_t B, uint32_t G, uint32_t hkv, uint32_t T, const uint32_t *seq_start, uint32_t tmax, \
+        const KvCache &C, float sc, const AttnPlan &pl, float *out, float *partials, hipStream_t s
+
+template <int D, int NG>
+void attn_by_group(KVQ_ATTN_PARAMS) {
+    switch (pl.gm) {
+        case 1: attn_launch<D, 1, NG>(KVQ_ATTN_ARGS); break;
+        case 2: attn_launch<D, 2, NG>(KVQ_ATTN_ARGS); break;
+        case 4: attn_launch<D, 4, NG>(KVQ_ATTN_ARGS); break;
+        default: attn_launch<D, 8, NG>(KVQ_ATTN_ARGS); break;
+    }
+}
+
+// ng == 0: INT8 per-token cache; else INT4 with ng groups of 32..128 values per row
+template <int D>
+void attn_by_format(int ng, KVQ_ATTN_PARAMS) {
+    if (ng == 0) attn_by_group<D, 0>(KVQ_ATTN_ARGS);
+    if constexpr (D <= 128) {
+        if (ng == 1) attn_by_group<D, 1>(KVQ_ATTN_ARGS);
+    }
+    if (ng == 2) attn_by_group<D, 2>(KVQ_ATTN_ARGS);
+    if constexpr (D >= 128) {
+        if (ng == 4) attn_by_group<D, 4>(KVQ_ATTN_ARGS);
+    }
+    if constexpr (D == 256) {
+        if (ng == 8) attn_by_group<D, 8>(KVQ_ATTN_ARGS);
+    }
+}
+
+// B sequences (seq_start NULL: one sequence of T tokens); T: cache tokens
+int attn_run(const char *fn, const float *q, uint32_t B, uint32_t hq, uint32_t hkv, uint32_t T,
+             const uint32_t *seq_start, uint32_t tmax, uint32_t D, int ng, const KvCache &C, float sc, float *out,
+             void *workspace, size_t workspace_bytes, void *stream) {
+    if (!(sc == sc) || __builtin_isinf(sc)) return fail(KVQ_E_INVALID, "%s: softmax_scale is not finite", fn);
+    AttnPlan pl = attn_plan(hq, hkv, B, tmax, D);
+    float *partials = nullptr;
+    if (pl.nchunks > 1) {
+        if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
+            pl.bpc = (tmax + kAttnBlk - 1) / kAttnBlk;   // no workspace: one workgroup per (sequence, KV head)
+            if (pl.bpc < 1) pl.bpc = 1;
+            pl.nchunks = 1;
+        } else {
+            partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
+        }
+    }
+    const uint32_t G = hq / hkv;
+    hipStream_t s = as_stream(stream);
+    if (D == 64) attn_by_format<64>(ng, KVQ_ATTN_ARGS);
+    else if (D == 128) attn_by_format<128>(ng, KVQ_ATTN_ARGS);
+    else attn_by_format<256>(ng, KVQ_ATTN_ARGS);
+    return launch_status(fn);
+}
+
+#undef KVQ_ATTN_ARGS
+#undef KVQ_ATTN_PARAMS
+
+KvCache cache8(const int8_t *kc, const float *ks, const int8_t *vc, const float *vs) {
+    KvCache C;
+    C.kc = reinterpret_cast<const uint8_t *>(kc);
+    C.vc = reinterpret_cast<const uint8_t *>(vc);
+    C.ks = ks; C.vs = vs;
+    C.kz = nullptr; C.vz = nullptr;
+    return C;
+}
+
+KvCache cache4(const uint8_t *kp, const float *ks, const float *kz, const uint8_t *vp, const float *vs,
+               const float *vz) {
+    KvCache C;
+    C.kc = kp; C.vc = vp;
+    C.ks = ks; C.vs = vs;
+    C.kz = kz; C.vz = vz;
+    return C;
+}
+
+int check_group(const char *fn, uint32_t group_size, uint32_t head_dim) {
+    if ((group_size != 32 && group_size != 64 && group_size != 128) || group_size > head_dim)
+        return fail(KVQ_E_INVALID, "%s: group_size=%u (supported: 32, 64, 128, at most head_dim)", fn, group_size);
     return KVQ_OK;
 }
 
@@ -419,74 +582,21 @@ extern "C" int kvq_attn_decode_workspace_bytes(uint32_t num_q_heads, uint32_t nu
     *bytes = 0;
     const int st = check_attn("kvq_attn_decode_workspace_bytes", num_q_heads, num_kv_heads, num_tokens, head_dim);
     if (st) return st;
-    *bytes = attn_plan(num_q_heads, num_kv_heads, num_tokens, head_dim).ws_bytes;
+    *bytes = attn_plan(num_q_heads, num_kv_heads, 1, num_tokens, head_dim).ws_bytes;
     return KVQ_OK;
 }
 
-namespace kvq {
-namespace {
-
-template <int D, int GM, int NG>
-void attn_launch(unsigned grid, const float *q, uint32_t G, uint32_t hkv, uint32_t T, const KvCache &C, float sc,
-                 const AttnPlan &pl, float *out, float *partials, hipStream_t s) {
-    attn_decode<D, GM, NG><<<grid, kAttnThreads, 0, s>>>(q, G, hkv, T, C, sc, pl.nchunks, pl.bpc, out, partials);
-    if (pl.nchunks > 1) attn_merge<D, GM><<<hkv * G, D, 0, s>>>(partials, G, pl.nchunks, out);
+extern "C" int kvq_attn_decode_varlen_workspace_bytes(uint32_t batch, uint32_t num_q_heads, uint32_t num_kv_heads,
+                                                      uint32_t max_seq_tokens, uint32_t head_dim, size_t *bytes) {
+    const char *fn = "kvq_attn_decode_varlen_workspace_bytes";
+    if (!bytes) return fail(KVQ_E_INVALID, "%s: null output pointer", fn);
+    *bytes = 0;
+    if (batch == 0) return fail(KVQ_E_INVALID, "%s: batch=0 (want > 0)", fn);
+    const int st = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
+    if (st) return st;
+    *bytes = attn_plan(num_q_heads, num_kv_heads, batch, max_seq_tokens, head_dim).ws_bytes;
+    return KVQ_OK;
 }
-
-template <int D, int NG>
-void attn_by_group(unsigned grid, const float *q, uint32_t G, uint32_t hkv, uint32_t T, const KvCache &C, float sc,
-                   const AttnPlan &pl, float *out, float *partials, hipStream_t s) {
-    switch (pl.gm) {
-        case 1: attn_launch<D, 1, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
-        case 2: attn_launch<D, 2, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
-        case 4: attn_launch<D, 4, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
-        default: attn_launch<D, 8, NG>(grid, q, G, hkv, T, C, sc, pl, out, partials, s); break;
-    }
-}
-
-// ng == 0: INT8 per-token cache; else INT4 with ng groups of 32..128 values per row
-template <int D>
-void attn_by_format(int ng, unsigned grid, const float *q, uint32_t G, uint32_t hkv, uint32_t T, const KvCache &C,
-                    float sc, const AttnPlan &pl, float *out, float *partials, hipStream_t s) {
-    if (ng == 0) attn_by_group<D, 0>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
-    if constexpr (D <= 128) {
-        if (ng == 1) attn_by_group<D, 1>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
-    }
-    if (ng == 2) attn_by_group<D, 2>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
-    if constexpr (D >= 128) {
-        if (ng == 4) attn_by_group<D, 4>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
-    }
-    if constexpr (D == 256) {
-        if (ng == 8) attn_by_group<D, 8>(grid, q, G, hkv, T, C, sc, pl, out, partials, s);
-    }
-}
-
-int attn_run(const char *fn, const float *q, uint32_t hq, uint32_t hkv, uint32_t T, uint32_t D, int ng,
-             const KvCache &C, float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
-             void *stream) {
-    if (!(softmax_scale == softmax_scale) || __builtin_isinf(softmax_scale))
-        return fail(KVQ_E_INVALID, "%s: softmax_scale is not finite", fn);
-    AttnPlan pl = attn_plan(hq, hkv, T, D);
-    float *partials = nullptr;
-    if (pl.nchunks > 1) {
-        if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
-            pl.bpc = (T + kAttnBlk - 1) / kAttnBlk;   // no workspace: one workgroup per KV head
-            pl.nchunks = 1;
-        } else {
-            partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
-        }
-    }
-    const uint32_t G = hq / hkv;
-    const unsigned grid = hkv * pl.nchunks;
-    hipStream_t s = as_stream(stream);
-    if (D == 64) attn_by_format<64>(ng, grid, q, G, hkv, T, C, softmax_scale, pl, out, partials, s);
-    else if (D == 128) attn_by_format<128>(ng, grid, q, G, hkv, T, C, softmax_scale, pl, out, partials, s);
-    else attn_by_format<256>(ng, grid, q, G, hkv, T, C, softmax_scale, pl, out, partials, s);
-    return launch_status(fn);
-}
-
-}  // namespace
-}  // namespace kvq
 
 extern "C" int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads, uint32_t num_kv_heads,
                                     uint32_t num_tokens, uint32_t head_dim, const int8_t *k_codes,
@@ -498,13 +608,9 @@ extern "C" int kvq_attn_decode_int8(const float *q, uint32_t num_q_heads, uint32
     if (st) return st;
     st = check_ptrs(fn, {q, k_codes, k_scales, v_codes, v_scales, out});
     if (st) return st;
-    KvCache C;
-    C.kc = reinterpret_cast<const uint8_t *>(k_codes);
-    C.vc = reinterpret_cast<const uint8_t *>(v_codes);
-    C.ks = k_scales; C.vs = v_scales;
-    C.kz = nullptr; C.vz = nullptr;
-    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, head_dim, 0, C, softmax_scale, out, workspace,
-                    workspace_bytes, stream);
+    return attn_run(fn, q, 1, num_q_heads, num_kv_heads, num_tokens, nullptr, num_tokens, head_dim, 0,
+                    cache8(k_codes, k_scales, v_codes, v_scales), softmax_scale, out, workspace, workspace_bytes,
+                    stream);
 }
 
 extern "C" int kvq_attn_decode_int4(const float *q, uint32_t num_q_heads, uint32_t num_kv_heads,
@@ -516,14 +622,46 @@ extern "C" int kvq_attn_decode_int4(const float *q, uint32_t num_q_heads, uint32
     const char *fn = "kvq_attn_decode_int4";
     int st = check_attn(fn, num_q_heads, num_kv_heads, num_tokens, head_dim);
     if (st) return st;
-    if ((group_size != 32 && group_size != 64 && group_size != 128) || group_size > head_dim)
-        return fail(KVQ_E_INVALID, "%s: group_size=%u (supported: 32, 64, 128, at most head_dim)", fn, group_size);
+    st = check_group(fn, group_size, head_dim);
+    if (st) return st;
     st = check_ptrs(fn, {q, k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros, out});
     if (st) return st;
-    KvCache C;
-    C.kc = k_packed; C.vc = v_packed;
-    C.ks = k_scales; C.vs = v_scales;
-    C.kz = k_zeros; C.vz = v_zeros;
-    return attn_run(fn, q, num_q_heads, num_kv_heads, num_tokens, head_dim, (int)(head_dim / group_size), C,
+    return attn_run(fn, q, 1, num_q_heads, num_kv_heads, num_tokens, nullptr, num_tokens, head_dim,
+                    (int)(head_dim / group_size), cache4(k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros),
+                    softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kvq_attn_decode_int8_varlen(const float *q, uint32_t batch, uint32_t num_q_heads,
+                                           uint32_t num_kv_heads, uint32_t head_dim, const uint32_t *seq_start,
+                                           uint32_t total_tokens, uint32_t max_seq_tokens, const int8_t *k_codes,
+                                           const float *k_scales, const int8_t *v_codes, const float *v_scales,
+                                           float softmax_scale, float *out, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    const char *fn = "kvq_attn_decode_int8_varlen";
+    int st = check_varlen(fn, batch, num_q_heads, num_kv_heads, total_tokens, max_seq_tokens, head_dim, seq_start);
+    if (st) return st;
+    st = check_ptrs(fn, {q, k_codes, k_scales, v_codes, v_scales, out});
+    if (st) return st;
+    return attn_run(fn, q, batch, num_q_heads, num_kv_heads, total_tokens, seq_start, max_seq_tokens, head_dim, 0,
+                    cache8(k_codes, k_scales, v_codes, v_scales), softmax_scale, out, workspace, workspace_bytes,
+                    stream);
+}
+
+extern "C" int kvq_attn_decode_int4_varlen(const float *q, uint32_t batch, uint32_t num_q_heads,
+                                           uint32_t num_kv_heads, uint32_t head_dim, uint32_t group_size,
+                                           const uint32_t *seq_start, uint32_t total_tokens,
+                                           uint32_t max_seq_tokens, const uint8_t *k_packed, const float *k_scales,
+                                           const float *k_zeros, const uint8_t *v_packed, const float *v_scales,
+                                           const float *v_zeros, float softmax_scale, float *out, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    const char *fn = "kvq_attn_decode_int4_varlen";
+    int st = check_varlen(fn, batch, num_q_heads, num_kv_heads, total_tokens, max_seq_tokens, head_dim, seq_start);
+    if (st) return st;
+    st = check_group(fn, group_size, head_dim);
+    if (st) return st;
+    st = check_ptrs(fn, {q, k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros, out});
+    if (st) return st;
+    return attn_run(fn, q, batch, num_q_heads, num_kv_heads, total_tokens, seq_start, max_seq_tokens, head_dim,
+                    (int)(head_dim / group_size), cache4(k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros),
                     softmax_scale, out, workspace, workspace_bytes, stream);
 }

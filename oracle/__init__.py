@@ -501,3 +501,19 @@ def attn_decode_int4(q, k_packed, k_scales, k_zeros, v_packed, v_scales, v_zeros
     vh = kv_int4_dequant(v_packed, v_scales, v_zeros, rows, head_dim, group_size)
     shp = (num_tokens, num_kv_heads, head_dim)
     return attn_decode(q, kh.reshape(shp), vh.reshape(shp), softmax_scale)
+
+
+def attn_decode_varlen(q, seq_start, k_hat, v_hat, softmax_scale: float):
+    """A batch: q float32 [B, Hq, D]; sequence b reads cache rows
+    seq_start[b] .. seq_start[b+1]-1 of k_hat, v_hat [T_total, Hkv, D]; a
+    sequence with no tokens has output 0 (and bound 0).  Returns (out, bound)
+    fp64 [B, Hq, D]."""
+    q = _c(q, np.float32)
+    bsz, hq, d = q.shape
+    out = np.zeros((bsz, hq, d))
+    bound = np.zeros((bsz, hq, d))
+    for b in range(bsz):
+        s0, s1 = int(seq_start[b]), int(seq_start[b + 1])
+        if s1 > s0:
+            out[b], bound[b] = attn_decode(q[b], k_hat[s0:s1], v_hat[s0:s1], softmax_scale)
+    return out, bound

@@ -263,3 +263,27 @@ def test_attn_decode_int4_validation(lib):
     # a group may not span two rows
     st, msg = _err(lib, "kvq_attn_decode_int4", FAKE, 32, 8, 4096, 64, 128, *cache, f, FAKE, None, 0, None)
     assert st == _lib.KVQ_E_INVALID and "group_size=128" in msg, msg
+
+
+def test_attn_decode_varlen_validation(lib):
+    f = ctypes.c_float(0.088)
+    cache8 = (FAKE, FAKE, FAKE, FAKE)
+
+    def call(batch=4, hq=32, hkv=8, d=128, seq=FAKE, total=1000, tmax=500):
+        return _err(lib, "kvq_attn_decode_int8_varlen", FAKE, batch, hq, hkv, d, seq, total, tmax, *cache8, f, FAKE,
+                    None, 0, None)
+    for kw, frag in [(dict(batch=0), "batch=0"), (dict(hq=12), "not 1..8 times"), (dict(d=96), "head_dim=96"),
+                     (dict(seq=0), "seq_start"), (dict(seq=FAKE + 2), "seq_start"),
+                     (dict(tmax=1001), "exceeds total_tokens")]:
+        st, msg = call(**kw)
+        assert st == _lib.KVQ_E_INVALID and frag in msg, (kw, msg)
+    b = ctypes.c_size_t()
+    # 4 sequences x 8 KV heads = 32 units over up to 4096 tokens (32 blocks):
+    # chunks of at most 2 blocks, 16 per unit
+    assert lib.kvq_attn_decode_varlen_workspace_bytes(4, 32, 8, 4096, 128, ctypes.byref(b)) == 0
+    assert b.value == 4096 + 4 * 8 * 16 * 4 * 132 * 4
+    assert lib.kvq_attn_decode_varlen_workspace_bytes(64, 32, 8, 4096, 128, ctypes.byref(b)) == 0
+    assert b.value == 4096 + 64 * 8 * 16 * 4 * 132 * 4
+    # 64 sequences of at most 256 tokens x 8 heads: one workgroup each, nothing to merge
+    assert lib.kvq_attn_decode_varlen_workspace_bytes(64, 32, 8, 256, 128, ctypes.byref(b)) == 0
+    assert b.value == 0

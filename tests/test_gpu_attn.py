@@ -190,3 +190,82 @@ def test_head_dims_int4(d, gs, t, hkv, g):
     inp = _cache4(t, hkv, hkv * g, d, gs, seed=950 + d + gs + t + g)
     scale = 1.0 / math.sqrt(d)
     _check4(inp, gs, scale, _run4(inp, gs, scale), f"D={d} gs={gs} T={t} Hkv={hkv} G={g}")
+
+
+# --------------------------------------------------------------- varlen ----
+
+def _varlen_inputs(lengths, hkv, g, d, seed):
+    total = int(sum(lengths))
+    q, k, v = synth.attn_decode(max(total, 1), hkv, hkv * g, d, seed=seed)
+    qb = np.stack([synth.attn_decode(1, 1, hkv * g, d, seed=seed + 1 + b)[0] for b in range(len(lengths))])
+    seq_start = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return qb, seq_start, k[:max(total, 1)], v[:max(total, 1)]
+
+
+def _quant8(a):
+    t, hkv, d = a.shape
+    c, s = _oracle.kv_int8_quant(a.reshape(t * hkv, d))
+    return c.reshape(t, hkv, d), s.reshape(t, hkv)
+
+
+@pytest.mark.parametrize("lengths,hkv,g", [
+    ([0, 1, 5, 127, 128, 129, 1000, 4095, 300], 2, 4),
+    ([4096] * 4, 8, 4),
+    (list(np.random.default_rng(7).integers(0, 2048, 64)), 8, 4),
+    ([3000, 0, 0, 17], 1, 8),
+])
+def test_varlen_int8(lengths, hkv, g):
+    print_case("attn int8 varlen", len(lengths), hkv, g)
+    d = 128
+    qb, seq_start, k, v = _varlen_inputs(lengths, hkv, g, d, seed=1100 + len(lengths))
+    kc, ks = _quant8(k)
+    vc, vs = _quant8(v)
+    kh = _oracle.kv_int8_dequant(kc.reshape(-1, d), ks.reshape(-1)).reshape(kc.shape)
+    vh = _oracle.kv_int8_dequant(vc.reshape(-1, d), vs.reshape(-1)).reshape(vc.shape)
+    ref, bound = _oracle.attn_decode_varlen(qb, seq_start, kh, vh, 0.0884)
+    tmax = int(max(lengths))
+    for ws in (True, False):
+        got = host(api.attn_decode_int8_varlen(dev(qb), dev(seq_start), tmax, dev(kc), dev(ks), dev(vc), dev(vs),
+                                               0.0884, use_workspace=ws))
+        torch.cuda.synchronize()
+        worst = float((np.abs(got.astype(np.float64) - ref) / np.maximum(bound, 1e-30)).max())
+        print(f"varlen int8 ws={ws}: max |err|/sum p|v| = {worst:.3e}", flush=True)
+        assert np.all(np.isfinite(got)) and worst <= RTOL
+        for b, n in enumerate(lengths):
+            if n == 0:
+                assert np.all(got[b] == 0.0)
+
+
+def test_varlen_batch_of_one_is_the_single_call():
+    print_case("attn int8 varlen B=1")
+    inp = _cache(1000, 2, 8, 128, seed=1200)
+    q, kc, ks, vc, vs = inp
+    single = _run(*inp, 0.0884)
+    seq_start = np.array([0, 1000], np.int32)
+    got = host(api.attn_decode_int8_varlen(dev(q[None]), dev(seq_start), 1000, dev(kc), dev(ks), dev(vc), dev(vs),
+                                           0.0884))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got[0].view(np.uint32), single.view(np.uint32))
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+def test_varlen_int4(gs):
+    print_case("attn int4 varlen", gs)
+    lengths, hkv, g, d = [0, 1, 129, 2000, 64], 2, 4, 128
+    qb, seq_start, k, v = _varlen_inputs(lengths, hkv, g, d, seed=1300 + gs)
+    t = k.shape[0]
+    ng = d // gs
+    parts = []
+    for a in (k, v):
+        p4, s4, z4 = _oracle.kv_int4_quant(a.reshape(t * hkv, d), gs)
+        parts.append((p4.reshape(t, hkv, d // 2), s4.reshape(t, hkv, ng), z4.reshape(t, hkv, ng),
+                      _oracle.kv_int4_dequant(p4, s4, z4, t * hkv, d, gs).reshape(t, hkv, d)))
+    (kp, ks, kz, kh), (vp, vs, vz, vh) = parts
+    ref, bound = _oracle.attn_decode_varlen(qb, seq_start, kh, vh, 0.0884)
+    got = host(api.attn_decode_int4_varlen(dev(qb), dev(seq_start), int(max(lengths)), gs, dev(kp), dev(ks),
+                                           dev(kz), dev(vp), dev(vs), dev(vz), 0.0884))
+    torch.cuda.synchronize()
+    worst = float((np.abs(got.astype(np.float64) - ref) / np.maximum(bound, 1e-30)).max())
+    print(f"varlen int4 gs={gs}: max |err|/sum p|v| = {worst:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and worst <= RTOL
+    assert np.all(got[0] == 0.0)

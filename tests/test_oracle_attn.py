@@ -112,3 +112,14 @@ def test_int8_and_int4_caches_dequantize_by_their_sections(orc):
     # quantization error of the cache moves the output only a little
     exact, bound = orc.attn_decode(q, k, v, 0.1)
     assert np.max(np.abs(got - exact) / bound.max()) < 0.05
+
+
+def test_varlen_is_each_sequence_alone(orc):
+    q0, k, v = synth.attn_decode(50, 2, 4, 32, seed=28)
+    q = np.stack([q0, q0 * np.float32(0.5), q0[::-1].copy()])
+    seq_start = np.array([0, 20, 20, 50], np.uint32)     # lengths 20, 0, 30
+    out, bound = orc.attn_decode_varlen(q, seq_start, k, v, 0.3)
+    np.testing.assert_array_equal(out[0], orc.attn_decode(q[0], k[:20], v[:20], 0.3)[0])
+    np.testing.assert_array_equal(out[1], 0.0)
+    np.testing.assert_array_equal(bound[1], 0.0)
+    np.testing.assert_array_equal(out[2], orc.attn_decode(q[2], k[20:], v[20:], 0.3)[0])
