@@ -269,3 +269,27 @@ def test_varlen_int4(gs):
     print(f"varlen int4 gs={gs}: max |err|/sum p|v| = {worst:.3e}", flush=True)
     assert np.all(np.isfinite(got)) and worst <= RTOL
     assert np.all(got[0] == 0.0)
+
+
+def test_varlen_bench_workload():
+    """The timed batch: 16 sequences of 1024..4096 tokens (lengths drawn with
+    seed 17), 8 KV heads, 32 query heads, head_dim 128, default scale, with
+    the workspace (split chunks and the merge launch), every output checked."""
+    lengths = [int(n) for n in np.random.default_rng(17).integers(1024, 4097, 16)]
+    hkv, hq, d = 8, 32, 128
+    print_case("attn int8 varlen timed batch", sum(lengths))
+    ttot = sum(lengths)
+    _, k, v = synth.attn_decode(ttot, hkv, hq, d, seed=19)
+    qb = np.stack([synth.attn_decode(1, 1, hq, d, seed=20 + b)[0] for b in range(len(lengths))])
+    seq_start = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    kc, ks = _quant8(k)
+    vc, vs = _quant8(v)
+    kh = _oracle.kv_int8_dequant(kc.reshape(-1, d), ks.reshape(-1)).reshape(kc.shape)
+    vh = _oracle.kv_int8_dequant(vc.reshape(-1, d), vs.reshape(-1)).reshape(vc.shape)
+    ref, bound = _oracle.attn_decode_varlen(qb, seq_start, kh, vh, 1.0 / math.sqrt(d))
+    got = host(api.attn_decode_int8_varlen(dev(qb), dev(seq_start), max(lengths), dev(kc), dev(ks), dev(vc),
+                                           dev(vs)))
+    torch.cuda.synchronize()
+    worst = float((np.abs(got.astype(np.float64) - ref) / np.maximum(bound, 1e-30)).max())
+    print(f"varlen timed batch: max |err|/sum p|v| = {worst:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and worst <= RTOL
