@@ -38,7 +38,7 @@ def test_act_quant_rowscale_qkv_shape(m):
     _act_case(inp.x_bf16[:m], 4096, 0)
 
 
-@pytest.mark.parametrize("m", [64, 256])
+@pytest.mark.parametrize("m", [64, 128, 256])
 @pytest.mark.parametrize("with_up", [False, True])
 def test_act_quant_g128_silu_down_shape(m, with_up):
     print_case("act g128 silu down", m, with_up)
