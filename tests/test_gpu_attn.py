@@ -275,8 +275,10 @@ def test_varlen_bench_workload():
     """The timed batch: 16 sequences of 1024..4096 tokens (lengths drawn with
     seed 17), 8 KV heads, 32 query heads, head_dim 128, default scale, with
     the workspace (split chunks and the merge launch), every output checked."""
-    lengths = [int(n) for n in np.random.default_rng(17).integers(1024, 4097, 16)]
-    hkv, hq, d = 8, 32, 128
+    import bench
+
+    lengths, hkv, hq, d = list(bench.ATTN_LENS), bench.ATTN_HKV, bench.ATTN_HQ, bench.ATTN_D
+    assert len(lengths) == 16 and (hkv, hq, d) == (8, 32, 128) and 1024 <= min(lengths) <= max(lengths) <= 4096
     print_case("attn int8 varlen timed batch", sum(lengths))
     ttot = sum(lengths)
     _, k, v = synth.attn_decode(ttot, hkv, hq, d, seed=19)
