@@ -12,12 +12,20 @@ shape, on one set of synthetic inputs already resident in HBM:
   INT4 AWQ fused QKV (K=4096, N=4096+1024+1024, g128): GEMV/GEMM at M = 1, 16, 128
 
 The step is captured once per input set in a HIP graph; the timed region
-replays K step graphs, rotating over enough input sets (>= 512 MB in total)
+replays K step graphs, rotating over input sets of >= 768 MiB in total, so
 that no step finds its data in the 256 MB MALL.  value = sum of the
-algorithmic bytes of all kernels / step time.  Each kernel is also timed
-alone (a graph of R launches rotating over the sets, HIP events on the launch
-stream, median of 5 replays) for the per-kernel breakdown and the roofline of
-the dominant kernel.
+algorithmic bytes of all kernels / step time.
+
+Each kernel is also timed alone, cold: a graph of R launches over
+ceil(512 MiB / working set) copies of that kernel's own inputs and outputs
+(R >= 100, a multiple of the copy count), HIP events on the launch stream,
+median of 5 replays.  ``us_warm`` repeats one copy.  The dominant kernel's
+roofline comes from its cold time.
+
+``--only NAME`` times one kernel cold and nothing else (after five 256 MiB
+device copies that calibrate the traffic counters): the command the
+rocprofv3 kernel-trace and FETCH_SIZE / WRITE_SIZE summaries under profiles/
+are taken with.
 
 Prints ONE JSON line.  --gpus N with N > 1 exits: every kernel here runs on
 one GPU.
@@ -27,6 +35,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -43,6 +52,11 @@ DOWN_K, DOWN_N = 14336, 4096
 AWQ_K, AWQ_NS, AWQ_GS = 4096, (4096, 1024, 1024), 128
 QKV_MS, DOWN_MS, AWQ_MS = (1, 8, 32), (64, 128, 256), (1, 16, 128)
 FUSED_MAX_ROWS = 8             # w8a8_proj is one launch up to this many rows
+
+COLD_BYTES = 512 << 20         # per-kernel rotation: at least this many bytes of copies
+STEP_ROTATION = 768 << 20      # step rotation: at least this many bytes of input sets
+MAX_COPIES = 4096              # copies of a tiny kernel's working set (then R = copies)
+COPY_CALIB_MIB = 256           # device copy that calibrates FETCH_SIZE / WRITE_SIZE
 
 
 # ----------------------------------------------------------- work model ---
@@ -73,16 +87,14 @@ def kernel_table():
         rows.append((f"w8a8_gemm_blk128_M{m}",
                      DOWN_N * DOWN_K + (DOWN_N // 128) * kb * 4 + m * DOWN_K + m * kb * 4 + m * DOWN_N * 2,
                      2 * m * DOWN_N * DOWN_K, "fp8"))
-    na = sum(AWQ_NS)
     for m in AWQ_MS:
-        rows.append((f"int4_awq_qkv_M{m}",
-                     AWQ_K * na // 2 + 2 * (AWQ_K // AWQ_GS) * na * 4 + m * AWQ_K * 4 + m * na * 4,
-                     2 * m * na * AWQ_K, "fp16"))
+        rows.append((f"int4_awq_qkv_M{m}", awq_bytes(m), 2 * m * sum(AWQ_NS) * AWQ_K, "fp16"))
     return rows
 
 
-AWQ_EXTRA_MS = (4, 8)
+AWQ_EXTRA_MS = (2, 4, 8)
 AWQ_F16X_MS = (1, 16, 128)   # INT4 AWQ with fp16 activations, beside the step
+C1_K = C1_N = 512             # INT4 single projection (one group of 128 per 128 K rows)
 # decode attention over the INT8 cache, beside the step: 4096 tokens x 8 KV
 # heads x 128 (the 32768 x 128 cache), 32 query heads
 ATTN_T, ATTN_HKV, ATTN_HQ, ATTN_D = 4096, 8, 32, 128
@@ -97,25 +109,30 @@ def attn_bytes(int4=False):
     return 2 * cache + 2 * ATTN_HQ * ATTN_D * 4
 
 
-def awq_bytes(m, xbytes=4):
-    na = sum(AWQ_NS)
-    return AWQ_K * na // 2 + 2 * (AWQ_K // AWQ_GS) * na * 4 + m * AWQ_K * xbytes + m * na * 4
+def awq_bytes(m, xbytes=4, k=AWQ_K, ns=AWQ_NS, gs=AWQ_GS):
+    na = sum(ns)
+    return k * na // 2 + 2 * (k // gs) * na * 4 + m * k * xbytes + m * na * 4
 
 
 def extra_table():
-    """Kernels timed beside the step but not part of it (widenings of the
-    path: per-tensor KV mode, bf16 KV caches, INT4 at M between the
-    configurations and with fp16 activations, decode attention over the INT8
-    cache): (name, bytes, flops, kind)."""
+    """Kernels timed beside the step but not part of it: the single INT4
+    projection (launch-bound: 152 KB), the SwiGLU form of the down
+    projection's activation quantization, the per-tensor KV mode, bf16 KV
+    caches, INT4 at M between the configurations and with fp16 activations,
+    decode attention over the quantized cache: (name, bytes, flops, kind)."""
     kv = KV_T * KV_D * 4 + KV_T * KV_D + 4
     n = KV_T * KV_D
     g = n // KV_GS
     na = sum(AWQ_NS)
-    rows = [("kv_int8_quant_tensor", kv, 0, "hbm"), ("kv_int8_dequant_tensor", kv, 0, "hbm"),
-            ("kv_int8_quant_bf16", n * 2 + n + KV_T * 4, 0, "hbm"),
-            ("kv_int8_dequant_bf16", n * 2 + n + KV_T * 4, 0, "hbm"),
-            ("kv_int4_quant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm"),
-            ("kv_int4_dequant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm")]
+    kb = DOWN_K // 128
+    rows = [("int4_awq_single_512_M1", awq_bytes(1, k=C1_K, ns=(C1_N,)), 2 * C1_K * C1_N, "fp16")]
+    rows += [(f"w8a8_act_quant_swiglu_g128_M{m}", m * DOWN_K * 4 + m * DOWN_K + m * kb * 4, 0, "hbm")
+             for m in DOWN_MS]
+    rows += [("kv_int8_quant_tensor", kv, 0, "hbm"), ("kv_int8_dequant_tensor", kv, 0, "hbm"),
+             ("kv_int8_quant_bf16", n * 2 + n + KV_T * 4, 0, "hbm"),
+             ("kv_int8_dequant_bf16", n * 2 + n + KV_T * 4, 0, "hbm"),
+             ("kv_int4_quant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm"),
+             ("kv_int4_dequant_bf16", n * 2 + n // 2 + g * 8, 0, "hbm")]
     rows += [(f"int4_awq_qkv_M{m}", awq_bytes(m), 2 * m * na * AWQ_K, "fp16") for m in AWQ_EXTRA_MS]
     rows += [(f"int4_awq_qkv_f16x_M{m}", awq_bytes(m, 2), 2 * m * na * AWQ_K, "fp16") for m in AWQ_F16X_MS]
     rows += [(f"attn_decode_int8_T{ATTN_T}", attn_bytes(), 0, "hbm"),   # HBM-bound: vector ALU products
@@ -124,6 +141,10 @@ def extra_table():
     rows += [(f"attn_decode_int8_varlen_B{ATTN_B}", 2 * vrows * (ATTN_D + 4) + 2 * ATTN_B * ATTN_HQ * ATTN_D * 4
               + (ATTN_B + 1) * 4, 0, "hbm")]
     return rows
+
+
+# kernels whose time is launch latency, not a bandwidth or arithmetic figure
+LAUNCH_BOUND = {"int4_awq_single_512_M1", "w8a8_act_quant_row_M32"}
 
 
 def roofline_for(name, nbytes, flops, kind, seconds):
@@ -137,6 +158,15 @@ def roofline_for(name, nbytes, flops, kind, seconds):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def cold_plan(ws_bytes, reps):
+    """(copies, launches) for a cold timing: enough copies of the working set
+    to span COLD_BYTES (at most MAX_COPIES), and at least `reps` launches, a
+    whole number of passes over the copies."""
+    copies = max(1, min(MAX_COPIES, -(-COLD_BYTES // max(ws_bytes, 1))))
+    launches = copies * max(1, -(-reps // copies))
+    return copies, launches
+
+
 # -------------------------------------------------------------- inputs ----
 
 def make_inputs(torch, api, synth):
@@ -147,14 +177,18 @@ def make_inputs(torch, api, synth):
     qkv = synth.w8a8_qkv(seed=3)
     s["qkv_x"] = dev(qkv.x_bf16.view(np.int16)).view(torch.bfloat16)
     s["qkv_w"] = [api.weight_quant(dev(w), api.ROWSCALE) for w in qkv.weights]
-    down = synth.w8a8_down(seed=4)
+    down = synth.w8a8_down(seed=4, with_up=True)
     s["down_x"] = dev(down.x_bf16.view(np.int16)).view(torch.bfloat16)
+    s["down_up"] = dev(down.up_bf16.view(np.int16)).view(torch.bfloat16)
     s["down_w"] = [api.weight_quant(dev(w), api.BLK128) for w in down.weights]
     x5, projs = synth.int4_qkv(seed=5)
     s["awq_x"] = dev(x5)
     s["awq_x16"] = s["awq_x"].to(torch.float16)
     s["kv_x16"] = s["kv_x"].to(torch.bfloat16)
     s["awq_p"] = [(dev(p.qweight.view(np.int32)), dev(p.scales), dev(p.zeros)) for p in projs]
+    x1, p1 = synth.int4_gemv_512(seed=1)
+    s["c1_x"] = dev(x1)
+    s["c1_p"] = [(dev(p.qweight.view(np.int32)), dev(p.scales), dev(p.zeros)) for p in p1]
     aq, ak, av = synth.attn_decode(ATTN_T, ATTN_HKV, ATTN_HQ, ATTN_D, seed=11)
     s["attn_q"] = dev(aq)
     rows = ATTN_T * ATTN_HKV
@@ -179,6 +213,30 @@ def make_inputs(torch, api, synth):
     return s, (qkv, down, x5, projs)
 
 
+def clone_arg(a, api):
+    """A copy of one launch argument: tensors cloned (a view becomes a
+    compact copy of what it shows), weights segment by segment."""
+    import torch
+    if isinstance(a, torch.Tensor):
+        return a.clone()
+    if isinstance(a, api.W8a8Weight):
+        return api.W8a8Weight(a.kind, [(c.clone(), s.clone()) for c, s in a.segments])
+    if isinstance(a, (list, tuple)):
+        return type(a)(clone_arg(x, api) for x in a)
+    return a
+
+
+def arg_bytes(a, api):
+    import torch
+    if isinstance(a, torch.Tensor):
+        return a.numel() * a.element_size()
+    if isinstance(a, api.W8a8Weight):
+        return sum(arg_bytes(list(seg), api) for seg in a.segments)
+    if isinstance(a, (list, tuple)):
+        return sum(arg_bytes(x, api) for x in a)
+    return 0
+
+
 def clone_set(torch, s):
     c = {}
     for k, v in s.items():
@@ -190,7 +248,11 @@ def clone_set(torch, s):
 
 
 class StepBuffers:
-    """Outputs and scratch for one input set, allocated before capture."""
+    """Outputs and scratch for one input set, allocated before capture.
+
+    launchers() / extra_launchers() give (name, fn, args): fn(*args) issues
+    exactly one call of the library, and args are every tensor it touches
+    (inputs and outputs), so a cold timing can rotate over copies of them."""
 
     def __init__(self, torch, api, s):
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
@@ -213,8 +275,9 @@ class StepBuffers:
         self.kv16_s4 = e((g,), torch.float32)
         self.kv16_z4 = e((g,), torch.float32)
         self.kv16_y4 = e((KV_T, KV_D), torch.bfloat16)
-        self.awqx_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_EXTRA_MS + (1, 16)}
+        self.awqx_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_EXTRA_MS}
         self.awq16_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_F16X_MS}
+        self.c1_out = [e((1, C1_N), torch.float32)]
         self.attn_out = e((ATTN_HQ, ATTN_D), torch.float32)
         self.attnv_out = e((ATTN_B, ATTN_HQ, ATTN_D), torch.float32)
         self.qkv_weight = api.W8a8Weight(api.ROWSCALE, s["qkv_w"])
@@ -225,6 +288,8 @@ class StepBuffers:
         self.down_q = {m: e((m, DOWN_K), torch.uint8) for m in DOWN_MS}
         self.down_sa = {m: e((m, DOWN_K // 128), torch.float32) for m in DOWN_MS}
         self.down_out = {m: e((m, DOWN_N), torch.bfloat16) for m in DOWN_MS}
+        self.sw_q = {m: e((m, DOWN_K), torch.uint8) for m in DOWN_MS}
+        self.sw_sa = {m: e((m, DOWN_K // 128), torch.float32) for m in DOWN_MS}
         self.awq_out = {m: [e((m, n), torch.float32) for n in AWQ_NS] for m in AWQ_MS}
 
     def outputs(self):
@@ -235,66 +300,79 @@ class StepBuffers:
             out += self.awq_out[m]
         return out
 
-    def extra_launchers(self, api):
-        s = self.s
-        L = [("kv_int8_quant_tensor", lambda: api.quant_int8_tensor(s["kv_x"], self.kvt_codes, self.kvt_scale)),
-             ("kv_int8_dequant_tensor", lambda: api.dequant_int8_tensor(self.kvt_codes, self.kvt_scale, self.kvt_y)),
-             ("kv_int8_quant_bf16", lambda: api.quant_int8_token(s["kv_x16"], self.kv16_codes, self.kv16_scales)),
-             ("kv_int8_dequant_bf16", lambda: api.dequant_int8_token(self.kv16_codes, self.kv16_scales,
-                                                                     self.kv16_y)),
-             ("kv_int4_quant_bf16", lambda: api.quant_int4_group(s["kv_x16"], KV_GS, self.kv16_packed, self.kv16_s4,
-                                                                 self.kv16_z4)),
-             ("kv_int4_dequant_bf16", lambda: api.dequant_int4_group(self.kv16_packed, self.kv16_s4, self.kv16_z4,
-                                                                     KV_T, KV_D, KV_GS, self.kv16_y4))]
-        for m in AWQ_EXTRA_MS:
-            L.append((f"int4_awq_qkv_M{m}", lambda m=m: api.int4_awq_qkv(s["awq_x"][:m], s["awq_p"], AWQ_GS,
-                                                                          outs=self.awqx_out[m])))
-        for m in AWQ_F16X_MS:
-            L.append((f"int4_awq_qkv_f16x_M{m}", lambda m=m: api.int4_awq_qkv(s["awq_x16"][:m], s["awq_p"], AWQ_GS,
-                                                                               outs=self.awq16_out[m])))
-        L.append((f"attn_decode_int8_T{ATTN_T}", lambda: api.attn_decode_int8(s["attn_q"], s["attn_kc"], s["attn_ks"],
-                                                                             s["attn_vc"], s["attn_vs"],
-                                                                             out=self.attn_out)))
-        L.append((f"attn_decode_int4_g{KV_GS}_T{ATTN_T}",
-                  lambda: api.attn_decode_int4(s["attn_q"], KV_GS, s["attn_kp4"], s["attn_ks4"], s["attn_kz4"],
-                                               s["attn_vp4"], s["attn_vs4"], s["attn_vz4"], out=self.attn_out)))
-        L.append((f"attn_decode_int8_varlen_B{ATTN_B}",
-                  lambda: api.attn_decode_int8_varlen(s["attnv_q"], s["attnv_start"], max(ATTN_LENS), s["attnv_kc"],
-                                                      s["attnv_ks"], s["attnv_vc"], s["attnv_vs"],
-                                                      out=self.attnv_out)))
-        return L
-
-    # each launcher issues exactly one call
     def launchers(self, api):
         s = self.s
         L = []
-        L.append(("kv_int8_quant", lambda: api.quant_int8_token(s["kv_x"], self.kv_codes, self.kv_scales)))
-        L.append(("kv_int8_dequant", lambda: api.dequant_int8_token(self.kv_codes, self.kv_scales, self.kv_y8)))
-        L.append(("kv_int4_quant", lambda: api.quant_int4_group(s["kv_x"], KV_GS, self.kv_packed, self.kv_s4,
-                                                                 self.kv_z4)))
-        L.append(("kv_int4_dequant", lambda: api.dequant_int4_group(self.kv_packed, self.kv_s4, self.kv_z4, KV_T,
-                                                                     KV_D, KV_GS, self.kv_y4)))
+        L.append(("kv_int8_quant", lambda x, c, sc: api.quant_int8_token(x, c, sc),
+                  (s["kv_x"], self.kv_codes, self.kv_scales)))
+        L.append(("kv_int8_dequant", lambda c, sc, y: api.dequant_int8_token(c, sc, y),
+                  (self.kv_codes, self.kv_scales, self.kv_y8)))
+        L.append(("kv_int4_quant", lambda x, p, sc, z: api.quant_int4_group(x, KV_GS, p, sc, z),
+                  (s["kv_x"], self.kv_packed, self.kv_s4, self.kv_z4)))
+        L.append(("kv_int4_dequant", lambda p, sc, z, y: api.dequant_int4_group(p, sc, z, KV_T, KV_D, KV_GS, y),
+                  (self.kv_packed, self.kv_s4, self.kv_z4, self.kv_y4)))
         for m in QKV_MS:
             if m <= FUSED_MAX_ROWS:
                 L.append((f"w8a8_proj_rowscale_M{m}",
-                          lambda m=m: api.proj(s["qkv_x"][:m], self.qkv_weight, out=self.qkv_out[m],
-                                               scratch=(self.qkv_q[m], self.qkv_sa[m]))))
+                          lambda x, w, o, q, sa: api.proj(x, w, out=o, scratch=(q, sa)),
+                          (s["qkv_x"][:m], self.qkv_weight, self.qkv_out[m], self.qkv_q[m], self.qkv_sa[m])))
                 continue
             L.append((f"w8a8_act_quant_row_M{m}",
-                      lambda m=m: api.act_quant(s["qkv_x"][:m], QKV_K, api.ROWSCALE, False, None, self.qkv_q[m],
-                                                self.qkv_sa[m])))
-            L.append((f"w8a8_gemv_rowscale_M{m}",
-                      lambda m=m: api.gemv(self.qkv_q[m], self.qkv_sa[m], self.qkv_weight, out=self.qkv_out[m])))
+                      lambda x, q, sa: api.act_quant(x, QKV_K, api.ROWSCALE, False, None, q, sa),
+                      (s["qkv_x"][:m], self.qkv_q[m], self.qkv_sa[m])))
+            L.append((f"w8a8_gemv_rowscale_M{m}", lambda q, sa, w, o: api.gemv(q, sa, w, out=o),
+                      (self.qkv_q[m], self.qkv_sa[m], self.qkv_weight, self.qkv_out[m])))
         for m in DOWN_MS:
             L.append((f"w8a8_act_quant_silu_g128_M{m}",
-                      lambda m=m: api.act_quant(s["down_x"][:m], DOWN_K, api.BLK128, True, None, self.down_q[m],
-                                                self.down_sa[m])))
-            L.append((f"w8a8_gemm_blk128_M{m}",
-                      lambda m=m: api.gemv(self.down_q[m], self.down_sa[m], self.down_weight,
-                                           out=self.down_out[m])))
+                      lambda x, q, sa: api.act_quant(x, DOWN_K, api.BLK128, True, None, q, sa),
+                      (s["down_x"][:m], self.down_q[m], self.down_sa[m])))
+            L.append((f"w8a8_gemm_blk128_M{m}", lambda q, sa, w, o: api.gemv(q, sa, w, out=o),
+                      (self.down_q[m], self.down_sa[m], self.down_weight, self.down_out[m])))
         for m in AWQ_MS:
-            L.append((f"int4_awq_qkv_M{m}",
-                      lambda m=m: api.int4_awq_qkv(s["awq_x"][:m], s["awq_p"], AWQ_GS, outs=self.awq_out[m])))
+            L.append((f"int4_awq_qkv_M{m}", lambda x, p, o: api.int4_awq_qkv(x, p, AWQ_GS, outs=o),
+                      (s["awq_x"][:m], s["awq_p"], self.awq_out[m])))
+        return L
+
+    def extra_launchers(self, api):
+        s = self.s
+        L = [("int4_awq_single_512_M1", lambda x, p, o: api.int4_awq_qkv(x, p, 128, outs=o),
+              (s["c1_x"], s["c1_p"], self.c1_out))]
+        for m in DOWN_MS:
+            L.append((f"w8a8_act_quant_swiglu_g128_M{m}",
+                      lambda x, u, q, sa: api.act_quant(x, DOWN_K, api.BLK128, True, u, q, sa),
+                      (s["down_x"][:m], s["down_up"][:m], self.sw_q[m], self.sw_sa[m])))
+        L += [("kv_int8_quant_tensor", lambda x, c, sc: api.quant_int8_tensor(x, c, sc),
+               (s["kv_x"], self.kvt_codes, self.kvt_scale)),
+              ("kv_int8_dequant_tensor", lambda c, sc, y: api.dequant_int8_tensor(c, sc, y),
+               (self.kvt_codes, self.kvt_scale, self.kvt_y)),
+              ("kv_int8_quant_bf16", lambda x, c, sc: api.quant_int8_token(x, c, sc),
+               (s["kv_x16"], self.kv16_codes, self.kv16_scales)),
+              ("kv_int8_dequant_bf16", lambda c, sc, y: api.dequant_int8_token(c, sc, y),
+               (self.kv16_codes, self.kv16_scales, self.kv16_y)),
+              ("kv_int4_quant_bf16", lambda x, p, sc, z: api.quant_int4_group(x, KV_GS, p, sc, z),
+               (s["kv_x16"], self.kv16_packed, self.kv16_s4, self.kv16_z4)),
+              ("kv_int4_dequant_bf16",
+               lambda p, sc, z, y: api.dequant_int4_group(p, sc, z, KV_T, KV_D, KV_GS, y),
+               (self.kv16_packed, self.kv16_s4, self.kv16_z4, self.kv16_y4))]
+        for m in AWQ_EXTRA_MS:
+            L.append((f"int4_awq_qkv_M{m}", lambda x, p, o: api.int4_awq_qkv(x, p, AWQ_GS, outs=o),
+                      (s["awq_x"][:m], s["awq_p"], self.awqx_out[m])))
+        for m in AWQ_F16X_MS:
+            L.append((f"int4_awq_qkv_f16x_M{m}", lambda x, p, o: api.int4_awq_qkv(x, p, AWQ_GS, outs=o),
+                      (s["awq_x16"][:m], s["awq_p"], self.awq16_out[m])))
+        L.append((f"attn_decode_int8_T{ATTN_T}",
+                  lambda q, kc, ks, vc, vs, o: api.attn_decode_int8(q, kc, ks, vc, vs, out=o),
+                  (s["attn_q"], s["attn_kc"], s["attn_ks"], s["attn_vc"], s["attn_vs"], self.attn_out)))
+        L.append((f"attn_decode_int4_g{KV_GS}_T{ATTN_T}",
+                  lambda q, kp, ks, kz, vp, vs, vz, o: api.attn_decode_int4(q, KV_GS, kp, ks, kz, vp, vs, vz,
+                                                                             out=o),
+                  (s["attn_q"], s["attn_kp4"], s["attn_ks4"], s["attn_kz4"], s["attn_vp4"], s["attn_vs4"],
+                   s["attn_vz4"], self.attn_out)))
+        L.append((f"attn_decode_int8_varlen_B{ATTN_B}",
+                  lambda q, st, kc, ks, vc, vs, o: api.attn_decode_int8_varlen(q, st, max(ATTN_LENS), kc, ks, vc,
+                                                                               vs, out=o),
+                  (s["attnv_q"], s["attnv_start"], s["attnv_kc"], s["attnv_ks"], s["attnv_vc"], s["attnv_vs"],
+                   self.attnv_out)))
         return L
 
 
@@ -307,16 +385,46 @@ def capture(torch, fns, stream):
     return g
 
 
-# ---------------------------------------------------------- cpu baseline --
+def per_launch(torch, fns, stream, replays=5):
+    """Seconds per launch: one graph of the launches, replayed once to warm
+    up, then the median of `replays` timed replays (HIP events recorded on
+    the stream the kernels run on)."""
+    g = capture(torch, fns, stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(replays)]
+        for a, b in ev:
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return sorted(a.elapsed_time(b) for a, b in ev)[replays // 2] / len(fns) / 1e3
 
-# HBM traffic of the dominant call (fetched + written bytes), from rocprofv3
-# --pmc FETCH_SIZE and WRITE_SIZE passes over kv_quantization_amd/
-# traffic_probe.py, scaled by what the same counters read for a 256 MiB
-# device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Reported only while the
-# GEMM source (comments aside) is the one the counters were taken on.
-TRAFFIC = {"kernel": "w8a8_gemm_blk128_M256", "bytes": 136316069,
-           "source": "kv_quantization_amd/csrc/w8a8_gemm.hip",
-           "sha256": "b726fabd67eb798d13491df72e134473203496b71d443563902c6727647a8d17"}
+
+def time_cold(torch, api, fn, args, stream, reps):
+    """Cold per-launch seconds over rotating copies of the launch's own
+    arguments, and the plan used: (seconds, copies, launches, ws bytes)."""
+    ws = arg_bytes(args, api)
+    copies, launches = cold_plan(ws, reps)
+    pool = [args] + [clone_arg(args, api) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    sec = per_launch(torch, [lambda a=pool[r % copies]: fn(*a) for r in range(launches)], stream)
+    del pool
+    return sec, copies, launches, ws
+
+
+# ------------------------------------------------------------ traffic -----
+
+# HBM traffic per call (fetched + written bytes) of the dominant kernel, from
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes over `bench.py --only
+# <kernel>`, each scaled by what the counter reads for a 256 MiB device copy.
+# Reported only while every listed source (comments aside) is the one the
+# counters were taken on.
+TRAFFIC = {"w8a8_gemm_blk128_M256": {"bytes": 136316069,
+                                     "sources": {"kv_quantization_amd/csrc/w8a8_gemm.hip":
+                                                 "b726fabd67eb798d13491df72e134473203496b71d443563902c6727647a8d17"}}}
 
 
 def code_digest(path):
@@ -330,15 +438,33 @@ def code_digest(path):
 
 
 def measured_traffic(kernel):
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC["source"])
-    try:
-        digest = code_digest(path)
-    except OSError:
+    entry = TRAFFIC.get(kernel)
+    if entry is None:
         return None
-    return TRAFFIC["bytes"] if kernel == TRAFFIC["kernel"] and digest == TRAFFIC["sha256"] else None
+    root = os.path.dirname(os.path.abspath(__file__))
+    for src, digest in entry["sources"].items():
+        try:
+            if code_digest(os.path.join(root, src)) != digest:
+                return None
+        except OSError:
+            return None
+    return entry["bytes"]
 
+
+# ---------------------------------------------------------- cpu baseline --
 
 CPU_SECONDS = 10.0
+
+
+def cpu_model():
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return "unknown"
 
 
 def cpu_baseline(host_inputs, table, single_core=True):
@@ -352,6 +478,7 @@ def cpu_baseline(host_inputs, table, single_core=True):
     wq = [oracle.weight_quant(oracle.ROWSCALE, w) for w in qkv.weights]
     wd = [oracle.weight_quant(oracle.BLK128, w) for w in down.weights]
     awq = [(p.qweight, p.scales, p.zeros) for p in projs]
+
     def one_step():
         c8, s8 = oracle.kv_int8_quant(kv_x)
         oracle.kv_int8_dequant(c8, s8)
@@ -376,6 +503,7 @@ def cpu_baseline(host_inputs, table, single_core=True):
     total = sum(r[1] for r in table) * steps
     cores = oracle.num_threads()
     res = {"value": round(total / seconds / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "cpu": cpu_model(),
            "sample": "%d full steps on the same inputs (every kernel at every M; products as fp64 numpy "
                      "matmuls), offline weight quantization excluded, %.1f s" % (steps, seconds)}
     if single_core:
@@ -401,16 +529,45 @@ def tensors_of(s):
 
 # ------------------------------------------------------------------ main --
 
+def run_only(torch, api, name, reps, stream, log):
+    """Time one kernel cold, nothing else (profiler runs)."""
+    src = torch.empty(COPY_CALIB_MIB << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    del src, dst
+    from kv_quantization_amd import synth
+    base, _ = make_inputs(torch, api, synth)
+    bufs = StepBuffers(torch, api, base)
+    table = {r[0]: r for r in kernel_table() + extra_table()}
+    launch = {n: (f, a) for n, f, a in bufs.launchers(api) + bufs.extra_launchers(api)}
+    if name not in launch:
+        print(f"bench.py: unknown kernel {name!r}; one of: {', '.join(launch)}", file=sys.stderr)
+        sys.exit(2)
+    fn, args = launch[name]
+    with torch.cuda.stream(stream):
+        fn(*args)                      # eager: allocates the workspace
+    torch.cuda.synchronize()
+    log(f"timing {name} cold")
+    sec, copies, launches, ws = time_cold(torch, api, fn, args, stream, reps)
+    _, nbytes, flops, kind = table[name]
+    print(json.dumps({"kernel": name, "us": round(sec * 1e6, 2), "copies": copies, "launches": launches,
+                      "working_set_bytes": ws, "algorithmic_bytes": nbytes,
+                      "roofline": roofline_for(name, nbytes, flops, kind, sec)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough for >= 512 MB)")
-    ap.add_argument("--kernel-reps", type=int, default=100, help="launches per isolated kernel timing")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated by the step (0: >= 768 MiB of them)")
+    ap.add_argument("--kernel-reps", type=int, default=100, help="least launches per isolated kernel timing")
+    ap.add_argument("--only", default=None, help="time this one kernel cold and nothing else")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single-core", action="store_true", help="skip the one-thread oracle step")
     ap.add_argument("--no-check", action="store_true", help="skip the graph-vs-eager self-check")
+    ap.add_argument("--no-extras", action="store_true", help="skip the kernels timed beside the step")
     ap.add_argument("--verbose", action="store_true")
     args = ap.parse_args()
 
@@ -425,6 +582,11 @@ def main():
     from kv_quantization_amd import api, synth
 
     log = (lambda *a: print(*a, file=sys.stderr, flush=True)) if args.verbose else (lambda *a: None)
+    stream = torch.cuda.Stream()
+    if args.only:
+        run_only(torch, api, args.only, args.kernel_reps, stream, log)
+        return
+
     table = kernel_table()
     names = [r[0] for r in table]
     step_bytes = sum(r[1] for r in table)
@@ -432,23 +594,22 @@ def main():
     log("generating inputs")
     base, host_inputs = make_inputs(torch, api, synth)
     set_bytes = sum(t.numel() * t.element_size() for t in tensors_of(base))
-    nsets = args.sets or max(2, -(-512 * 2 ** 20 // (set_bytes + 64 * 2 ** 20)))
+    nsets = args.sets or max(2, -(-STEP_ROTATION // set_bytes))
     sets = [base] + [clone_set(torch, base) for _ in range(nsets - 1)]
     bufs = [StepBuffers(torch, api, s) for s in sets]
     launch = [b.launchers(api) for b in bufs]
-    assert [n for n, _ in launch[0]] == names
-    xtable = extra_table()
-    xlaunch = [b.extra_launchers(api) for b in bufs]
-    assert [n for n, _ in xlaunch[0]] == [r[0] for r in xtable]
+    assert [n for n, _, _ in launch[0]] == names
+    xtable = [] if args.no_extras else extra_table()
+    xlaunch = bufs[0].extra_launchers(api) if xtable else []
+    assert [n for n, _, _ in xlaunch] == [r[0] for r in xtable]
 
-    stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for L in launch + xlaunch:          # eager pass: allocates workspaces, checks launches
-            for _, f in L:
-                f()
+        for L in launch + [xlaunch]:          # eager pass: allocates workspaces, checks launches
+            for _, f, a in L:
+                f(*a)
     torch.cuda.synchronize()
     log(f"{nsets} input sets of {set_bytes / 2**20:.0f} MiB; capturing")
-    step_graphs = [capture(torch, [f for _, f in L], stream) for L in launch]
+    step_graphs = [capture(torch, [lambda f=f, a=a: f(*a) for _, f, a in L], stream) for L in launch]
 
     # ---- timed region: exactly `steps` steps
     with torch.cuda.stream(stream):
@@ -463,42 +624,7 @@ def main():
         end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-
-    # ---- per-kernel durations (graphs of R launches rotating over the sets)
-    per_kernel = {}
-    reps = max(nsets, args.kernel_reps // nsets * nsets)
-    timed = [(name, launch, ki) for ki, name in enumerate(names)]
-    timed += [(r[0], xlaunch, ki) for ki, r in enumerate(xtable)]
-    def per_launch(fns, replays=5):
-        """Seconds per launch: one graph of the launches, replayed once to
-        warm up, then the median of `replays` timed replays."""
-        g = capture(torch, fns, stream)
-        with torch.cuda.stream(stream):
-            g.replay()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(replays)]
-            for a, b in ev:
-                a.record(stream)
-                g.replay()
-                b.record(stream)
-        torch.cuda.synchronize()
-        del g
-        return sorted(a.elapsed_time(b) for a, b in ev)[replays // 2] / len(fns) / 1e3
-
-    for name, lset, ki in timed:
-        per_kernel[name] = per_launch([lset[r % nsets][ki][1] for r in range(reps)])
-    # warm: the same input set every launch (what fits the 256 MB MALL stays there)
-    per_kernel_warm = {name: per_launch([lset[0][ki][1]] * reps) for name, lset, ki in timed}
-    # empirical read ceiling: a plain 16-byte-load read of each kernel's
-    # algorithmic byte count, rotating through 1 GiB so every read is cold
-    ceil_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    read_ceiling = {}
-    for nbytes in sorted({r[1] // 16 * 16 for r in table + xtable}):
-        slots = max(1, (1 << 30) // nbytes)
-        views = [ceil_buf[(r % slots) * nbytes:(r % slots + 1) * nbytes] for r in range(reps)]
-        read_ceiling[nbytes] = nbytes / per_launch([lambda v=v: api.stream_read(v, nbytes, sink) for v in views])
-    del ceil_buf
+    log(f"step {ms_per_step:.4f} ms")
 
     # ---- self-check: the replayed graphs (which share one cached workspace
     # across every kernel of a step) must give the same bits as an eager run
@@ -511,17 +637,45 @@ def main():
         snap = [t.clone() for t in bufs[0].outputs()]
         fresh = torch.cuda.Stream()
         with torch.cuda.stream(fresh):
-            for _, f in launch[0]:
-                f()
+            for _, f, a in launch[0]:
+                f(*a)
         torch.cuda.synchronize()
         bad = [i for i, (a, b) in enumerate(zip(snap, bufs[0].outputs())) if not torch.equal(a, b)]
         if bad:
             print(f"bench.py: graph replay differs from a fresh eager run in outputs {bad}", file=sys.stderr)
             sys.exit(1)
         check = "graph replay == fresh eager run, bit for bit"
+    del step_graphs
+    for b in bufs[1:]:
+        b.s = None
+    del sets[1:], bufs[1:], launch[1:]
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # ---- per-kernel durations: cold over copies of each kernel's own data, and warm
+    cold, warm = {}, {}
+    for name, f, a in launch[0] + xlaunch:
+        cold[name] = time_cold(torch, api, f, a, stream, args.kernel_reps)
+        warm[name] = per_launch(torch, [lambda f=f, a=a: f(*a)] * args.kernel_reps, stream)
+        torch.cuda.empty_cache()
+        log(f"{name}: cold {cold[name][0] * 1e6:.2f} us over {cold[name][1]} copies, "
+            f"warm {warm[name] * 1e6:.2f} us")
+
+    # empirical read ceiling: a plain 16-byte-load read of each kernel's
+    # algorithmic byte count, rotating through 1 GiB so every read is cold
+    ceil_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    read_ceiling = {}
+    for nbytes in sorted({r[1] // 16 * 16 for r in table + xtable}):
+        slots = max(1, (1 << 30) // nbytes)
+        reps = max(args.kernel_reps, min(slots, MAX_COPIES))
+        views = [ceil_buf[(r % slots) * nbytes:(r % slots + 1) * nbytes] for r in range(reps)]
+        read_ceiling[nbytes] = nbytes / per_launch(torch, [lambda v=v: api.stream_read(v, nbytes, sink)
+                                                           for v in views], stream)
+    del ceil_buf
 
     def entry_for(name, nbytes, flops, kind):
-        sec = per_kernel[name]
+        sec, copies, _, ws = cold[name]
         peak_tf = {"fp8": FP8_PEAK_TFLOPS, "fp16": FP16_PEAK_TFLOPS}.get(kind)
         floor = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (peak_tf * 1e12) if peak_tf else 0.0)
         e = {"kernel": name, "us": round(sec * 1e6, 2), "GB/s": round(nbytes / sec / 1e9, 1),
@@ -530,14 +684,17 @@ def main():
             e["TFLOP/s"] = round(flops / sec / 1e12, 2)
             e["mfma_frac"] = round(flops / sec / 1e12 / peak_tf, 4)
         e["attainable_frac"] = round(floor / sec, 4)       # roofline time min(peak, AI*BW) / measured
-        e["us_warm"] = round(per_kernel_warm[name] * 1e6, 2)
+        e["us_warm"] = round(warm[name] * 1e6, 2)
         e["read_ceiling_GB/s"] = round(read_ceiling[nbytes // 16 * 16] / 1e9, 1)
+        e["rotation_MB"] = round(copies * ws / 1e6, 1)
+        if name in LAUNCH_BOUND:
+            e["bound"] = "launch latency"
         return e
 
     breakdown = [entry_for(*r) for r in table]
     extras = [dict(entry_for(*r), in_step=False) for r in xtable]
-    dom = max(table, key=lambda r: per_kernel[r[0]])
-    roof = roofline_for(*dom, per_kernel[dom[0]])
+    dom = max(table, key=lambda r: cold[r[0]][0])
+    roof = roofline_for(*dom, cold[dom[0]][0])
     roof["kernel"] = dom[0]
     roof["traffic"] = measured_traffic(dom[0])
 
@@ -552,7 +709,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3+f16 MFMA, f32 quantizers",
+        "dtype": "e4m3+f16 MFMA, f32 quantizers and INT4 GEMV",
         "data": "synthetic",
         "config": {
             "workload": "decode hot-path pass: KV cache 32768x128 INT8 + INT4(g32) quant/dequant; W8A8 rowscale "
@@ -561,9 +718,12 @@ def main():
                         "M=64,128,256; INT4 AWQ fused QKV K=4096 N=6144 g128 M=1,16,128",
             "input_sets": nsets,
             "step_bytes": step_bytes,
-            "timing": "HIP graph per step, rotating input sets (no MALL reuse across steps); per kernel: "
-                      "us = graph of launches over rotating sets (cold), us_warm = same set every launch, "
-                      "read_ceiling = plain 16-byte-load read of the same byte count, cold",
+            "timing": "step: HIP graph per step over %d rotating input sets (%.0f MiB, > the 256 MB MALL); per "
+                      "kernel: us = cold, a graph of >= %d launches rotating over ceil(512 MiB / working set) "
+                      "copies of that kernel's own inputs and outputs (at most %d copies; rotation_MB per "
+                      "entry), us_warm = one copy every launch; read_ceiling = plain 16-byte-load read of the "
+                      "same byte count rotating through 1 GiB" % (nsets, nsets * set_bytes / 2**20,
+                                                                  args.kernel_reps, MAX_COPIES),
             "check": check,
         },
         "roofline": roof,

@@ -66,6 +66,11 @@ int kvq_abi_version(void);
  *   codes[t][d] = clamp(rint_half_even(x[t][d] / scale[t]), -128, 127)
  *   y[t][d] = (float)codes[t][d] * scale[t]
  *
+ * x / scale is the correctly rounded fp32 quotient: the kernels form it from
+ * the scale's reciprocal plus one fused correction, which gives the IEEE
+ * quotient's bits wherever a code depends on it (the same holds for every
+ * quantizer below).
+ *
  * x, y: fp32 [num_tokens][head_dim] row-major; codes: int8, same shape;
  * scales: fp32 [num_tokens].  num_tokens >= 1, head_dim >= 1.  Inputs must be
  * finite (NaN/Inf are outside the contract). */

@@ -41,16 +41,30 @@ def _empty(shape, dtype, like: torch.Tensor):
 # ------------------------------------------------------------ workspace ----
 
 _workspaces: dict = {}
+# Buffers replaced by a larger one.  They are never freed: a HIP graph
+# captured while one was current keeps its address and may be replayed later.
+_retired: list = []
 
 
 def workspace(device: torch.device, nbytes: int, stream: int) -> torch.Tensor:
     """A zero-filled device buffer of at least nbytes, cached per (device,
     stream).  The kernels leave the counter area at its start zero-filled and
     put partial results only behind it, so reuse by calls ordered on one
-    stream is safe."""
+    stream is safe.  A buffer is created or grown only outside graph capture
+    (the zero fill must run before the first kernel reads the counters);
+    inside a capture a call that needs a new or larger buffer raises: make
+    one eager call of that shape on the stream first."""
     key = (torch.device(device), stream)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                f"kv_quantization_amd: this call needs a workspace of {nbytes} bytes on stream {stream:#x}, "
+                "which cannot be allocated and zero-filled during graph capture; make one eager call of the "
+                "same shape on this stream before capturing")
+        if buf is not None:
+            _retired.append(buf)
+        # zero fill enqueued on the current stream, the one the kernels use
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = buf
     return buf

@@ -11,9 +11,13 @@
 // each lane writes its packed codes with one 4-byte (INT8) or 2-byte (INT4)
 // store.  Shapes the teams cannot tile fall back to one wave per unit.
 //
-// Numerics match the page operation for operation in fp32: IEEE division
-// (v_div_scale/fmas/fixup, never a reciprocal multiply), round-half-to-even
-// via v_rndne_f32, and no fused multiply-add (the library is built with
+// Numerics match the page's fp32 arithmetic: the scale itself is an IEEE
+// division; each element's quotient x / scale comes from the scale's
+// reciprocal (once per token or group), a product and one fused correction
+// (div_by_scale), which yields the correctly rounded IEEE quotient for every
+// pair these codecs form (a CPU test checks the sequence against IEEE
+// division), so the codes are those of a division; round-half-to-even via
+// v_rndne_f32; no other fused multiply-add (the library is built with
 // -ffp-contract=off).
 #include "kvq_common.h"
 

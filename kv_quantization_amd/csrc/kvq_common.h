@@ -150,9 +150,11 @@ __device__ __forceinline__ T pick(int p, T a0, T a1, T a2) {
 // quotients below 2^-70 here (s >= 1e-8), far under every code boundary
 // (E4M3's smallest half-step 2^-10, rint's 0.5), so the codes equal those
 // of an IEEE division.  The sequence turns -0 / s into +0, so zeros pass
-// through unchanged (E4M3 has a negative-zero code).  (Checked on 2e9 random
-// pairs: same sign always, and every value mismatch had a quotient below
-// 2^-82.)
+// through unchanged (E4M3 has a negative-zero code).  tests/
+// div_by_scale_check.c runs this sequence against IEEE division on the CPU
+// over ~40 million seeded pairs of the codecs' kinds plus every code
+// boundary: the quotients agree bit for bit except a few below 2^-80, which
+// keep their sign.
 __device__ __forceinline__ float div_by_scale(float v, float s, float y) {
     const float q = v * y;
     const float r = __builtin_fmaf(__builtin_fmaf(-q, s, v), y, q);

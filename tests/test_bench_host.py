@@ -43,16 +43,32 @@ def test_roofline_picks_the_binding_roof():
 
 
 def test_stored_traffic_only_for_the_measured_source(tmp_path):
-    assert bench.measured_traffic(bench.TRAFFIC["kernel"]) == bench.TRAFFIC["bytes"]
+    for kernel, entry in bench.TRAFFIC.items():
+        assert bench.measured_traffic(kernel) == entry["bytes"]
+        # comments do not change the digest, code does
+        for src, digest in entry["sources"].items():
+            text = (ROOT / src).read_text()
+            assert bench.code_digest(ROOT / src) == digest
+            probe = tmp_path / "probe.hip"
+            probe.write_text(text + "\n// a comment\n")
+            assert bench.code_digest(probe) == digest
+            probe.write_text(text + "\nint extra;\n")
+            assert bench.code_digest(probe) != digest
     assert bench.measured_traffic("kv_int8_quant") is None
-    # comments do not change the digest, code does
-    src = (ROOT / bench.TRAFFIC["source"]).read_text()
-    assert bench.code_digest(ROOT / bench.TRAFFIC["source"]) == bench.TRAFFIC["sha256"]
-    probe = tmp_path / "probe.hip"
-    probe.write_text(src + "\n// a comment\n")
-    assert bench.code_digest(probe) == bench.TRAFFIC["sha256"]
-    probe.write_text(src + "\nint extra;\n")
-    assert bench.code_digest(probe) != bench.TRAFFIC["sha256"]
+
+
+def test_cold_plan_spans_the_rotation():
+    # a 64.6 MB working set needs 9 copies for 512 MiB, launches a multiple of them
+    copies, launches = bench.cold_plan(64_616_448, 100)
+    assert copies == 9 and launches % copies == 0 and launches >= 100
+    assert copies * 64_616_448 >= bench.COLD_BYTES
+    # a tiny working set: as many copies as allowed, one pass
+    copies, launches = bench.cold_plan(12_292, 100)
+    assert copies == bench.MAX_COPIES and launches == copies
+    # every kernel of the step and beside it gets a plan covering 512 MiB or MAX_COPIES copies
+    for name, nbytes, _, _ in bench.kernel_table() + bench.extra_table():
+        c, n = bench.cold_plan(nbytes, 100)
+        assert c * nbytes >= bench.COLD_BYTES or c == bench.MAX_COPIES, name
 
 
 @pytest.mark.parametrize("n", ["2", "8"])

@@ -9,7 +9,7 @@ import torch
 
 from conftest import print_case
 from gpu_util import assert_canary, dev, host, poisoned
-from kv_quantization_amd import api, synth
+from kv_quantization_amd import _lib, api, synth
 
 pytestmark = pytest.mark.gpu
 RTOL = 1e-3
@@ -45,6 +45,12 @@ def _check(out_bf16, ref, bound, what, strict=False):
     assert not over.any(), f"{what}: {int(over.sum())} outputs beyond tolerance, worst ratio {worst:.3e}"
     if strict:
         assert worst <= RTOL, f"{what}: {int((ratio > RTOL).sum())} outputs beyond 1e-3, worst {worst:.3e}"
+
+
+def _expect_invalid(call, text):
+    with pytest.raises(_lib.KvqError) as e:
+        call()
+    assert e.value.status == _lib.KVQ_E_INVALID and text in str(e.value), str(e.value)
 
 
 def _case(kind, x_bf16, k, ws, rows, silu=False, up=None, ldc_pad=0, what="", strict=False):
@@ -106,10 +112,13 @@ def test_row_counts(kind, rows):
 @pytest.mark.parametrize("seg_n,k", [((1,), 128), ((7,), 256), ((16, 1), 128), ((128,), 128), ((64, 64, 64), 512),
                                      ((2048,), 1024)])
 def test_segment_shapes(kind, seg_n, k):
-    if kind == 1 and any(n % 128 for n in seg_n[:-1]):
-        pytest.skip("BLK128 needs 128-aligned non-last segments")
     print_case("w8a8 segments", kind, seg_n, k)
     inp = synth.w8a8(70, k, seg_n, seed=400 + k + sum(seg_n))
+    if kind == 1 and any(n % 128 for n in seg_n[:-1]):
+        # block scales cover 128 weight rows: a non-last segment that is not a
+        # multiple of 128 rows is refused on the host, before any launch
+        _expect_invalid(lambda: _case(kind, inp.x_bf16, k, inp.weights, 9), "not a multiple of 128")
+        return
     for rows in (1, 9, 70):
         _case(kind, inp.x_bf16, k, inp.weights, rows, what=f"kind={kind} segs={seg_n} rows={rows}")
 
@@ -171,8 +180,6 @@ def test_shared_workspace_across_calls():
                                           (5, 4096, (128, 256)), (8, 4096, (1024, 256, 100)),
                                           (2, 4736, (256, 31)), (8, 14336, (256,)), (6, 8192, (128, 128))])
 def test_proj_single_launch(kind, silu, with_up, rows, k, seg_n):
-    if kind == 1 and any(n % 128 for n in seg_n[:-1]):
-        pytest.skip("BLK128 needs 128-aligned non-last segments")
     print_case("w8a8 proj fused", kind, silu, with_up, rows, k, seg_n)
     inp = synth.w8a8(rows, k + 8, seg_n, seed=700 + rows + k, with_up=with_up)
     xb = inp.x_bf16.copy()
@@ -182,6 +189,10 @@ def test_proj_single_launch(kind, silu, with_up, rows, k, seg_n):
     weight = api.W8a8Weight(kind, [(dev(q), dev(s)) for q, s in segs])
     x = dev(xb)                                     # ldx = k + 8
     up = None if inp.up_bf16 is None else dev(inp.up_bf16)
+    if kind == 1 and any(n % 128 for n in seg_n[:-1]):
+        # refused on the host (block scales cover 128 weight rows), nothing launched
+        _expect_invalid(lambda: api.proj(x, weight, silu=silu, up=up), "not a multiple of 128")
+        return
     sshape = (rows,) if kind == 0 else (rows, k // 128)
     q, raw_q = poisoned((rows, k), torch.uint8)
     sa, raw_s = poisoned(sshape, torch.float32)
