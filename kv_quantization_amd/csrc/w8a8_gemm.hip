@@ -522,8 +522,9 @@ void fused_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t
 // (deterministic), applies per-row scales and writes bf16.
 
 constexpr int kWideN = 128;
-constexpr int kWideWaves = 8;
-constexpr int kWideThreads = kWideWaves * kWave;
+constexpr int kWideWaves = 8;                              // waves that multiply
+constexpr int kWideLoaders = 4;                            // waves that only load (2 per stream)
+constexpr int kWideThreads = (kWideWaves + kWideLoaders) * kWave;
 
 // LDS byte offset of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
@@ -574,39 +575,74 @@ __device__ __forceinline__ void wait_vm() {
 
 template <int MTW, int KIND>
 struct WideCfg {
-    static constexpr int WM = 4;                         // waves along rows
+    static constexpr int WM = 4;                         // multiplying waves along rows
     static constexpr int BM = 16 * MTW * WM;             // rows per workgroup
     static constexpr int A_BYTES = BM * 128;
     static constexpr int B_BYTES = kWideN * 128;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_INSTR = A_BYTES / 1024 / kWideWaves;   // 1 KiB loads per wave
-    static constexpr int B_INSTR = B_BYTES / 1024 / kWideWaves;
-    static constexpr int SA_ROWS = BM / kWideWaves;               // activation-scale rows per wave
-    static constexpr int SC_INSTR = (SA_ROWS * 4 + 63) / 64;        // dword loads per wave per chunk
-    static constexpr int SC_BYTES = (BM + 1) * 16;                  // one chunk: [BM rows + sw][4 K blocks]
-    static constexpr int N_INSTR = A_INSTR + B_INSTR;
-    // LDS ring depth: double buffering (one K step in flight while one is
-    // multiplied) measured fastest; 3..5 stages were slower (more loads in
-    // flight per CU, no better latency hiding).  At most 5 in any case: the
-    // double-buffered scale chunks are refilled 8 K blocks apart.
-    static constexpr int ST = 2;
+    // Producer / consumer: waves 0-7 only read LDS and multiply; waves 8-9
+    // load the activation tiles (and block scales), waves 10-11 the weight
+    // tiles.  A wave that issues a load waits while the address unit's queue
+    // is full, and in-order issue then holds back its matrix instructions
+    // too; loader waves take that wait instead.  Each loader's vector-memory
+    // counter tracks one stream, so the weight ring can run further ahead
+    // than the activation ring (a wave can only wait for its loads in issue
+    // order).
+    static constexpr int LW = kWideLoaders / 2;                   // loader waves per stream
+    static constexpr int A_INSTR = A_BYTES / 1024 / LW;           // 1 KiB loads per A loader per stage
+    static constexpr int B_INSTR = B_BYTES / 1024 / LW;           // per B loader per stage
+    static constexpr int SA_ROWS = BM / LW;                       // activation-scale rows per A loader
+    static constexpr int SC_INSTR = (SA_ROWS * 4 + 63) / 64;      // dword loads per A loader per chunk
+    static constexpr int SC_BYTES = (BM + 1) * 16;                // one chunk: [BM rows + sw][4 K blocks]
+    // Ring depths: the activation tiles come from L2 (every column tile
+    // reads them), the weight tiles from HBM with its longer latency; the
+    // weight ring takes what LDS is left.  The double-buffered scale chunks
+    // are refilled 8 K blocks apart, so SA <= 5.
+    static constexpr int SA = 3;
+    static constexpr int LDS_MAX = 160 * 1024 - 2 * ((4 * 16 * WM + 1) * 16) - 1024;
+    static constexpr int SB_FIT = (LDS_MAX - SA * A_BYTES) / B_BYTES;
+    static constexpr int SB = SB_FIT > 8 ? 8 : SB_FIT;
     static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SA_ROWS % 8 == 0, "tile shape");
+    static_assert(SB >= 3 && SA <= 5, "ring depths");
+    static_assert((SB - 2) * B_INSTR + 15 < 64 && (SA - 2) * (A_INSTR + SC_INSTR + 1) + 15 < 64, "vmcnt range");
+    static_assert(SC_INSTR + 1 <= 15, "scale loads per chunk");
 };
 
-// s_waitcnt vmcnt(base + extra) for a run-time extra in [0, 3]
+// s_waitcnt vmcnt(base + extra) for a run-time extra in [0, 15] (larger
+// extras wait for more loads than needed: slower, never wrong)
 template <int BASE>
 __device__ __forceinline__ void wait_vm_plus(uint32_t extra) {
     switch (extra) {
         case 0: wait_vm<BASE>(); break;
         case 1: wait_vm<BASE + 1>(); break;
         case 2: wait_vm<BASE + 2>(); break;
-        default: wait_vm<BASE + 3>(); break;
+        case 3: wait_vm<BASE + 3>(); break;
+        case 4: wait_vm<BASE + 4>(); break;
+        case 5: wait_vm<BASE + 5>(); break;
+        case 6: wait_vm<BASE + 6>(); break;
+        case 7: wait_vm<BASE + 7>(); break;
+        case 8: wait_vm<BASE + 8>(); break;
+        case 9: wait_vm<BASE + 9>(); break;
+        case 10: wait_vm<BASE + 10>(); break;
+        case 11: wait_vm<BASE + 11>(); break;
+        case 12: wait_vm<BASE + 12>(); break;
+        case 13: wait_vm<BASE + 13>(); break;
+        case 14: wait_vm<BASE + 14>(); break;
+        default: wait_vm<BASE + 15>(); break;
     }
 }
 
-// wait until at most `later` stages of N loads (plus `extra`, <= 3) are in flight
+// wait until at most `later` stages of N loads (plus `extra`) are in flight
 template <int N, int MAXL>
 __device__ __forceinline__ void wait_stages(int later, uint32_t extra) {
+    if constexpr (MAXL >= 6) {
+        if (later == 6) { wait_vm_plus<6 * N>(extra); return; }
+    }
+    if constexpr (MAXL >= 5) {
+        if (later == 5) { wait_vm_plus<5 * N>(extra); return; }
+    }
+    if constexpr (MAXL >= 4) {
+        if (later == 4) { wait_vm_plus<4 * N>(extra); return; }
+    }
     if constexpr (MAXL >= 3) {
         if (later == 3) { wait_vm_plus<3 * N>(extra); return; }
     }
@@ -614,7 +650,7 @@ __device__ __forceinline__ void wait_stages(int later, uint32_t extra) {
         if (later == 2) { wait_vm_plus<2 * N>(extra); return; }
     }
     if (later == 1) { wait_vm_plus<N>(extra); return; }
-    wait_vm<0>();
+    wait_vm_plus<0>(extra);
 }
 
 
@@ -624,13 +660,19 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
                                                           uint16_t *__restrict__ out, uint32_t ldc, uint32_t splits,
                                                           uint32_t ntiles, float *__restrict__ partials) {
     using C = WideCfg<MTW, KIND>;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::ST * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a[C::SA * C::A_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b[C::SB * C::B_BYTES];
     // block scales (KIND 1), double-buffered in chunks of 4 K blocks
     __shared__ __attribute__((aligned(16))) float lds_sc[KIND == 1 ? 2 : 1][KIND == 1 ? C::SC_BYTES / 4 : 4];
     const int lane = lane_id();
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wv >> 1, wn = wv & 1;
     const int r16 = lane & 15, g = lane >> 4;
+    // wave-uniform roles: multiply (0-7), load activations (8-9), load weights (10-11)
+    const bool mul_wave = wv < (uint32_t)kWideWaves;
+    const bool a_wave = !mul_wave && wv < (uint32_t)(kWideWaves + C::LW);
+    const bool b_wave = !mul_wave && !a_wave;
+    const uint32_t lw = a_wave ? wv - kWideWaves : (b_wave ? wv - kWideWaves - C::LW : 0);
     // consecutive workgroups take the K slices of one column tile: with the
     // usual round-robin dispatch over the 8 XCDs each XCD then works on few
     // K slices, so fewer copies of the activation tile sit in its L2
@@ -641,145 +683,195 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
     const uint32_t kb1 = (uint32_t)((uint64_t)(split + 1) * nkb / splits);
     const int nks = (int)(kb1 - kb0);
 
-    // -- sources of the direct loads.  Load j of wave w fills 1 KiB of the
-    // tile: rows 8*(w*INSTR + j) .. +8; lane i writes LDS chunk slot i%8 of
-    // row (that + i/8), which holds logical chunk (i%8) ^ (row & 7).
-    const u32x4 ra = buffer_rsrc(q, rows * K);
-    uint32_t aoff[C::A_INSTR];
-#pragma unroll
-    for (int j = 0; j < C::A_INSTR; ++j) {
-        const uint32_t row = 8 * (wv * C::A_INSTR + j) + (lane >> 3);
-        aoff[j] = row * K + (((lane & 7) ^ (row & 7)) << 4);   // rows >= `rows` read zeros
-    }
     const int sg0 = seg_of(S, n0);
-    const uint8_t *wseg = sg0 == 0 ? S.w[0] : (sg0 == 1 ? S.w[1] : S.w[2]);
     const uint32_t seg_start = sg0 == 0 ? S.start[0] : (sg0 == 1 ? S.start[1] : S.start[2]);
-    const uint32_t seg_n = sg0 == 0 ? S.n[0] : (sg0 == 1 ? S.n[1] : S.n[2]);
-    const u32x4 rb = buffer_rsrc(wseg, seg_n * K);
-    uint32_t boff[C::B_INSTR];
-    const uint8_t *bsrc[C::B_INSTR];
-#pragma unroll
-    for (int j = 0; j < C::B_INSTR; ++j) {
-        const uint32_t row = 8 * (wv * C::B_INSTR + j) + (lane >> 3);
-        const uint32_t chunk = ((lane & 7) ^ (row & 7)) << 4;
-        boff[j] = (n0 - seg_start + row) * K + chunk;          // past the segment: zeros
-        if (!UNI) {
-            uint32_t jg = n0 + row;
-            int sg = seg_of(S, jg < S.ntotal ? jg : 0);
-            uint32_t jl = (jg < S.ntotal ? jg : 0) - S.start[sg];
-            if (jl >= S.n[sg]) { sg = 0; jl = 0; }           // past the end: any valid row
-            bsrc[j] = S.w[sg] + (size_t)jl * K + chunk;
-        }
-    }
-    // Block scales travel in chunks of 4 K blocks (kb = 4c .. 4c+3), loaded
-    // with the first stage that needs them: lane i of load j of wave w takes
-    // sa[row][4c + i%4] for row w*SA_ROWS + 16j + i/4 (rows past the end and
-    // K blocks past the array read zero), so a chunk holds [row][4] floats;
-    // wave 0 also loads sw[band][4c .. 4c+3] of this 128-column band behind
-    // the rows.  Scales are re-read from HBM once per 4 K blocks, not per
-    // stage: a per-row 4-byte read touches a whole cache line.
-    const u32x4 rsa = buffer_rsrc(sa, KIND == 1 ? rows * nkb * 4 : 4);
-    u32x4 rsw = rsa;
-    if (KIND == 1) {
-        const float *sseg = sg0 == 0 ? S.s[0] : (sg0 == 1 ? S.s[1] : S.s[2]);
-        rsw = buffer_rsrc(sseg + (size_t)((n0 - seg_start) / 128) * nkb, nkb * 4);
-    }
-    uint32_t scoff[C::SC_INSTR];
-#pragma unroll
-    for (int j = 0; j < C::SC_INSTR; ++j)
-        scoff[j] = ((wv * C::SA_ROWS + 16 * j + (lane >> 2)) * nkb + (lane & 3)) * 4;
 
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
-    const uint32_t sc0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sc[0][0]));
-    // number of scale loads this wave adds to stage it
-    auto sc_count = [&](int it) -> uint32_t {
-        if (KIND != 1 || it >= nks || (it != 0 && ((kb0 + it) & 3) != 0)) return 0;
-        return C::SC_INSTR + (wv == 0 ? 1 : 0);
-    };
-    auto issue = [&](int it) {
-        const uint32_t st = (uint32_t)(it % C::ST);
-        const uint32_t kb = kb0 + it;
-        const uint32_t abase = lds0 + st * C::STAGE;
-        const uint32_t bbase = abase + C::A_BYTES;
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(kb * 128);
+    if (!mul_wave) {
+        // ------------------------------------------------------ loaders --
+        // Load j of loader wave w fills 1 KiB of its tile: rows
+        // 8*(w*INSTR + j) .. +8; lane i writes LDS chunk slot i%8 of row
+        // (that + i/8), which holds logical chunk (i%8) ^ (row & 7).
+        const uint32_t a0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_a));
+        const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_b));
+        const uint32_t sc0 = __builtin_amdgcn_readfirstlane(lds_offset(&lds_sc[0][0]));
+        // number of scale loads an A loader adds to activation stage it
+        auto sc_count = [&](int it) -> uint32_t {
+            if (KIND != 1 || it >= nks || (it != 0 && ((kb0 + it) & 3) != 0)) return 0;
+            return C::SC_INSTR + (lw == 0 ? 1 : 0);
+        };
+        if (a_wave) {
+            const u32x4 ra = buffer_rsrc(q, rows * K);
+            uint32_t aoff[C::A_INSTR];
 #pragma unroll
-        for (int j = 0; j < C::A_INSTR; ++j) lds_buf16(ra, aoff[j], soff, abase + (wv * C::A_INSTR + j) * 1024);
-#pragma unroll
-        for (int j = 0; j < C::B_INSTR; ++j) {
-            if (UNI) lds_buf16(rb, boff[j], soff, bbase + (wv * C::B_INSTR + j) * 1024);
-            else lds_glb16(bsrc[j] + (size_t)kb * 128, bbase + (wv * C::B_INSTR + j) * 1024);
-        }
-        if (sc_count(it)) {
-            // the chunk offset goes into the per-lane offset, which the
-            // buffer range check covers
-            const uint32_t c4 = (kb & ~3u) * 4;
-            const uint32_t slot = sc0 + ((kb >> 2) & 1) * C::SC_BYTES;
-#pragma unroll
-            for (int j = 0; j < C::SC_INSTR; ++j) {
-                const uint32_t dst = slot + (wv * C::SA_ROWS + 16 * j) * 16;
-                if (16 * j + (lane >> 2) < C::SA_ROWS) lds_buf4(rsa, scoff[j] + c4, 0, dst);
+            for (int j = 0; j < C::A_INSTR; ++j) {
+                const uint32_t row = 8 * (lw * C::A_INSTR + j) + (lane >> 3);
+                aoff[j] = row * K + (((lane & 7) ^ (row & 7)) << 4);   // rows >= `rows` read zeros
             }
-            if (wv == 0 && lane < 4) lds_buf4(rsw, lane * 4 + c4, 0, slot + C::BM * 16);
+            // Block scales travel in chunks of 4 K blocks (kb = 4c .. 4c+3),
+            // loaded with the first activation stage that needs them: lane i
+            // of load j of A loader w takes sa[row][4c + i%4] for row
+            // w*SA_ROWS + 16j + i/4 (rows past the end and K blocks past the
+            // array read zero), so a chunk holds [row][4] floats; A loader 0
+            // also loads sw[band][4c .. 4c+3] of this 128-column band behind
+            // the rows.  Scales are re-read from HBM once per 4 K blocks, not
+            // per stage: a per-row 4-byte read touches a whole cache line.
+            const u32x4 rsa = buffer_rsrc(sa, KIND == 1 ? rows * nkb * 4 : 4);
+            u32x4 rsw = rsa;
+            if (KIND == 1) {
+                const float *sseg = sg0 == 0 ? S.s[0] : (sg0 == 1 ? S.s[1] : S.s[2]);
+                rsw = buffer_rsrc(sseg + (size_t)((n0 - seg_start) / 128) * nkb, nkb * 4);
+            }
+            uint32_t scoff[C::SC_INSTR];
+#pragma unroll
+            for (int j = 0; j < C::SC_INSTR; ++j)
+                scoff[j] = ((lw * C::SA_ROWS + 16 * j + (lane >> 2)) * nkb + (lane & 3)) * 4;
+            auto issue_a = [&](int it) {
+                const uint32_t kb = kb0 + it;
+                const uint32_t abase = a0 + (uint32_t)(it % C::SA) * C::A_BYTES;
+                const uint32_t soff = __builtin_amdgcn_readfirstlane(kb * 128);
+#pragma unroll
+                for (int j = 0; j < C::A_INSTR; ++j)
+                    lds_buf16(ra, aoff[j], soff, abase + (lw * C::A_INSTR + j) * 1024);
+                if (sc_count(it)) {
+                    // the chunk offset goes into the per-lane offset, which the
+                    // buffer range check covers
+                    const uint32_t c4 = (kb & ~3u) * 4;
+                    const uint32_t slot = sc0 + ((kb >> 2) & 1) * C::SC_BYTES;
+#pragma unroll
+                    for (int j = 0; j < C::SC_INSTR; ++j) {
+                        const uint32_t dst = slot + (lw * C::SA_ROWS + 16 * j) * 16;
+                        if (16 * j + (lane >> 2) < C::SA_ROWS) lds_buf4(rsa, scoff[j] + c4, 0, dst);
+                    }
+                    if (lw == 0 && lane < 4) lds_buf4(rsw, lane * 4 + c4, 0, slot + C::BM * 16);
+                }
+            };
+            // this wave's loads of K step `next` complete; later steps may stay in flight
+            auto wait_a = [&](int next) {
+                if (next >= nks) return;
+                int later = nks - 1 - next;
+                if (later > C::SA - 2) later = C::SA - 2;
+                uint32_t extra = 0;
+                for (int j = 1; j <= later; ++j) extra += sc_count(next + j);
+                wait_stages<C::A_INSTR, C::SA - 2>(later, extra);
+            };
+            for (int i = 0; i < C::SA - 1 && i < nks; ++i) issue_a(i);
+            wait_a(0);
+            asm volatile("s_barrier" ::: "memory");
+            for (int it = 0; it < nks; ++it) {
+                if (it + C::SA - 1 < nks) issue_a(it + C::SA - 1);
+                wait_a(it + 1);
+                asm volatile("s_barrier" ::: "memory");
+            }
+        } else {
+            const uint8_t *wseg = sg0 == 0 ? S.w[0] : (sg0 == 1 ? S.w[1] : S.w[2]);
+            const uint32_t seg_n = sg0 == 0 ? S.n[0] : (sg0 == 1 ? S.n[1] : S.n[2]);
+            const u32x4 rb = buffer_rsrc(wseg, seg_n * K);
+            uint32_t boff[C::B_INSTR];
+            const uint8_t *bsrc[C::B_INSTR];
+#pragma unroll
+            for (int j = 0; j < C::B_INSTR; ++j) {
+                const uint32_t row = 8 * (lw * C::B_INSTR + j) + (lane >> 3);
+                const uint32_t chunk = ((lane & 7) ^ (row & 7)) << 4;
+                boff[j] = (n0 - seg_start + row) * K + chunk;          // past the segment: zeros
+                if (!UNI) {
+                    uint32_t jg = n0 + row;
+                    int sg = seg_of(S, jg < S.ntotal ? jg : 0);
+                    uint32_t jl = (jg < S.ntotal ? jg : 0) - S.start[sg];
+                    if (jl >= S.n[sg]) { sg = 0; jl = 0; }           // past the end: any valid row
+                    bsrc[j] = S.w[sg] + (size_t)jl * K + chunk;
+                }
+            }
+            auto issue_b = [&](int it) {
+                const uint32_t kb = kb0 + it;
+                const uint32_t bbase = b0 + (uint32_t)(it % C::SB) * C::B_BYTES;
+                const uint32_t soff = __builtin_amdgcn_readfirstlane(kb * 128);
+#pragma unroll
+                for (int j = 0; j < C::B_INSTR; ++j) {
+                    if (UNI) lds_buf16(rb, boff[j], soff, bbase + (lw * C::B_INSTR + j) * 1024);
+                    else lds_glb16(bsrc[j] + (size_t)kb * 128, bbase + (lw * C::B_INSTR + j) * 1024);
+                }
+            };
+            auto wait_b = [&](int next) {
+                if (next >= nks) return;
+                int later = nks - 1 - next;
+                if (later > C::SB - 2) later = C::SB - 2;
+                wait_stages<C::B_INSTR, C::SB - 2>(later, 0);
+            };
+            for (int i = 0; i < C::SB - 1 && i < nks; ++i) issue_b(i);
+            wait_b(0);
+            asm volatile("s_barrier" ::: "memory");
+            for (int it = 0; it < nks; ++it) {
+                if (it + C::SB - 1 < nks) issue_b(it + C::SB - 1);
+                wait_b(it + 1);
+                asm volatile("s_barrier" ::: "memory");
+            }
         }
-    };
+        return;
+    }
 
+    // ------------------------------------------------------- multiply ---
+    // Step it reads the slots of step it: filled before the barrier that
+    // ended step it-1 (its loaders waited for them), and refilled only after
+    // the barrier that ends step it.  lgkmcnt(0) before each barrier makes
+    // this wave's LDS reads of the step complete first.  The asm barrier
+    // keeps LDS accesses on their side of it.
     f32x4 acc[MTW][4];
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int i = 0; i < C::ST - 1 && i < nks; ++i) issue(i);
+    asm volatile("s_barrier" ::: "memory");
     for (int it = 0; it < nks; ++it) {
-        // this wave's loads of stage it have landed (later stages may stay in
-        // flight); after the barrier so have everyone's, and everyone has
-        // finished multiplying stage it-1, whose buffer the next issue
-        // refills.  One barrier per K step; the asm form keeps LDS accesses
-        // on their side of it without waiting for the loads in flight.
-        int later = nks - 1 - it;
-        if (later > C::ST - 2) later = C::ST - 2;
-        uint32_t extra = 0;
-        for (int j = 1; j <= later; ++j) extra += sc_count(it + j);
-        wait_stages<C::N_INSTR, C::ST - 2>(later, extra);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (it + C::ST - 1 < nks) issue(it + C::ST - 1);
-        const int st = it % C::ST;
         const uint32_t kbi = kb0 + it;
         const float *scs = &lds_sc[KIND == 1 ? (kbi >> 2) & 1 : 0][kbi & 3];   // [row * 4] of this K block
-        const float swk = KIND == 1 ? scs[C::BM * 4] : 1.0f;
-        const uint8_t *abase = lds + st * C::STAGE;
-        const uint8_t *bbase = abase + C::A_BYTES;
+        const uint8_t *abase = lds_a + (it % C::SA) * C::A_BYTES;
+        const uint8_t *bbase = lds_b + (it % C::SB) * C::B_BYTES;
+        // operand fragments: the weight fragments of the step and the first
+        // activation fragment are read together; activation fragment mt+1
+        // is read before the matrix instructions of fragment mt, so its LDS
+        // latency runs under them instead of between the groups
+        auto frag = [&](const uint8_t *base, int row) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + row * 128 + ((g ^ (row & 7)) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + row * 128 + (((g + 4) ^ (row & 7)) << 4));
+            return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        auto scales = [&](int mt) {
+            // rows 4g..4g+3 of this M tile, times the weight block scale
+            const int r0 = wm * 16 * MTW + mt * 16 + 4 * g;
+            const float swk = scs[C::BM * 4];
+            return f32x4{scs[r0 * 4], scs[r0 * 4 + 4], scs[r0 * 4 + 8], scs[r0 * 4 + 12]} * swk;
+        };
         i32x8 b[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int row = wn * 64 + nt * 16 + r16;
-            const u32x4 lo = *reinterpret_cast<const u32x4 *>(bbase + row * 128 + ((g ^ (row & 7)) << 4));
-            const u32x4 hi = *reinterpret_cast<const u32x4 *>(bbase + row * 128 + (((g + 4) ^ (row & 7)) << 4));
-            b[nt] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
+        for (int nt = 0; nt < 4; ++nt) b[nt] = frag(bbase, wn * 64 + nt * 16 + r16);
+        i32x8 a_cur = frag(abase, wm * 16 * MTW + r16);
+        f32x4 sc_cur = KIND == 1 ? scales(0) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) {
-            const int row = wm * 16 * MTW + mt * 16 + r16;
-            const u32x4 lo = *reinterpret_cast<const u32x4 *>(abase + row * 128 + ((g ^ (row & 7)) << 4));
-            const u32x4 hi = *reinterpret_cast<const u32x4 *>(abase + row * 128 + (((g + 4) ^ (row & 7)) << 4));
-            const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            i32x8 a_next = a_cur;
+            f32x4 sc_next = sc_cur;
+            if (mt + 1 < MTW) {
+                a_next = frag(abase, wm * 16 * MTW + (mt + 1) * 16 + r16);
+                if (KIND == 1) sc_next = scales(mt + 1);
+            }
             if (KIND == 0) {
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_fp8(a, b[nt], acc[mt][nt]);
+                for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_fp8(a_cur, b[nt], acc[mt][nt]);
             } else {
-                // rows 4g..4g+3 of this M tile
-                const int r0 = wm * 16 * MTW + mt * 16 + 4 * g;
-                const f32x4 sc = f32x4{scs[r0 * 4], scs[r0 * 4 + 4], scs[r0 * 4 + 8], scs[r0 * 4 + 12]} * swk;
                 f32x4 p[4];
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) p[nt] = mfma_fp8(a, b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+                for (int nt = 0; nt < 4; ++nt) p[nt] = mfma_fp8(a_cur, b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[mt][nt][e] = __builtin_fmaf(p[nt][e], sc[e], acc[mt][nt][e]);
+                    for (int e = 0; e < 4; ++e) acc[mt][nt][e] = __builtin_fmaf(p[nt][e], sc_cur[e], acc[mt][nt][e]);
             }
+            a_cur = a_next;
+            sc_cur = sc_next;
         }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+
 
     // ---- epilogue: bf16 output (no split) or fp32 partial tile [split][rows][N]
     float *part = partials + (size_t)split * rows * S.ntotal;
