@@ -42,19 +42,26 @@ def test_roofline_picks_the_binding_roof():
     assert r["frac"] == round(1000.0 / bench.FP8_PEAK_TFLOPS, 4)
 
 
-def test_stored_traffic_only_for_the_measured_source(tmp_path):
-    for kernel, entry in bench.TRAFFIC.items():
-        assert bench.measured_traffic(kernel) == entry["bytes"]
-        # comments do not change the digest, code does
-        for src, digest in entry["sources"].items():
-            text = (ROOT / src).read_text()
-            assert bench.code_digest(ROOT / src) == digest
-            probe = tmp_path / "probe.hip"
-            probe.write_text(text + "\n// a comment\n")
-            assert bench.code_digest(probe) == digest
-            probe.write_text(text + "\nint extra;\n")
-            assert bench.code_digest(probe) != digest
-    assert bench.measured_traffic("kv_int8_quant") is None
+def test_stored_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
+    # the figure is reported only while every listed source hashes (comments
+    # aside) to the digest it was measured on
+    src = tmp_path / "k.hip"
+    src.write_text("__global__ void k() { int a = 1; }\n")
+    digest = bench.code_digest(src)
+    monkeypatch.setattr(bench, "TRAFFIC", {"kern": {"bytes": 1234, "sources": {str(src): digest}}})
+    assert bench.measured_traffic("kern") == 1234
+    assert bench.measured_traffic("other") is None
+    src.write_text("__global__ void k() { int a = 1; }  // a comment\n/* and another */\n")
+    assert bench.code_digest(src) == digest and bench.measured_traffic("kern") == 1234
+    src.write_text("__global__ void k() { int a = 2; }\n")
+    assert bench.measured_traffic("kern") is None
+
+
+def test_stored_traffic_digests_name_existing_sources():
+    for entry in bench.TRAFFIC.values():
+        assert entry["bytes"] > 0
+        for src in entry["sources"]:
+            assert (ROOT / src).exists(), src
 
 
 def test_cold_plan_spans_the_rotation():
