@@ -263,17 +263,25 @@ typedef struct {
 
 /* Q, K and V in one launch (the page dispatches three kernels).  k_proj and
  * v_proj are both NULL (a single projection) or both set with equal n.
- * x: fp32 [m][k], m >= 1, k % group_size == 0.
- * group_size is 32, 64, 128 or 256.  Activations are rounded to fp16 (round
- * to nearest even) for the matrix cores; codes are exact; accumulation is
- * fp32; |x| must stay below 65504.
+ * x: fp32 [m][k], m >= 1, k % group_size == 0.  group_size is 32, 64, 128
+ * or 256.
+ * m < 16: every product and sum is fp32, as on the page (a weight-streaming
+ * GEMV on the vector ALUs: codes unpacked to exact floats, x unrounded, s
+ * and z applied once per group as s * (sum x q - z * sum x)); 9..15 rows run
+ * as two launches of at most 8.
+ * m >= 16: the matrix cores take x rounded to fp16 (round to nearest even)
+ * and the exact codes, accumulating in fp32; |x| must stay below 65504 (a
+ * larger value becomes inf; the error from the rounding is at most 2^-11
+ * |x| per term).
  * workspace: NULL, or at least int4_awq_workspace_bytes(), zero-filled before
  * its first use; the call leaves its counter area at zero and writes partial
  * tiles behind it, and for m > 16 the fp16-rounded activations behind those
  * (one extra launch converts them; every column tile then reads half the
- * bytes).  Without it, one workgroup per tile (less parallelism) and the
- * rounding happens inside the product kernel: the same fp16 operands.
- * Concurrent calls must not share a workspace. */
+ * bytes).  Without it, one workgroup per tile (less parallelism) and, for
+ * m > 16, the rounding happens inside the product kernel: the same fp16
+ * operands.  The workspace arguments extend the page's call (which has
+ * none): split-K partial sums need device scratch the library does not
+ * allocate.  Concurrent calls must not share a workspace. */
 int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k,
                       uint32_t group_size, const int4_awq_proj_t *q_proj,
                       const int4_awq_proj_t *k_proj,
@@ -284,10 +292,12 @@ int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_size,
                              uint32_t n_total, size_t *bytes);
 
 /* The same call with 16-bit activations (kvq_dtype_t: KVQ_DT_F32, KVQ_DT_F16
- * or KVQ_DT_BF16; x holds m*k values of that type).  fp16 values go to the
- * matrix cores unchanged; bf16 values are widened exactly and rounded to
- * fp16 like fp32 input (exact for |x| in [2^-14, 65504]).  Outputs stay fp32.
- * KVQ_DT_F32 is exactly int4_awq_qkv_gemm. */
+ * or KVQ_DT_BF16; x holds m*k values of that type).  m < 16: the values are
+ * widened exactly to fp32 (the same results as the fp32 call on the widened
+ * values).  m >= 16: fp16 values go to the matrix cores unchanged; bf16
+ * values are widened exactly and rounded to fp16 like fp32 input (exact for
+ * |x| in [2^-14, 65504]).  Outputs stay fp32.  KVQ_DT_F32 is exactly
+ * int4_awq_qkv_gemm. */
 int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k,
                          uint32_t group_size, const int4_awq_proj_t *q_proj,
                          const int4_awq_proj_t *k_proj,

@@ -368,6 +368,324 @@ __global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ 
     if (threadIdx.x == 0) __hip_atomic_store(&counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ----------------------------------------------------- fp32 GEMV ---
+//
+// Below 16 rows the products run on the vector ALUs in fp32, as the page's
+// kernel does (x is never rounded): a weight-streaming GEMV.  A workgroup
+// owns a tile of 256 output columns of one projection; each of its GW waves
+// takes whole blocks of rows of it.  Lane (cl, kl) of a wave covers
+// CPL consecutive columns (CPL/8 words of every weight row: one 16-, 8- or
+// 4-byte load per row, so the CL = 256/CPL column lanes of a row read 128
+// contiguous bytes) and RPL = gs/KL consecutive rows of the group, KL =
+// 64/CL lanes splitting the group's rows.  Codes are unpacked in registers:
+// (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) hold the 8 nibbles of a word
+// as bytes, which v_cvt_f32_ubyte0..3 turn into exact floats; byte b of the
+// low part is the nibble at bit 8b (column 0, 4, 1, 5 of the word in AWQ
+// order), of the high part the nibble at bit 8b+4 (columns 2, 6, 3, 7).
+//
+// Per group g the lane forms P[m][c] = sum_k x[m][k] q[k][c] and X[m] =
+// sum_k x[m][k] over its rows (fp32 FMAs, x staged once per group in LDS);
+// the KL partial sums of a column are combined by a reduce-scatter over the
+// lanes (v_permlane32_swap, v_permlane16_swap, then DPP row_ror:8), which
+// leaves every lane 4 columns, and the lane adds s (P - z X) for them.  That
+// is the page's sum of x (q - z) s regrouped per group (the scale and zero are
+// constant over a group); every product and sum stays fp32.
+//
+// The waves of a workgroup are added in LDS in wave order; when a tile's
+// groups are split over several workgroups ("slices"), their fp32 partial
+// tiles are exchanged through the workspace with device-scope stores and
+// loads and an agent-scope counter, and the last workgroup adds them in
+// slice order (deterministic) and resets the counter.
+constexpr uint32_t kGemvTile = 256;   // output columns per workgroup
+
+// s_waitcnt vmcnt(N) with N a template constant (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void gemv_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// v_permlane32_swap / v_permlane16_swap based halving of a set of 2H values:
+// lanes with the given bit clear keep the sums of the first H values over
+// the lane pair, lanes with it set the sums of the second H.
+template <int H, int BIT>
+__device__ __forceinline__ void halve(float *v) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        if (BIT == 5) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + H]), false,
+                                                            false);
+            v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        } else if (BIT == 4) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + H]), false,
+                                                            false);
+            v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        } else {
+            // lanes 8 apart inside a row of 16: row_ror:8 brings the partner's value
+            const bool hi = (lane_id() & 8) != 0;
+            const float keep = hi ? v[i + H] : v[i];
+            const float send = hi ? v[i] : v[i + H];
+            v[i] = keep + dpp_move<0x128>(send);
+        }
+    }
+}
+
+// Sum over the KL lanes that share a column set (lane bits 3..5 above the
+// column-lane bits): all-reduce, every lane gets the same bits.
+template <int KL>
+__device__ __forceinline__ float klane_sum(float v) {
+    if (KL >= 8) v += dpp_move<0x128>(v);
+    if (KL >= 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if (KL >= 2) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return v;
+}
+
+// CPL: columns per lane (32, 16 or 8).  MR: activation rows the accumulators
+// are built for (M <= MR), taken MRP at a time over the codes held in
+// registers.  RB: rows per block, min(group size, 128): a wave takes whole
+// blocks, and a group of 256 rows is two blocks with the same scale and
+// zero (s (P - z X) is linear in P and X, so the blocks add).  gs (run
+// time): group size.  xt (run time): activation format (0 fp32, 1 fp16,
+// 2 bf16; 16-bit values are widened exactly).
+template <int CPL, int MR, int MRP, int RB, int GW>
+__global__ __launch_bounds__(GW * kWave) void awq_gemv(const void *__restrict__ x, uint32_t M, uint32_t K,
+                                                              uint32_t gs, int xt, Projs P, uint32_t slices,
+                                                              uint32_t gpw,
+                                                              uint32_t *__restrict__ counters,
+                                                              float *__restrict__ partials) {
+    constexpr int CL = (int)kGemvTile / CPL;     // column lanes
+    constexpr int KL = kWave / CL;               // lanes splitting a group's rows
+    constexpr int RPL = RB / KL;                 // rows per lane per block
+    constexpr int WPL = CPL / 8;                 // words per lane per row
+    constexpr int NW = RPL * WPL;                // words per lane per group
+    static_assert(KL >= 2 && KL <= 8 && RPL >= 4 && RPL % 4 == 0, "lane layout");
+    static_assert(NW <= 64 && MR % MRP == 0, "codes of a group per lane; row passes");
+    __shared__ __attribute__((aligned(16))) float xs[GW][MR][RB];
+    __shared__ __attribute__((aligned(16))) f32x4 red[GW][MR][kGemvTile / 4];
+    __shared__ int s_last;
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cl = lane % CL, kl = lane / CL;
+
+    const uint32_t t = blockIdx.x / slices, slice = blockIdx.x % slices;
+    const int p = (P.count > 1 && t >= P.tstart[1]) ? ((P.count > 2 && t >= P.tstart[2]) ? 2 : 1) : 0;
+    const uint32_t np = pick(p, P.n[0], P.n[1], P.n[2]), wp = np / 8;
+    const uint32_t col0 = (t - pick(p, P.tstart[0], P.tstart[1], P.tstart[2])) * kGemvTile;
+    const uint32_t lcol = col0 + cl * CPL;             // first column of this lane
+    const bool cok = lcol < np;                        // n % CPL == 0: a lane is wholly in or out
+    const uint32_t nblocks = K / RB, ngroups = K / gs;
+
+    const uint32_t wbytes = K * wp * 4;
+    const rsrc_t rw = make_rsrc(pick(p, P.qw[0], P.qw[1], P.qw[2]), wbytes);
+    const uint32_t szbytes = ngroups * np * 4;
+    const rsrc_t rs = make_rsrc(pick(p, P.sc[0], P.sc[1], P.sc[2]), szbytes);
+    const rsrc_t rz = make_rsrc(pick(p, P.zr[0], P.zr[1], P.zr[2]), szbytes);
+    const uint32_t xb = xt == 0 ? 4 : 2;
+    const rsrc_t rx = make_rsrc(x, M * K * xb);
+
+    // after the reduce-scatter a lane keeps columns cb .. cb+3 of its CPL
+    const int cb = (CPL == 32 ? 16 * ((lane >> 5) & 1) + 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1)
+                              : (CPL == 16 ? 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1) : 4 * ((lane >> 5) & 1)));
+
+    float acc[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[m][c] = 0.0f;
+
+    const uint32_t bbeg = (slice * GW + wv) * gpw;
+    for (uint32_t bi = 0; bi < gpw; ++bi) {
+        const uint32_t b = bbeg + bi;
+        if (b >= nblocks) break;                            // wave-uniform
+        const uint32_t g = b * RB / gs;                     // the block's quantization group
+        // activation slab x[0..M)[b*RB .. +RB) -> this wave's LDS rows:
+        // issued first, so its wait below does not hold the code loads
+        constexpr int XV = RB / 4;                          // float4 per row
+        constexpr int XL = (MR * XV + kWave - 1) / kWave;   // loads per lane
+        u32x4 xv[XL];
+#pragma unroll
+        for (int j = 0; j < XL; ++j) {
+            const uint32_t e = j * kWave + lane;            // float4 index in [MR][XV]
+            const uint32_t m = e / XV, q4 = e % XV;
+            const bool ok = m < M;
+            if (xt == 0) {
+                xv[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (m * K + b * RB + q4 * 4) * 4 : kOffNone, 0, 0);
+            } else {
+                const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(rx, ok ? (m * K + b * RB + q4 * 4) * 2 : kOffNone,
+                                                                     0, 0);
+                xv[j] = u32x4{h[0], h[1], 0u, 0u};
+            }
+        }
+        // codes of the lane's rows, then this group's scales and zeros for
+        // the 4 columns the lane keeps
+        uint32_t w[NW];
+        const uint32_t row0 = b * RB + kl * RPL;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const uint32_t off = cok ? ((row0 + r) * wp + lcol / 8) * 4 : kOffNone;
+            if (WPL == 4) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+                w[4 * r] = v[0]; w[4 * r + 1] = v[1]; w[4 * r + 2] = v[2]; w[4 * r + 3] = v[3];
+            } else if (WPL == 2) {
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 0);
+                w[2 * r] = v[0]; w[2 * r + 1] = v[1];
+            } else {
+                w[r] = __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0);
+            }
+        }
+        const uint32_t soff = cok ? (g * np + lcol + cb) * 4 : kOffNone;
+        const f32x4 sv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff, 0, 0));
+        const f32x4 zv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, soff, 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+        gemv_wait_vm<(RPL + 2 < 63 ? RPL + 2 : 63)>();      // the activation loads have landed (in-order count)
+#pragma unroll
+        for (int j = 0; j < XL; ++j) {
+            const uint32_t e = j * kWave + lane;
+            if (e < (uint32_t)(MR * XV)) {
+                f32x4 f;
+                if (xt == 0) {
+                    f = __builtin_bit_cast(f32x4, xv[j]);
+                } else if (xt == 1) {
+                    const _Float16 *hh = reinterpret_cast<const _Float16 *>(&xv[j]);
+                    f = f32x4{(float)hh[0], (float)hh[1], (float)hh[2], (float)hh[3]};
+                } else {
+                    f = f32x4{__uint_as_float(xv[j][0] << 16), __uint_as_float(xv[j][0] & 0xFFFF0000u),
+                              __uint_as_float(xv[j][1] << 16), __uint_as_float(xv[j][1] & 0xFFFF0000u)};
+                }
+                reinterpret_cast<f32x4 *>(&xs[wv][0][0])[e] = f;
+            }
+        }
+        // the reads below are this wave's, after its own writes (LDS
+        // operations of a wave complete in order): stop code motion only
+        asm volatile("" ::: "memory");
+
+        // rows in passes of MRP over the codes in registers (unrolled: the
+        // accumulators are indexed by compile-time row numbers)
+#pragma unroll
+        for (int mp = 0; mp < MR; mp += MRP) {
+            if ((uint32_t)mp >= M) break;                   // wave-uniform
+            float pm[MRP][CPL];
+            float xsum[MRP];
+#pragma unroll
+            for (int i = 0; i < MRP; ++i) {
+                xsum[i] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) pm[i][c] = 0.0f;
+            }
+#pragma unroll
+            for (int r4 = 0; r4 < RPL; r4 += 4) {
+                f32x4 x4[MRP];
+#pragma unroll
+                for (int i = 0; i < MRP; ++i)
+                    x4[i] = *reinterpret_cast<const f32x4 *>(&xs[wv][mp + i][kl * RPL + r4]);   // zeros past M
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = r4 + rr;
+                    float q[CPL];
+#pragma unroll
+                    for (int u = 0; u < WPL; ++u) {
+                        const uint32_t wd = w[r * WPL + u];
+                        const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;
+                        // word column j sits at AWQ shift {0,16,4,20,8,24,12,28}[j]
+                        q[8 * u + 0] = (float)(lo & 0xFFu);
+                        q[8 * u + 4] = (float)((lo >> 8) & 0xFFu);
+                        q[8 * u + 1] = (float)((lo >> 16) & 0xFFu);
+                        q[8 * u + 5] = (float)(lo >> 24);
+                        q[8 * u + 2] = (float)(hi & 0xFFu);
+                        q[8 * u + 6] = (float)((hi >> 8) & 0xFFu);
+                        q[8 * u + 3] = (float)((hi >> 16) & 0xFFu);
+                        q[8 * u + 7] = (float)(hi >> 24);
+                    }
+#pragma unroll
+                    for (int i = 0; i < MRP; ++i) {
+                        const float xm = x4[i][rr];
+                        xsum[i] += xm;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) pm[i][c] = __builtin_fmaf(xm, q[c], pm[i][c]);
+                    }
+                }
+                // keep the unpacking of later rows (and passes) from being
+                // hoisted here: it would hold all the unpacked codes at once
+                if (MR > 4) __builtin_amdgcn_sched_barrier(0);
+            }
+            // combine the KL lanes of each column: reduce-scatter down to 4
+            // columns per lane, all-reduce of the activation sums
+#pragma unroll
+            for (int i = 0; i < MRP; ++i) {
+                if (CPL == 32) { halve<16, 5>(pm[i]); halve<8, 4>(pm[i]); halve<4, 3>(pm[i]); }
+                if (CPL == 16) { halve<8, 5>(pm[i]); halve<4, 4>(pm[i]); }
+                if (CPL == 8) { halve<4, 5>(pm[i]); }
+                const float xg = klane_sum<KL>(xsum[i]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[mp + i][c] = __builtin_fmaf(sv[c], __builtin_fmaf(-zv[c], xg, pm[i][c]), acc[mp + i][c]);
+            }
+        }
+        // the next block's activation slab overwrites this wave's LDS rows
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+
+    // waves -> LDS [wave][row][column/4], then 4 columns per thread summed in wave order
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+        red[wv][m][(cl * CPL + cb) / 4] = f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+    __syncthreads();
+    const uint32_t tile_id = t;
+    float *part = partials + ((size_t)tile_id * slices) * (MR * kGemvTile);
+    const rsrc_t rp = make_rsrc(part, slices * (MR * kGemvTile) * 4);
+    float *outp = pick(p, P.out[0], P.out[1], P.out[2]);
+    for (uint32_t e = threadIdx.x; e < M * (kGemvTile / 4); e += GW * kWave) {
+        const uint32_t m = e / (kGemvTile / 4), c4 = e % (kGemvTile / 4);
+        if (col0 + c4 * 4 >= np) continue;
+        f32x4 v = red[0][m][c4];
+#pragma unroll
+        for (int w2 = 1; w2 < GW; ++w2) v += red[w2][m][c4];
+        if (slices == 1) {
+            *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + col0 + c4 * 4) = v;
+        } else {
+            const uint32_t off = ((slice * MR + m) * kGemvTile + c4 * 4) * 4;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, off, 0, kAuxSc1);
+        }
+    }
+    if (slices == 1) return;
+
+    // cross-workgroup sum, as in awq_gemm: stores complete and visible at
+    // device scope before the counter moves; the last workgroup loads after
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&counters[tile_id], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == slices - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    for (uint32_t e = threadIdx.x; e < M * (kGemvTile / 4); e += GW * kWave) {
+        const uint32_t m = e / (kGemvTile / 4), c4 = e % (kGemvTile / 4);
+        if (col0 + c4 * 4 >= np) continue;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (uint32_t q0 = 0; q0 < slices; q0 += 8) {
+            u32x4 tv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t q = q0 + u;
+                const uint32_t off = q < slices ? ((q * MR + m) * kGemvTile + c4 * 4) * 4 : kOffNone;
+                tv[u] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSc1);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < slices) v += as_f32x4(tv[u]);
+        }
+        *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + col0 + c4 * 4) = v;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ host --
 
 struct Plan {
@@ -429,6 +747,50 @@ int check_proj(const char *fn, const int4_awq_proj_t *p, const char *which, uint
 
 uint32_t tiles_of(uint32_t n) { return (n / 8 + 15) / 16; }
 
+// ---- fp32 GEMV plan (m < kGemvMaxM)
+constexpr uint32_t kGemvMaxM = 16;        // the matrix-core path takes 16 rows and more
+constexpr uint32_t kGemvTargetWgs = 192;  // ~1 workgroup per CU: every load of a call in flight at once
+// rows per block (a wave's unit of work) and waves per workgroup: up to 2
+// activation rows, 64-row blocks in 8-wave workgroups (a workgroup still
+// covers 512 rows, so the exchange is unchanged, and each wave's unpacking
+// and FMAs are half those of a 128-row block); more rows, 128-row blocks
+// (64 with 8 rows, to keep the codes in registers) in 4-wave workgroups
+constexpr uint32_t kGemvRbSmall = 64, kGemvGwSmall = 8;
+constexpr uint32_t kGemvGwLarge = 4;
+
+struct GemvPlan {
+    uint32_t mr, rb, gw, slices, gpw;
+    size_t ws_bytes;   // counters + partial tiles, 0 when one workgroup covers a tile's K
+};
+
+// rows the accumulators are built for; 9..15 rows run as two launches of 8
+uint32_t gemv_mr(uint32_t m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
+
+GemvPlan gemv_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t tiles, bool have_ws) {
+    GemvPlan g;
+    g.mr = gemv_mr(m);
+    const uint32_t rbmax = g.mr <= 2 ? kGemvRbSmall : (g.mr >= 8 ? 64 : 128);
+    g.rb = gs < rbmax ? gs : rbmax;
+    g.gw = g.mr <= 2 ? kGemvGwSmall : kGemvGwLarge;
+    const uint32_t nblocks = k / g.rb;
+    // one block per wave while the grid stays at or under the target,
+    // otherwise more blocks per wave; slices of gw*gpw blocks
+    uint32_t gpw = 1;
+    while ((uint64_t)tiles * ((nblocks + g.gw * gpw - 1) / (g.gw * gpw)) > kGemvTargetWgs && g.gw * gpw < nblocks)
+        gpw *= 2;
+    g.gpw = gpw;
+    g.slices = (nblocks + g.gw * gpw - 1) / (g.gw * gpw);
+    if (tiles * 4 > KVQ_WORKSPACE_COUNTER_BYTES) g.slices = 1;   // more tiles than counters
+    if (!have_ws || g.slices == 1) {
+        g.slices = 1;
+        g.gpw = (nblocks + g.gw - 1) / g.gw;
+    }
+    g.ws_bytes = g.slices > 1 ? KVQ_WORKSPACE_COUNTER_BYTES + (size_t)tiles * g.slices * g.mr * kGemvTile * 4 : 0;
+    return g;
+}
+
+uint32_t gemv_tiles_of(uint32_t n) { return (n + kGemvTile - 1) / kGemvTile; }
+
 }  // namespace
 }  // namespace kvq
 
@@ -441,8 +803,13 @@ extern "C" int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_s
     if (m == 0 || group_size < 32 || group_size % 32 || k % group_size || n_total % 8) return KVQ_OK;
     // splitting n_total into up to three projections adds at most two tiles
     for (uint32_t extra = 0; extra <= 2; ++extra) {
-        const Plan pl = make_plan(m, k, group_size, tiles_of(n_total) + extra);
-        if (pl.ws_bytes > *bytes) *bytes = pl.ws_bytes;
+        if (m < kGemvMaxM) {
+            const GemvPlan g = gemv_plan(m, k, group_size, gemv_tiles_of(n_total) + extra, true);
+            if (g.ws_bytes > *bytes) *bytes = g.ws_bytes;
+        } else {
+            const Plan pl = make_plan(m, k, group_size, tiles_of(n_total) + extra);
+            if (pl.ws_bytes > *bytes) *bytes = pl.ws_bytes;
+        }
     }
     return KVQ_OK;
 }
@@ -450,9 +817,11 @@ extern "C" int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_s
 namespace kvq {
 namespace {
 
+// need: when set, validate, store the workspace bytes this call's full plan
+// uses, and launch nothing.
 int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint32_t group_size,
             const int4_awq_proj_t *q_proj, const int4_awq_proj_t *k_proj, const int4_awq_proj_t *v_proj,
-            void *workspace, size_t workspace_bytes, void *stream) {
+            void *workspace, size_t workspace_bytes, void *stream, size_t *need = nullptr) {
     if (xt != KVQ_DT_F32 && xt != KVQ_DT_F16 && xt != KVQ_DT_BF16)
         return fail(KVQ_E_INVALID, "%s: x dtype %d is not fp32 (0), fp16 (1) or bf16 (2)", fn, xt);
     if (!x || !q_proj) return fail(KVQ_E_INVALID, "%s: null x or q projection", fn);
@@ -487,8 +856,84 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
         if (i < P.count) tiles += tiles_of(pr->n);
     }
     P.ntiles = tiles;
+    hipStream_t s = as_stream(stream);
+
+    if (m < kGemvMaxM) {
+        // fp32 weight-streaming GEMV: 256-column tiles per projection
+        Projs G = P;
+        uint32_t gt = 0;
+        bool c32 = true, c16 = true;
+        for (uint32_t i = 0; i < 3; ++i) {
+            G.tstart[i] = gt;
+            if (i < P.count) {
+                gt += gemv_tiles_of(P.n[i]);
+                c32 = c32 && P.n[i] % 32 == 0;
+                c16 = c16 && P.n[i] % 16 == 0;
+            }
+        }
+        G.ntiles = gt;
+        if (need) {
+            *need = gemv_plan(m, k, group_size, gt, true).ws_bytes;
+            return KVQ_OK;
+        }
+        GemvPlan gp = gemv_plan(m, k, group_size, gt, false);
+        uint32_t *counters = nullptr;
+        float *partials = nullptr;
+        const GemvPlan gw = gemv_plan(m, k, group_size, gt, true);
+        if (gw.slices > 1 && workspace && aligned16(workspace) && workspace_bytes >= gw.ws_bytes) {
+            gp = gw;
+            counters = static_cast<uint32_t *>(workspace);
+            partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
+        }
+        const unsigned blocks = gt * gp.slices;
+        // columns per lane: 32 up to 2 rows, 16 up to 4, 8 above (and
+        // whenever a projection's n is not a multiple of the wider choice);
+        // 9..15 rows: rows 0-7, then the rest, with the output pointers moved
+#define KVQ_GEMV5(CPL, MR, MRP, RB, GW, XP, MM, PP)                                                            \
+    awq_gemv<CPL, MR, MRP, RB, GW><<<blocks, GW * kWave, 0, s>>>(XP, MM, k, group_size, xt, PP, gp.slices, gp.gpw, \
+                                                                counters, partials)
+#define KVQ_GEMV4(CPL, MR, MRP, RB, XP, MM, PP)                                           \
+    do {                                                                                  \
+        if (gp.gw == kGemvGwSmall) KVQ_GEMV5(CPL, MR, MRP, RB, kGemvGwSmall, XP, MM, PP); \
+        else KVQ_GEMV5(CPL, MR, MRP, RB, kGemvGwLarge, XP, MM, PP);                       \
+    } while (0)
+#define KVQ_GEMV(CPL, MR, MRP, XP, MM, PP)                                 \
+    do {                                                                   \
+        if (gp.rb == 32) KVQ_GEMV4(CPL, MR, MRP, 32, XP, MM, PP);          \
+        else if (gp.rb == 64) KVQ_GEMV4(CPL, MR, MRP, 64, XP, MM, PP);     \
+        else KVQ_GEMV4(CPL, MR, MRP, 128, XP, MM, PP);                     \
+    } while (0)
+        if (gp.mr == 1) {
+            if (c32) KVQ_GEMV(32, 1, 1, x, m, G);
+            else KVQ_GEMV(8, 1, 1, x, m, G);
+        } else if (gp.mr == 2) {
+            if (c32) KVQ_GEMV(32, 2, 2, x, m, G);
+            else KVQ_GEMV(8, 2, 2, x, m, G);
+        } else if (gp.mr == 4) {
+            if (c16) KVQ_GEMV(16, 4, 4, x, m, G);
+            else KVQ_GEMV(8, 4, 4, x, m, G);
+        } else {
+            KVQ_GEMV(8, 8, 4, x, (m < 8 ? m : 8u), G);
+            if (m > 8) {
+                int st = launch_status(fn);
+                if (st) return st;
+                Projs G2 = G;
+                for (uint32_t i = 0; i < 3; ++i) G2.out[i] = G.out[i] + (size_t)8 * G.n[i];
+                const void *x2 = static_cast<const uint8_t *>(x) + (size_t)8 * k * (xt == KVQ_DT_F32 ? 4 : 2);
+                KVQ_GEMV(8, 8, 4, x2, m - 8, G2);
+            }
+        }
+#undef KVQ_GEMV
+#undef KVQ_GEMV4
+#undef KVQ_GEMV5
+        return launch_status(fn);
+    }
 
     Plan pl = make_plan(m, k, group_size, P.ntiles);
+    if (need) {
+        *need = pl.ws_bytes;
+        return KVQ_OK;
+    }
     uint32_t *counters = nullptr;
     float *partials = nullptr;
     if (pl.ks_b > 1) {
@@ -502,7 +947,6 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
     const uint64_t tile_slots = pl.nchunks > 1 ? (uint64_t)kXcds * ((P.ntiles + kXcds - 1) / kXcds) : P.ntiles;
     const uint64_t blocks = tile_slots * pl.nchunks * pl.ks_b;
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
-    hipStream_t s = as_stream(stream);
     // fp32 activations with two 16-row tiles per wave: convert once to fp16
     // behind the partials when the workspace holds it, then read that copy
     if (xt == KVQ_DT_F32 && pl.x16_bytes && workspace && aligned16(workspace) && workspace_bytes >= pl.ws_bytes) {

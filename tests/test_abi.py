@@ -287,3 +287,4 @@ def test_attn_decode_varlen_validation(lib):
     # 64 sequences of at most 256 tokens x 8 heads: one workgroup each, nothing to merge
     assert lib.kvq_attn_decode_varlen_workspace_bytes(64, 32, 8, 256, 128, ctypes.byref(b)) == 0
     assert b.value == 0
+

@@ -204,3 +204,64 @@ def test_16bit_activations(dt, m):
     got32 = _run(xw, projs, 128)
     for a, b in zip(got16, got32):
         np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------ fp32 GEMV below 16 rows --
+# Below 16 rows the products are fp32 on the vector ALUs (the page's
+# arithmetic): no rounding of x, so the error against the fp64 definition is
+# fp32 summation error only, far under the 1e-3 contract.  FP32_RTOL pins
+# that: fp16 activations alone would exceed it (2^-11 per term).
+FP32_RTOL = 2e-5
+
+
+def _ratio(x, projs, gs, got):
+    refs = _oracle.int4_awq_qkv(x, [(p.qweight, p.scales, p.zeros) for p in projs], gs)
+    worst = 0.0
+    for (ref, bound), g in zip(refs, got):
+        worst = max(worst, float((np.abs(g.astype(np.float64) - ref) / np.maximum(bound, 1e-300)).max()))
+    return worst
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128, 256])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 13, 15])
+def test_gemv_fp32_rows_below_16(m, gs):
+    # n = 512 / 96 / 96: 32-column lanes (96 % 32 == 0), partial 256-column
+    # tiles; K = 2048 splits each tile's groups over several workgroups
+    print_case("int4 gemv fp32", m, gs)
+    x, projs = synth.int4_awq(m, 2048, (512, 96, 96), gs, seed=3000 + 16 * m + gs)
+    got = _run(x, projs, gs)
+    worst = _ratio(x, projs, gs, got)
+    print(f"gemv m={m} gs={gs}: max |err|/sum|x||w| = {worst:.3e}", flush=True)
+    assert worst <= FP32_RTOL
+    nows = _run(x, projs, gs, use_workspace=False)
+    assert _ratio(x, projs, gs, nows) <= FP32_RTOL
+
+
+@pytest.mark.parametrize("m", [1, 4, 8, 15])
+def test_gemv_fp32_qkv_workload(m):
+    print_case("int4 gemv fp32 qkv", m)
+    x5, projs = _qkv_inputs()
+    worst = _ratio(x5[:m], projs, 128, _run(x5[:m], projs, 128))
+    print(f"qkv M={m}: max |err|/sum|x||w| = {worst:.3e}", flush=True)
+    assert worst <= FP32_RTOL
+
+
+@pytest.mark.parametrize("sigma", [1e-6, 1e5])
+@pytest.mark.parametrize("m", [1, 4, 15])
+def test_gemv_fp32_activation_range(m, sigma):
+    """Activations far outside fp16's range (tiny: 1e-6, subnormal in fp16;
+    large: |x| ~ 1e5, past fp16's 65504) stay within the fp32 bound."""
+    print_case("int4 gemv range", m, sigma)
+    x, projs = synth.int4_awq(m, 1024, (256, 64, 64), 128, seed=3100 + m)
+    xs = (x * np.float32(sigma)).astype(np.float32)
+    worst = _ratio(xs, projs, 128, _run(xs, projs, 128))
+    print(f"range m={m} sigma={sigma}: max |err|/sum|x||w| = {worst:.3e}", flush=True)
+    assert worst <= FP32_RTOL
+
+
+def test_gemv_single_projection_fp32():
+    # the 512 x 512 single projection at M=1 runs the fp32 path too
+    print_case("int4 gemv single 512")
+    x, projs = synth.int4_gemv_512()
+    worst = _ratio(x, projs, 128, _run(x, projs, 128))
+    assert worst <= FP32_RTOL
