@@ -304,6 +304,24 @@ int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k,
                          const int4_awq_proj_t *v_proj, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/* int4_awq_qkv_gemm for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, hosts that forbid hipMalloc.  Same
+ * arguments, rules and results as int4_awq_qkv_gemm with a sufficient
+ * workspace (fp32 activations), but the workspace is a device array inside
+ * the library: KVQ_INT4_NOALLOC_SCRATCH_BYTES on each GPU, held while the
+ * library's code is loaded there (until the process ends).  The call
+ * allocates and frees nothing.  Shapes whose plan needs more scratch than
+ * that return KVQ_E_INVALID (use int4_awq_qkv_gemm with a workspace).
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (different streams, or host threads) race and must be ordered by the
+ * caller. */
+#define KVQ_INT4_NOALLOC_SCRATCH_BYTES (4u << 20)
+int int4_awq_qkv_gemm_noalloc(const float *x, uint32_t m, uint32_t k,
+                              uint32_t group_size,
+                              const int4_awq_proj_t *q_proj,
+                              const int4_awq_proj_t *k_proj,
+                              const int4_awq_proj_t *v_proj, void *stream);
+
 /* ======================================================================== */
 /* Decode attention over the INT8 per-token cache                           */
 /* The consumer of the [KVQ] "INT8 Per-Token Quantization" cache.  The pages

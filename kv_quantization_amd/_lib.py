@@ -57,6 +57,8 @@ SIGNATURES = {
     "int4_awq_workspace_bytes": [_u32, _u32, _u32, _u32, _psz],
     "int4_awq_qkv_gemm_dt": [_p, _i, _u32, _u32, _u32, ctypes.POINTER(Int4AwqProj), ctypes.POINTER(Int4AwqProj),
                              ctypes.POINTER(Int4AwqProj), _p, _sz, _p],
+    "int4_awq_qkv_gemm_noalloc": [_p, _u32, _u32, _u32, ctypes.POINTER(Int4AwqProj), ctypes.POINTER(Int4AwqProj),
+                                  ctypes.POINTER(Int4AwqProj), _p],
     "kvq_stream_read": [_p, _sz, _p, _p],
     "kvq_attn_decode_int8": [_p, _u32, _u32, _u32, _u32, _p, _p, _p, _p, ctypes.c_float, _p, _p, _sz, _p],
     "kvq_attn_decode_workspace_bytes": [_u32, _u32, _u32, _u32, _psz],
@@ -71,6 +73,8 @@ SIGNATURES = {
 
 # include/kvq.h: KVQ_INT8_TENSOR_WORKSPACE_BYTES (counter area + 512 partials)
 INT8_TENSOR_WORKSPACE_BYTES = 4096 + 2048
+# include/kvq.h: KVQ_INT4_NOALLOC_SCRATCH_BYTES (the library's own scratch per GPU)
+INT4_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _lib = None
 

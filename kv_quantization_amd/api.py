@@ -329,6 +329,34 @@ def int4_awq_qkv(x: torch.Tensor, projections, group_size: int, outs=None, use_w
     return res
 
 
+def int4_awq_qkv_noalloc(x: torch.Tensor, projections, group_size: int, outs=None):
+    """int4_awq_qkv through int4_awq_qkv_gemm_noalloc: the library's own
+    per-GPU scratch instead of a workspace (nothing is allocated for it).
+    x fp32 [m, k]; projections and outputs as int4_awq_qkv."""
+    m, k = x.shape
+    if len(projections) not in (1, 3):
+        raise ValueError("need 1 (single) or 3 (Q, K, V) projections")
+    structs, res = [], []
+    for i, (qw, sc, zr) in enumerate(projections):
+        n = int(qw.shape[1]) * 8
+        o = _empty((m, n), torch.float32, x) if outs is None else outs[i]
+        p = Int4AwqProj()
+        if qw.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("qweight must be int32/uint32")
+        p.qweight = _dev(qw, qw.dtype, "qweight")
+        p.scales = _dev(sc, torch.float32, "scales")
+        p.zeros = _dev(zr, torch.float32, "zeros")
+        p.out = _dev(o, torch.float32, "out")
+        p.n = n
+        structs.append(p)
+        res.append(o)
+    kp = ctypes.byref(structs[1]) if len(structs) == 3 else None
+    vp = ctypes.byref(structs[2]) if len(structs) == 3 else None
+    _lib.call("int4_awq_qkv_gemm_noalloc", _dev(x, torch.float32, "x"), m, k, group_size, ctypes.byref(structs[0]),
+              kp, vp, _stream(x))
+    return res
+
+
 # ---------------------------------------------------- decode attention ----
 
 def attn_decode_workspace_bytes(num_q_heads: int, num_kv_heads: int, num_tokens: int, head_dim: int) -> int:

@@ -40,6 +40,8 @@
 // workgroup of a tile adds them in slice order and resets the counter.
 #include "kvq_common.h"
 
+#include <mutex>
+
 namespace kvq {
 namespace {
 
@@ -1010,4 +1012,65 @@ extern "C" int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint
                                     void *stream) {
     return awq_run("int4_awq_qkv_gemm_dt", x, x_dtype, m, k, group_size, q_proj, k_proj, v_proj, workspace,
                    workspace_bytes, stream);
+}
+
+// ---------------------------------------------------- without allocation --
+//
+// int4_awq_qkv_gemm for callers that cannot allocate (code under HIP graph
+// capture, serving loops, hosts that forbid hipMalloc): the workspace is a
+// file-scope device array, one copy per GPU held until the process ends.
+// Host code reaches it only through the address hipGetSymbolAddress returns
+// for the current device (the array's name on the host is a stand-in, not a
+// device address).  Its counter area starts zero (module load) and every
+// call leaves it zero; partial tiles and the fp16 activation copy are
+// written before they are read by each call.  Calls that overlap on one GPU
+// share the array and race.
+
+namespace kvq {
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = KVQ_INT4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+int scratch_of_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVQ_E_LAUNCH, "int4_awq_qkv_gemm_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KVQ_E_UNSUPPORTED, "int4_awq_qkv_gemm_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(e == hipErrorNoBinaryForGpu ? KVQ_E_UNSUPPORTED : KVQ_E_LAUNCH,
+                        "int4_awq_qkv_gemm_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" int int4_awq_qkv_gemm_noalloc(const float *x, uint32_t m, uint32_t k, uint32_t group_size,
+                                         const int4_awq_proj_t *q_proj, const int4_awq_proj_t *k_proj,
+                                         const int4_awq_proj_t *v_proj, void *stream) {
+    const char *fn = "int4_awq_qkv_gemm_noalloc";
+    size_t need = 0;
+    int st = awq_run(fn, x, KVQ_DT_F32, m, k, group_size, q_proj, k_proj, v_proj, nullptr, 0, stream, &need);
+    if (st) return st;
+    if (need > kNoAllocScratchBytes)
+        return fail(KVQ_E_INVALID, "%s: this shape needs %zu bytes of scratch, more than the %zu the library holds "
+                    "per GPU; use int4_awq_qkv_gemm with a workspace", fn, need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st) return st;
+    return awq_run(fn, x, KVQ_DT_F32, m, k, group_size, q_proj, k_proj, v_proj, ws, kNoAllocScratchBytes, stream);
 }

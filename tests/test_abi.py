@@ -288,3 +288,12 @@ def test_attn_decode_varlen_validation(lib):
     assert lib.kvq_attn_decode_varlen_workspace_bytes(64, 32, 8, 256, 128, ctypes.byref(b)) == 0
     assert b.value == 0
 
+
+def test_int4_noalloc_rejects_a_plan_beyond_its_scratch(lib):
+    # 256 rows x K=16384: the fp16 activation copy alone needs 8 MiB; the
+    # call refuses on the host, before any HIP call
+    p = _lib.Int4AwqProj(FAKE, FAKE, FAKE, FAKE, 128)
+    st, msg = _err(lib, "int4_awq_qkv_gemm_noalloc", FAKE, 256, 16384, 128, ctypes.byref(p), None, None, None)
+    assert st == _lib.KVQ_E_INVALID and "scratch" in msg
+    st, msg = _err(lib, "int4_awq_qkv_gemm_noalloc", FAKE, 0, 16384, 128, ctypes.byref(p), None, None, None)
+    assert st == _lib.KVQ_E_INVALID and "m == 0" in msg

@@ -1,0 +1,57 @@
+"""GPU: int4_awq_qkv_gemm_noalloc (the library's own per-GPU scratch instead
+of a caller workspace) gives the same bits as int4_awq_qkv_gemm with a
+workspace, through the C ABI, on two calls in a row (the second smaller), and
+both match the oracle within the contract's bound."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import print_case
+from gpu_util import dev, host
+from kv_quantization_amd import _lib, api, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _bind_oracle(oracle_mod):
+    global _oracle
+    _oracle = oracle_mod
+
+
+def _both(m, k, ns, gs, seed):
+    x, projs = synth.int4_awq(m, k, ns, gs, seed=seed)
+    dp = [(dev(p.qweight.view(np.int32)), dev(p.scales), dev(p.zeros)) for p in projs]
+    xd = dev(x)
+    a = api.int4_awq_qkv_noalloc(xd, dp, gs)
+    torch.cuda.synchronize()
+    a = [host(o) for o in a]
+    b = api.int4_awq_qkv(xd, dp, gs)
+    torch.cuda.synchronize()
+    b = [host(o) for o in b]
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u.view(np.uint32), v.view(np.uint32))
+    refs = _oracle.int4_awq_qkv(x, [(p.qweight, p.scales, p.zeros) for p in projs], gs)
+    for (ref, bound), g in zip(refs, a):
+        assert np.all(np.abs(g.astype(np.float64) - ref) <= 1e-3 * bound)
+
+
+@pytest.mark.parametrize("first,second", [
+    ((8, 4096, (4096, 1024, 1024), 128), (1, 2048, (512, 96, 96), 64)),      # fp32 GEMV: exchange through the scratch
+    ((64, 2048, (1024, 256, 256), 128), (16, 1024, (512, 128, 128), 128)),   # matrix-core path: partials, fp16 copy
+])
+def test_noalloc_matches_workspace_call_twice(first, second):
+    print_case("int4 noalloc", first, second)
+    _both(*first, seed=4000)
+    _both(*second, seed=4001)          # smaller: the scratch keeps the first call's contents
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    print_case("int4 noalloc too large")
+    # 256 rows x K=16384: the fp16 activation copy alone is 8 MiB > 4 MiB
+    x = torch.zeros((256, 16384), dtype=torch.float32, device="cuda")
+    qw = torch.zeros((16384, 16), dtype=torch.int32, device="cuda")
+    sc = torch.zeros((128, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(_lib.KvqError) as e:
+        api.int4_awq_qkv_noalloc(x, [(qw, sc, sc)], 128)
+    assert e.value.status == _lib.KVQ_E_INVALID and "scratch" in str(e.value)
