@@ -25,19 +25,19 @@
 // that each 16-bit half holds the same column's nibble from the two rows: the
 // even columns of a word live in its bytes 0-1, the odd ones in bytes 2-3.
 //
-// Layout of the work: one wave owns 16 word columns (128 output columns) of
-// one projection, a chunk of 16 or 32 activation rows, and a slice of the
-// 32-wide K steps.  Lane (wc = l % 16, kg = l / 16) supplies word column wc
-// and K rows 8*kg .. 8*kg+7 of each step; MFMA number c computes output
-// columns 8*wc + c.  The activation operand holds x~[m][8*kg .. 8*kg+7] in the
-// same K order.  Loads go through buffer resources (SGPR base + per-lane
-// offset + uniform row offset), so the hot loop does no 64-bit address math,
-// and out-of-range lanes read zeros.  A workgroup's 4 waves take 4 K slices of
-// the same tile and meet in LDS; when more K slices are needed to fill the
-// GPU, workgroups exchange fp32 partial tiles through the caller's workspace
-// with device-scope (sc1) stores and loads, which bypass the per-XCD L2s that
-// are not coherent with each other, and an agent-scope counter; the last
+// Layout of the work (16 rows and more, awq_ring): one wave owns 16 word
+// columns (128 output columns) of one projection, a chunk of 16 or 32
+// activation rows, and a run of whole quantization groups.  Lane (wc = l % 16,
+// kg = l / 16) supplies word column wc and K rows 8*kg .. 8*kg+7 of each
+// 32-wide K step; MFMA number c computes output columns 8*wc + c.  The
+// activation operand holds x~[m][8*kg .. 8*kg+7] in the same K order.  The
+// waves of a workgroup take consecutive runs of groups of the same tile and
+// add their sums in LDS; when more K slices are needed to fill the GPU,
+// workgroups exchange fp32 partial tiles through the caller's workspace with
+// device-scope (sc1) stores and loads, which bypass the per-XCD L2s that are
+// not coherent with each other, and an agent-scope counter; the last
 // workgroup of a tile adds them in slice order and resets the counter.
+// Below 16 rows the products run on the vector ALUs (awq_gemv, further down).
 #include "kvq_common.h"
 
 #include <mutex>
@@ -47,8 +47,6 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 4;            // waves per workgroup (K slices of one tile)
-constexpr int kTargetWaves = 2048;
 constexpr uint32_t kXcds = 8;           // XCDs of an MI355X (workgroups are dealt to them in turn)
 
 struct Projs {
@@ -124,42 +122,86 @@ __device__ __forceinline__ f16x8 act_f16x8(const u32x4 &lo, const u32x4 &hi) {
     return h;
 }
 
-// fp32 activations -> fp16 with the rounding act_f16x8<0> applies (round to
-// nearest even), 8 values per thread.  Above 16 rows every column tile
-// re-reads its rows of the activations from L2 over the whole of K, so
-// reading them at half the width pays for this extra pass (M=128: 23.6 ->
-// 18.9 us in the product kernel).
-__global__ __launch_bounds__(256) void x_to_f16(const f32x4 *__restrict__ x, uint32_t n8, f16x8 *__restrict__ y) {
-    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    y[i] = to_f16x8(x[2 * i], x[2 * i + 1]);
+// ------------------------------------------------ matrix-core ring ---
+//
+// 16 rows and more: P_g and X_g on the matrix cores, s and z per group in
+// fp32, codes unpacked by awq_operands, with every wave streaming its own K range through a private ring of R LDS
+// stages, filled by direct-to-LDS loads (buffer_load ... lds).  A stage is KB
+// rows of K: the tile's 16 weight words of each row (KB x 64 bytes), the
+// chunk's MR activation rows over those KB columns, and, on the last stage of
+// a quantization group, the group's 128 scales and 128 zeros.  The wave
+// issues R stages, then per stage waits for exactly that stage (loads return
+// in order, so vmcnt <= L * stages issued after it), reads it into registers,
+// refills the slot with stage +R and multiplies while the loads fly.  No
+// barrier is needed until the waves of the workgroup add their sums, so
+// R stages of every wave are always in flight without holding registers.
+//
+// LDS layouts, chosen so that the reads of a fragment are free of bank
+// conflicts:
+//  * weights: the 32 rows of a K step are stored in the order 4i + kg for
+//    row 8kg + i, so word i of the lanes (wc, kg) lies in 4 consecutive 64-byte
+//    rows: one 256-byte line per read, every lane a different bank;
+//  * activations: row m of the stage holds its 16-byte chunks with chunk c at
+//    slot c ^ swz(m), swz(m) = (m / RPB) mod CPR (CPR chunks per row, RPB rows
+//    per 256 bytes), so the 16 rows read at the same K offset fall into 16
+//    different 16-byte bank groups.
+template <int MT, int XT, int KB, int R, int WV>
+struct RingCfg {
+    static constexpr int MR = 16 * MT;
+    static constexpr int XB = XT == 0 ? 4 : 2;
+    static constexpr int SUB = KB / 32;            // 32-wide K steps per stage
+    static constexpr int W_BYTES = KB * 64;        // KB rows x 16 words
+    static constexpr int X_ROW = KB * XB;          // one activation row of a stage
+    static constexpr int X_BYTES = MR * X_ROW;
+    static constexpr int CPR = X_ROW / 16;
+    static constexpr int RPB = 16 / CPR;
+    static constexpr int W_INSTR = W_BYTES / 1024;
+    static constexpr int X_INSTR = X_BYTES / 1024;
+    static constexpr int SZ_INSTR = 4;             // scales, zeros: 2 x 256-byte loads each
+    static constexpr int L = W_INSTR + X_INSTR + SZ_INSTR;   // loads per stage
+    static constexpr int STAGE = W_BYTES + X_BYTES + 1024;
+    static constexpr int WAVE_BYTES = R * STAGE;
+    static_assert(KB == 32 || KB == 64, "stage rows");
+    static constexpr int SUMS = WV * 16 * 32 * 16;   // the waves' sums, stored over the ring at the end
+    static constexpr int LDS = (WV * WAVE_BYTES > SUMS + 16 ? WV * WAVE_BYTES : SUMS + 16);
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(L * (R - 1) < 64, "vmcnt range");
+    static_assert(X_BYTES % 1024 == 0 && CPR >= 4 && CPR <= 16, "stage shape");
+};
+
+// wait until at most `later` stages of L loads are in flight
+template <int L, int MAXL>
+__device__ __forceinline__ void ring_wait(int later) {
+    if constexpr (MAXL >= 3) {
+        if (later >= 3) { wait_vm<3 * L>(); return; }
+    }
+    if constexpr (MAXL >= 2) {
+        if (later == 2) { wait_vm<2 * L>(); return; }
+    }
+    if constexpr (MAXL >= 1) {
+        if (later == 1) { wait_vm<L>(); return; }
+    }
+    wait_vm<0>();
 }
 
-// MT: 16-row activation tiles per chunk (1 or 2).  R: accumulator rows per
-// lane that can hold real outputs (1 when m == 1, else 4).  KSG: 32-wide K
-// steps per quantization group.  U: K steps loaded together (a "piece"; U
-// divides KSG).  PF: prefetch the next piece while computing this one.
-// WV: waves per workgroup, each a K slice of the tile, summed in LDS.
-template <int MT, int R, int KSG, int U, bool PF, int XT, int WV>
-__global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ x, uint32_t M, uint32_t K, Projs P,
-                                                   uint32_t nchunks, uint32_t ks_b, uint32_t *__restrict__ counters,
-                                                   float *__restrict__ partials) {
-    constexpr int MR = 16 * MT;
-    constexpr uint32_t GS = 32 * KSG;
+template <int MT, int XT, int KB, int R, int WV>
+__global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ x, uint32_t M, uint32_t K,
+                                                      uint32_t gs, Projs P, uint32_t nchunks, uint32_t ks_b,
+                                                      uint32_t *__restrict__ counters, float *__restrict__ partials) {
+    using C = RingCfg<MT, XT, KB, R, WV>;
+    constexpr int MR = C::MR;
     constexpr int NTH = WV * kWave;
-    __shared__ f32x4 red[WV][16][32];
-    __shared__ int s_last;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[C::LDS];
     const int lane = lane_id();
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wc = lane & 15, kg = lane >> 4;
 
-    // Workgroups go to the XCDs in turn (index mod kXcds), and each XCD has
-    // its own L2.  With several row chunks, all workgroups of one tile (its
-    // chunks and K slices) are placed on the XCD of index t mod kXcds, so
-    // the tile's weights are fetched from HBM once instead of once per chunk
-    // (M=128: 65 -> ~30 MB fetched per call); slots past the last tile exit
-    // at once.  With one chunk, consecutive workgroups take the K slices of a
-    // tile (measured faster at M=1: 9.6 vs 11.0 us).
+    // Tile, row chunk and K slice of this workgroup.  Workgroups go to the
+    // XCDs in turn (index mod kXcds), each XCD with its own L2: with several
+    // row chunks, all workgroups of one tile are placed on the XCD of index
+    // t mod kXcds, so the tile's weights are fetched from HBM once instead of
+    // once per chunk; slots past the last tile exit at once.  With one chunk,
+    // consecutive workgroups take the K slices of a tile.
     const uint32_t per_tile = nchunks * ks_b;
     uint32_t t, r;
     if (nchunks > 1) {
@@ -174,92 +216,128 @@ __global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ 
     const uint32_t c = r / ks_b, bs = r % ks_b;
     const int p = (P.count > 1 && t >= P.tstart[1]) ? ((P.count > 2 && t >= P.tstart[2]) ? 2 : 1) : 0;
     const uint32_t np = pick(p, P.n[0], P.n[1], P.n[2]), wp = np / 8;
-    const uint32_t tp = t - pick(p, P.tstart[0], P.tstart[1], P.tstart[2]);   // tile within the projection
-    const uint32_t lw = tp * 16 + wc;     // lane's word column in its projection
-    const bool wok = lw < wp;
+    const uint32_t tp = t - pick(p, P.tstart[0], P.tstart[1], P.tstart[2]);
 
-    // K slice of this wave, in pieces of U steps
-    const uint32_t npieces = K / (32 * U);
-    const uint32_t nsplit = ks_b * WV, split = bs * WV + wv;
-    const uint32_t pc0 = (uint32_t)((uint64_t)split * npieces / nsplit);
-    const uint32_t pc1 = (uint32_t)((uint64_t)(split + 1) * npieces / nsplit);
+    // this wave's whole groups [g0, g1) and its stages
+    const uint32_t ngroups = K / gs;
+    const uint32_t nwaves = ks_b * WV, u = bs * WV + wv;
+    const uint32_t g0 = (uint32_t)((uint64_t)u * ngroups / nwaves);
+    const uint32_t g1 = (uint32_t)((uint64_t)(u + 1) * ngroups / nwaves);
+    const uint32_t spg = gs / KB;                      // stages per group
+    const int nst = (int)((g1 - g0) * spg);
+    const uint32_t krow0 = g0 * gs;
 
-    // buffer resources and per-lane offsets (out-of-range lanes point past the end: reads give 0)
-    const uint32_t wbytes = K * wp * 4;
-    const rsrc_t rw = make_rsrc(pick(p, P.qw[0], P.qw[1], P.qw[2]), wbytes);
-    const uint32_t voff_w = wok ? ((uint32_t)(kg * 8) * wp + lw) * 4 : wbytes;
-    constexpr uint32_t XB = XT == 0 ? 4 : 2;   // bytes per activation value
-    const uint32_t xbytes = M * K * XB;
-    const rsrc_t rx = make_rsrc(x, xbytes);
-    uint32_t voff_x[MT];
+    // buffer resources and the per-lane halves of the load offsets
+    const u32x4 rw = buffer_rsrc(pick(p, P.qw[0], P.qw[1], P.qw[2]), K * wp * 4);
+    const u32x4 rx = buffer_rsrc(x, M * K * C::XB);
+    const uint32_t szb = ngroups * np * 4;
+    const u32x4 rs = buffer_rsrc(pick(p, P.sc[0], P.sc[1], P.sc[2]), szb);
+    const u32x4 rz = buffer_rsrc(pick(p, P.zr[0], P.zr[1], P.zr[2]), szb);
+    uint32_t w_off[C::W_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::W_INSTR; ++j) {
+        const int rho = 16 * (j & 1) + (lane >> 2);
+        const uint32_t row = 32 * (j >> 1) + 8 * (rho & 3) + (rho >> 2);
+        w_off[j] = row * wp * 4 + (tp * 16 + 4 * (lane & 3)) * 4;   // past the row: unused columns
+    }
+    uint32_t x_off[C::X_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::X_INSTR; ++j) {
+        const int e = j * 64 + lane;
+        const int ml = e / C::CPR, cs = e % C::CPR;
+        const int ch = cs ^ ((ml / C::RPB) & (C::CPR - 1));
+        const uint32_t m = c * MR + ml;
+        x_off[j] = m < M ? m * K * C::XB + ch * 16 : kOffNone;   // rows past M read zeros
+    }
+    const uint32_t sz_off = (tp * 128 + lane) * 4;
+
+    const uint32_t ring0 = lds_offset(ring) + wv * C::WAVE_BYTES;
+    auto issue = [&](int b) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(ring0 + (uint32_t)(b % R) * C::STAGE);
+        const uint32_t k0 = krow0 + (uint32_t)b * KB;
+        const uint32_t sw = __builtin_amdgcn_readfirstlane(k0 * wp * 4);
+        const uint32_t sx = __builtin_amdgcn_readfirstlane(k0 * C::XB);
+#pragma unroll
+        for (int j = 0; j < C::W_INSTR; ++j) lds_buf16(rw, w_off[j], sw, base + j * 1024);
+#pragma unroll
+        for (int j = 0; j < C::X_INSTR; ++j) lds_buf16(rx, x_off[j], sx, base + C::W_BYTES + j * 1024);
+        // scales and zeros of the group, on its last stage only (other
+        // stages issue the same loads out of range: no traffic, same count)
+        const bool gend = ((uint32_t)b + 1) % spg == 0;
+        const uint32_t g = g0 + (uint32_t)b / spg;
+        const uint32_t ss = __builtin_amdgcn_readfirstlane(g * np * 4);
+        const uint32_t o = gend ? sz_off : kOffNone;
+        const uint32_t sz0 = base + C::W_BYTES + C::X_BYTES;
+        lds_buf4(rs, o, ss, sz0);
+        lds_buf4(rs, gend ? sz_off + 256 : kOffNone, ss, sz0 + 256);
+        lds_buf4(rz, o, ss, sz0 + 512);
+        lds_buf4(rz, gend ? sz_off + 256 : kOffNone, ss, sz0 + 768);
+    };
+
+    f32x4 acc[MT][8], pg[MT][8], xg[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t m = c * MR + mt * 16 + wc;
-        voff_x[mt] = m < M ? (m * K + kg * 8) * XB : xbytes;
+        xg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) acc[mt][cc] = pg[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const uint32_t szbytes = (K / GS) * np * 4;
-    const rsrc_t rs = make_rsrc(pick(p, P.sc[0], P.sc[1], P.sc[2]), szbytes);
-    const rsrc_t rz = make_rsrc(pick(p, P.zr[0], P.zr[1], P.zr[2]), szbytes);
-    const uint32_t voff_sz = wok ? lw * 32 : szbytes;
-
-    f32x4 acc[MT][8];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) acc[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 pg[MT][8], xg[MT];
-    auto reset = [&]() {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            xg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    };
-    reset();
     f16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
 
-    struct Piece {
-        uint32_t w[U][8];
-        u32x4 xv[U][MT][2];
-    };
-    auto load = [&](uint32_t pc, Piece &pz) {
+    for (int b = 0; b < R && b < nst; ++b) issue(b);
+    for (int b = 0; b < nst; ++b) {
+        const int later = (nst - b < R ? nst - b : R) - 1;
+        ring_wait<C::L, R - 1>(later);
+        asm volatile("" ::: "memory");
+        const uint8_t *st = ring + wv * C::WAVE_BYTES + (b % R) * C::STAGE;
+        uint32_t w[C::SUB][8];
+        u32x4 xv[C::SUB][MT][2];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t k0 = (pc * U + u) * 32;
+        for (int s = 0; s < C::SUB; ++s) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                pz.w[u][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, (k0 + i) * wp * 4, 0);
+                w[s][i] = *reinterpret_cast<const uint32_t *>(st + s * 2048 + (4 * i + kg) * 64 + wc * 4);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                pz.xv[u][mt][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * XB, 0);
-                if (XT == 0) pz.xv[u][mt][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[mt], k0 * 4 + 16, 0);
+                const int ml = mt * 16 + wc;
+                const int swz = (ml / C::RPB) & (C::CPR - 1);
+                const uint8_t *xr = st + C::W_BYTES + ml * C::X_ROW;
+                if (XT == 0) {
+                    const int c0 = 8 * s + 2 * kg;
+                    xv[s][mt][0] = *reinterpret_cast<const u32x4 *>(xr + ((c0 ^ swz) << 4));
+                    xv[s][mt][1] = *reinterpret_cast<const u32x4 *>(xr + (((c0 + 1) ^ swz) << 4));
+                } else {
+                    xv[s][mt][0] = *reinterpret_cast<const u32x4 *>(xr + (((4 * s + kg) ^ swz) << 4));
+                    xv[s][mt][1] = xv[s][mt][0];
+                }
             }
         }
-    };
-    auto compute = [&](uint32_t pc, const Piece &pz) {
+        const bool gend = ((uint32_t)b + 1) % spg == 0;
+        f32x4 s0, s1, z0, z1;
+        if (gend) {
+            const uint8_t *sz = st + C::W_BYTES + C::X_BYTES;
+            s0 = *reinterpret_cast<const f32x4 *>(sz + 32 * wc);
+            s1 = *reinterpret_cast<const f32x4 *>(sz + 32 * wc + 16);
+            z0 = *reinterpret_cast<const f32x4 *>(sz + 512 + 32 * wc);
+            z1 = *reinterpret_cast<const f32x4 *>(sz + 512 + 32 * wc + 16);
+        }
+        // the slot's reads are done: refill it while this stage is multiplied
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (b + R < nst) issue(b + R);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int s = 0; s < C::SUB; ++s) {
             f16x8 B[8];
-            awq_operands(pz.w[u], B);
+            awq_operands(w[s], B);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const f16x8 a = act_f16x8<XT>(pz.xv[u][mt][0], pz.xv[u][mt][1]);
+                const f16x8 a = act_f16x8<XT>(xv[s][mt][0], xv[s][mt][1]);
                 xg[mt] = mfma16(a, ones, xg[mt]);
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = mfma16(a, B[cc], pg[mt][cc]);
             }
         }
-        // group epilogue at the end of a group or of this wave's slice
-        const uint32_t kstep_end = (pc + 1) * U;
-        if (kstep_end % KSG == 0 || pc + 1 == pc1) {
-            const uint32_t g = (pc * U) / KSG;
-            const f32x4 s0 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff_sz, g * np * 4, 0));
-            const f32x4 s1 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff_sz, g * np * 4 + 16, 0));
-            const f32x4 z0 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rz, voff_sz, g * np * 4, 0));
-            const f32x4 z1 = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rz, voff_sz, g * np * 4 + 16, 0));
+        if (gend) {
             // columns 0,1,4,5 were unpacked as q*2^-24, columns 2,3,6,7 as q*2^-20
             const float f[8] = {0x1p24f, 0x1p24f, 0x1p20f, 0x1p20f, 0x1p24f, 0x1p24f, 0x1p20f, 0x1p20f};
             const float sv[8] = {s0.x * f[0], s0.y * f[1], s0.z * f[2], s0.w * f[3],
@@ -267,39 +345,27 @@ __global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ 
             const float zv[8] = {z0.x / f[0], z0.y / f[1], z0.z / f[2], z0.w / f[3],
                                  z1.x / f[4], z1.y / f[5], z1.z / f[6], z1.w / f[7]};
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc)
+                for (int cc = 0; cc < 8; ++cc) {
 #pragma unroll
-                    for (int i = 0; i < R; ++i)
+                    for (int i = 0; i < 4; ++i)
                         acc[mt][cc][i] = __builtin_fmaf(sv[cc], __builtin_fmaf(-zv[cc], xg[mt][i], pg[mt][cc][i]),
                                                         acc[mt][cc][i]);
-            reset();
-        }
-    };
-
-    if (PF) {
-        Piece b0, b1;
-        if (pc0 < pc1) load(pc0, b0);
-        for (uint32_t pc = pc0; pc < pc1; pc += 2) {
-            if (pc + 1 < pc1) load(pc + 1, b1);
-            compute(pc, b0);
-            if (pc + 1 < pc1) {
-                if (pc + 2 < pc1) load(pc + 2, b0);
-                compute(pc + 1, b1);
+                    pg[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+                xg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-        }
-    } else {
-        for (uint32_t pc = pc0; pc < pc1; ++pc) {
-            Piece b0;
-            load(pc, b0);
-            compute(pc, b0);
         }
     }
 
-    // Waves -> LDS, one 16-row tile at a time, as [row][column] with
-    // row = 4*kg + i and column = 8*wc + cc; then 256 threads add the four
-    // waves' values and write 16-byte pieces of the output (or partial) rows.
+    // Waves -> LDS (the ring's memory, once every wave is done with it), one
+    // 16-row tile at a time, as [row][column] with row = 4*kg + i and column
+    // = 8*wc + cc; then the threads add the waves' values in wave order and
+    // write 16-byte pieces of the output (or partial) rows.
+    __syncthreads();
+    f32x4(*red)[16][32] = reinterpret_cast<f32x4(*)[16][32]>(ring);
+    int *s_last = reinterpret_cast<int *>(ring + C::SUMS);
     const uint32_t tile_id = t * nchunks + c;
     float *part = partials + (size_t)tile_id * ks_b * (MR * 128);
     const rsrc_t rp = make_rsrc(part, ks_b * (MR * 128) * 4);
@@ -320,7 +386,7 @@ __global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ 
             if (m >= M || lwo >= wp) continue;
             f32x4 v = red[0][row][col4];
 #pragma unroll
-            for (int w = 1; w < WV; ++w) v += red[w][row][col4];
+            for (int w2 = 1; w2 < WV; ++w2) v += red[w2][row][col4];
             if (ks_b == 1) {
                 *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + 8 * lwo + (col4 & 1) * 4) = v;
             } else {
@@ -332,38 +398,36 @@ __global__ __launch_bounds__(WV * kWave) void awq_gemm(const void *__restrict__ 
     }
     if (ks_b == 1) return;
 
-    // Cross-workgroup K reduction (see the header comment): every thread's
-    // device-scope stores have completed before the barrier, so they are
-    // visible at the coherence point before the counter moves; the last
-    // workgroup's device-scope loads are issued after it has seen the count.
+    // cross-workgroup K reduction: every thread's device-scope stores have
+    // completed before the barrier, so they are visible at the coherence
+    // point before the counter moves; the last workgroup's device-scope loads
+    // are issued after it has seen the count
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(&counters[tile_id], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == ks_b - 1;
+        *s_last = prev == ks_b - 1;
     }
     __syncthreads();
-    if (!s_last) return;
+    if (!*s_last) return;
     for (int e = threadIdx.x; e < MR * 32; e += NTH) {
         const int row = e >> 5, col4 = e & 31;
         const uint32_t m = c * MR + row;
         const uint32_t lwo = tp * 16 + (col4 >> 1);
         if (m >= M || lwo >= wp) continue;
-        // up to 8 partials in flight, added in slice order (deterministic;
-        // one load at a time paid a memory round trip per slice)
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         for (uint32_t q0 = 0; q0 < ks_b; q0 += 8) {
-            u32x4 t[8];
+            u32x4 tq[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t q = q0 + u;
+            for (int uu = 0; uu < 8; ++uu) {
+                const uint32_t q = q0 + uu;
                 const uint32_t off = q < ks_b ? ((q * MR + row) * 128 + col4 * 4) * 4 : kOffNone;
-                t[u] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSc1);
+                tq[uu] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSc1);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (q0 + u < ks_b) v += as_f32x4(t[u]);
+            for (int uu = 0; uu < 8; ++uu)
+                if (q0 + uu < ks_b) v += as_f32x4(tq[uu]);
         }
         *reinterpret_cast<f32x4 *>(outp + (size_t)m * np + 8 * lwo + (col4 & 1) * 4) = v;
     }
@@ -657,7 +721,7 @@ __global__ __launch_bounds__(GW * kWave) void awq_gemv(const void *__restrict__ 
     }
     if (slices == 1) return;
 
-    // cross-workgroup sum, as in awq_gemm: stores complete and visible at
+    // cross-workgroup sum, as in awq_ring: stores complete and visible at
     // device scope before the counter moves; the last workgroup loads after
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -690,49 +754,50 @@ __global__ __launch_bounds__(GW * kWave) void awq_gemv(const void *__restrict__ 
 
 // ------------------------------------------------------------------ host --
 
-struct Plan {
-    uint32_t mt, mr, nchunks, ks_b, u, wv;
-    size_t counter_bytes, partial_bytes;
-    size_t x16_bytes;   // fp16 copy of fp32 activations (two 16-row tiles per wave)
-    size_t x16_offset;  // behind the counter area (kept zero for every call) and the partials
-    size_t ws_bytes;    // workspace this plan uses in full
+// ---- matrix-core ring plan (m >= 16)
+constexpr int kRingWaves = 8;
+constexpr int kRingStages = 2;
+constexpr uint32_t kRingTargetWgs = 256;   // one 8-wave workgroup per CU
+
+struct RingPlan {
+    uint32_t mt, mr, nchunks, ks_b, kb;
+    size_t counter_bytes, partial_bytes, ws_bytes;
 };
 
-uint32_t piece_steps(uint32_t mt, uint32_t ksg) {
-    const uint32_t cap = mt == 1 ? 4 : 1;   // two 16-row tiles: one K step per piece, prefetched
-    return ksg < cap ? ksg : cap;
-}
-
-Plan make_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles) {
-    Plan pl;
+// 16 rows per wave up to 16 rows, else 32-row chunks; 64-row stages except
+// where the group is 32 rows or two fp32 row tiles would not fit the ring;
+// K slices (a power of two, whole groups per wave) until ~one workgroup per CU
+RingPlan ring_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles, int xt) {
+    RingPlan pl;
     pl.mt = m <= 16 ? 1 : 2;
     pl.mr = 16 * pl.mt;
     pl.nchunks = (m + pl.mr - 1) / pl.mr;
-    pl.u = piece_steps(pl.mt, gs / 32);
-    // two 16-row tiles per wave (M > 16): 8 waves split K inside the
-    // workgroup (LDS), which leaves fewer or no slices to exchange between
-    // workgroups (M=128: 28 -> 24 us); one tile: 4 waves measured faster
-    pl.wv = pl.mt == 2 ? 8 : kWaves;
-    const uint32_t npieces = k / (32 * pl.u);
+    pl.kb = (gs >= 64 && !(pl.mt == 2 && xt == KVQ_DT_F32)) ? 64 : 32;
     const uint64_t units = (uint64_t)ntiles * pl.nchunks;
-    // 2 <= m <= 16 streams the same weights as m = 1 with four times the
-    // matrix work per word: fewer, longer K slices exchange fewer partials
-    uint64_t waves = (m > 1 && m <= 16 ? kTargetWaves / 2 : kTargetWaves) / (units ? units : 1);
-    if (waves > npieces) waves = npieces;
-    // a power of two: consecutive workgroups go to the 8 XCDs in turn, so
-    // with ks_b | 8 or 8 | ks_b each XCD's L2 sees a fixed subset of the K
-    // slices and holds only that part of the activations (measured at M=16:
-    // ks_b 5 -> 4 halves the fetched bytes, 12.1 -> 11.3 us)
+    const uint32_t ngroups = k / gs;
     pl.ks_b = 1;
-    while (pl.ks_b * 2 <= waves / pl.wv) pl.ks_b *= 2;
+    while (units * pl.ks_b * 2 <= kRingTargetWgs && (uint64_t)pl.ks_b * 2 * kRingWaves <= ngroups) pl.ks_b *= 2;
     const size_t tiles = (size_t)ntiles * pl.nchunks;
     if (tiles * 4 > KVQ_WORKSPACE_COUNTER_BYTES) pl.ks_b = 1;   // more tiles than counters: no exchange
     pl.counter_bytes = pl.ks_b > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;
     pl.partial_bytes = pl.ks_b > 1 ? tiles * pl.ks_b * pl.mr * 128 * 4 : 0;
-    pl.x16_bytes = pl.mt == 2 ? ((size_t)m * k * 2 + 255) / 256 * 256 : 0;
-    pl.x16_offset = KVQ_WORKSPACE_COUNTER_BYTES + pl.partial_bytes;
-    pl.ws_bytes = pl.x16_bytes ? pl.x16_offset + pl.x16_bytes : pl.counter_bytes + pl.partial_bytes;
+    pl.ws_bytes = pl.counter_bytes + pl.partial_bytes;
     return pl;
+}
+
+// two fp32 row tiles per wave only fit the ring with 32-row stages
+template <int MT, int XT>
+void ring_launch(const RingPlan &pl, uint64_t blocks, const void *x, uint32_t m, uint32_t k, uint32_t gs,
+                 const Projs &P, uint32_t *counters, float *partials, hipStream_t s) {
+    if constexpr (!(MT == 2 && XT == 0)) {
+        if (pl.kb == 64) {
+            awq_ring<MT, XT, 64, kRingStages, kRingWaves><<<(unsigned)blocks, kRingWaves * kWave, 0, s>>>(
+                x, m, k, gs, P, pl.nchunks, pl.ks_b, counters, partials);
+            return;
+        }
+    }
+    awq_ring<MT, XT, 32, kRingStages, kRingWaves><<<(unsigned)blocks, kRingWaves * kWave, 0, s>>>(
+        x, m, k, gs, P, pl.nchunks, pl.ks_b, counters, partials);
 }
 
 int check_proj(const char *fn, const int4_awq_proj_t *p, const char *which, uint32_t k, uint32_t gs) {
@@ -809,7 +874,7 @@ extern "C" int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_s
             const GemvPlan g = gemv_plan(m, k, group_size, gemv_tiles_of(n_total) + extra, true);
             if (g.ws_bytes > *bytes) *bytes = g.ws_bytes;
         } else {
-            const Plan pl = make_plan(m, k, group_size, tiles_of(n_total) + extra);
+            const RingPlan pl = ring_plan(m, k, group_size, tiles_of(n_total) + extra, KVQ_DT_F32);
             if (pl.ws_bytes > *bytes) *bytes = pl.ws_bytes;
         }
     }
@@ -931,7 +996,7 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
         return launch_status(fn);
     }
 
-    Plan pl = make_plan(m, k, group_size, P.ntiles);
+    RingPlan pl = ring_plan(m, k, group_size, P.ntiles, xt);
     if (need) {
         *need = pl.ws_bytes;
         return KVQ_OK;
@@ -939,7 +1004,7 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
     uint32_t *counters = nullptr;
     float *partials = nullptr;
     if (pl.ks_b > 1) {
-        if (!workspace || workspace_bytes < pl.counter_bytes + pl.partial_bytes || !aligned16(workspace)) {
+        if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
             pl.ks_b = 1;   // no (or too small) workspace: one workgroup per tile
         } else {
             counters = static_cast<uint32_t *>(workspace);
@@ -949,49 +1014,15 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
     const uint64_t tile_slots = pl.nchunks > 1 ? (uint64_t)kXcds * ((P.ntiles + kXcds - 1) / kXcds) : P.ntiles;
     const uint64_t blocks = tile_slots * pl.nchunks * pl.ks_b;
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
-    // fp32 activations with two 16-row tiles per wave: convert once to fp16
-    // behind the partials when the workspace holds it, then read that copy
-    if (xt == KVQ_DT_F32 && pl.x16_bytes && workspace && aligned16(workspace) && workspace_bytes >= pl.ws_bytes) {
-        void *x16 = static_cast<uint8_t *>(workspace) + pl.x16_offset;
-        const uint32_t n8 = (uint32_t)((uint64_t)m * k / 8);
-        x_to_f16<<<(n8 + 255) / 256, 256, 0, s>>>(static_cast<const f32x4 *>(x), n8, static_cast<f16x8 *>(x16));
-        x = x16;
-        xt = KVQ_DT_F16;
-    }
-    const uint32_t ksg = group_size / 32;
-#define KVQ_AWQ3(MT, R, KSG, U, PF, WV)                                                                        \
-    do {                                                                                                       \
-        if (xt == KVQ_DT_F32)                                                                                  \
-            awq_gemm<MT, R, KSG, U, PF, 0, WV><<<(unsigned)blocks, WV * kWave, 0, s>>>(x, m, k, P, pl.nchunks, \
-                                                                                  pl.ks_b, counters, partials); \
-        else if (xt == KVQ_DT_F16)                                                                             \
-            awq_gemm<MT, R, KSG, U, PF, 1, WV><<<(unsigned)blocks, WV * kWave, 0, s>>>(x, m, k, P, pl.nchunks, \
-                                                                                  pl.ks_b, counters, partials); \
-        else                                                                                                   \
-            awq_gemm<MT, R, KSG, U, PF, 2, WV><<<(unsigned)blocks, WV * kWave, 0, s>>>(x, m, k, P, pl.nchunks, \
-                                                                                  pl.ks_b, counters, partials); \
-    } while (0)
-#define KVQ_AWQ(MT, R, KSG, U, PF)                                 \
-    do {                                                           \
-        if (pl.wv == 8) KVQ_AWQ3(MT, R, KSG, U, PF, 8);            \
-        else KVQ_AWQ3(MT, R, KSG, U, PF, kWaves);                  \
-    } while (0)
-#define KVQ_AWQ_K(MT, R, CAP, PF)                                   \
-    switch (ksg) {                                                  \
-        case 1: KVQ_AWQ(MT, R, 1, 1, PF); break;                    \
-        case 2: KVQ_AWQ(MT, R, 2, 2, PF); break;                    \
-        case 4: KVQ_AWQ(MT, R, 4, (CAP < 4 ? CAP : 4), PF); break;  \
-        default: KVQ_AWQ(MT, R, 8, (CAP < 4 ? CAP : 4), PF); break; \
-    }
     if (pl.mt == 1) {
-        if (m == 1) KVQ_AWQ_K(1, 1, 4, true)
-        else KVQ_AWQ_K(1, 4, 4, true)
+        if (xt == KVQ_DT_F32) ring_launch<1, 0>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
+        else if (xt == KVQ_DT_F16) ring_launch<1, 1>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
+        else ring_launch<1, 2>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
     } else {
-        KVQ_AWQ_K(2, 4, 1, true)
+        if (xt == KVQ_DT_F32) ring_launch<2, 0>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
+        else if (xt == KVQ_DT_F16) ring_launch<2, 1>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
+        else ring_launch<2, 2>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
     }
-#undef KVQ_AWQ_K
-#undef KVQ_AWQ
-#undef KVQ_AWQ3
     return launch_status(fn);
 }
 

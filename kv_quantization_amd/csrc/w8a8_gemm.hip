@@ -526,52 +526,6 @@ constexpr int kWideWaves = 8;                              // waves that multipl
 constexpr int kWideLoaders = 4;                            // waves that only load (2 per stream)
 constexpr int kWideThreads = (kWideWaves + kWideLoaders) * kWave;
 
-// LDS byte offset of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// Raw buffer resource (4 SGPRs): base, stride 0, size in bytes (reads past
-// it return zero), untyped dword format of the gfx9 family.
-__device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    u32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
-    r[2] = __builtin_amdgcn_readfirstlane(bytes);
-    r[3] = 0x00020000u;
-    return r;
-}
-
-// Direct loads into LDS, written as inline assembly so that the compiler does
-// not add its conservative "all LDS DMA complete" wait before every LDS read;
-// the ring waits explicitly (wait_vm) for exactly the stage it is about to
-// read.  lds_wave_base must be wave-uniform (it goes to M0).  M0 is named as
-// clobbered; nothing else in these kernels keeps a value in M0 (gfx9 LDS
-// instructions do not use it), so the "reserved register" warning does not
-// apply.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_buf16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_wave_base) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 ::"v"(voff), "s"(rsrc), "s"(soff), "s"(lds_wave_base) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_buf4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_wave_base) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-                 ::"v"(voff), "s"(rsrc), "s"(soff), "s"(lds_wave_base) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_glb16(const void *g, uint32_t lds_wave_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <int MTW, int KIND>
 struct WideCfg {

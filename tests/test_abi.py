@@ -149,15 +149,17 @@ def test_workspace_sizes(lib):
     assert b.value > 0          # small M slices K across workgroups
     assert lib.int4_awq_workspace_bytes(1, 512, 128, 512, ctypes.byref(b)) == 0
     assert b.value == 0         # tiny problem: one workgroup per tile
-    # above 16 rows it also holds an fp16 copy of fp32 activations (rounded
-    # to 256 bytes), always behind the counter area, which other calls on the
-    # same workspace expect at zero; at 128 rows x 6144 columns K is not
-    # split: counter area and copy only
+    # 16 rows and more (matrix cores): counter area and partial tiles when K
+    # is split, with up to two extra tiles for any split of n into three
+    # projections; 16 rows x 6144 columns: 4 K slices of 16 x 128 fp32 tiles
     counters = 4096
+    assert lib.int4_awq_workspace_bytes(16, 4096, 128, 6144, ctypes.byref(b)) == 0
+    assert b.value == counters + (6144 // 128 + 2) * 4 * 16 * 128 * 4
+    # 128 rows x 6144 columns: enough (tile, row chunk) units, K is not split
     assert lib.int4_awq_workspace_bytes(128, 4096, 128, 6144, ctypes.byref(b)) == 0
-    assert b.value == counters + 128 * 4096 * 2
+    assert b.value == 0
     assert lib.int4_awq_workspace_bytes(17, 96, 32, 8, ctypes.byref(b)) == 0
-    assert b.value == counters + (17 * 96 * 2 + 255) // 256 * 256   # one tile, 3 K steps: no split either
+    assert b.value == 0         # one tile, 3 groups: fewer groups than waves, no split
     assert lib.int4_awq_workspace_bytes(16, 96, 32, 8, ctypes.byref(b)) == 0
     assert b.value == 0
     assert lib.w8a8_gemv_workspace_bytes(0, 8, 4096, 6144, ctypes.byref(b)) == 0
@@ -290,10 +292,11 @@ def test_attn_decode_varlen_validation(lib):
 
 
 def test_int4_noalloc_rejects_a_plan_beyond_its_scratch(lib):
-    # 256 rows x K=16384: the fp16 activation copy alone needs 8 MiB; the
-    # call refuses on the host, before any HIP call
-    p = _lib.Int4AwqProj(FAKE, FAKE, FAKE, FAKE, 128)
-    st, msg = _err(lib, "int4_awq_qkv_gemm_noalloc", FAKE, 256, 16384, 128, ctypes.byref(p), None, None, None)
+    # 32 rows x K=4096 x 16384 columns: 128 tiles in 2 K slices of 32 x 128
+    # fp32 partials need 4 MiB behind the 4 KiB counter area; the call
+    # refuses on the host, before any HIP call
+    p = _lib.Int4AwqProj(FAKE, FAKE, FAKE, FAKE, 16384)
+    st, msg = _err(lib, "int4_awq_qkv_gemm_noalloc", FAKE, 32, 4096, 128, ctypes.byref(p), None, None, None)
     assert st == _lib.KVQ_E_INVALID and "scratch" in msg
     st, msg = _err(lib, "int4_awq_qkv_gemm_noalloc", FAKE, 0, 16384, 128, ctypes.byref(p), None, None, None)
     assert st == _lib.KVQ_E_INVALID and "m == 0" in msg

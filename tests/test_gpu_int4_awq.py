@@ -94,33 +94,31 @@ def test_without_workspace_same_bits_order_independent(m):
 
 @pytest.mark.parametrize("m,k,ns", [(33, 2048, (8192, 1024, 1024)), (128, 4096, (4096, 1024, 1024)),
                                     (256, 1024, (2048, 512, 512))])
-def test_fp32_activations_fp16_copy_same_bits(m, k, ns):
-    """Above 16 rows fp32 activations are rounded to fp16 once, into the
-    workspace, and read from there; without a workspace they are rounded
-    inside the product kernel.  These shapes have more than 128 (tile, row
-    chunk) units, so neither call splits K across workgroups: same plan, same
-    fp16 operands, the same bits."""
-    print_case("int4 fp32 x via fp16 copy", m, k)
+def test_no_k_split_needs_no_workspace(m, k, ns):
+    """These shapes have more than 128 (tile, row chunk) units, so no call
+    splits K across workgroups: the workspace query says 0 bytes, and calls
+    with and without a workspace run the same plan and give the same bits."""
+    print_case("int4 no split-K", m, k)
     x, projs = synth.int4_awq(m, k, ns, 128, seed=1900 + m)
-    # the counter area (4096 bytes, left zero) and the copy: no partial tiles
-    assert api.int4_workspace_bytes(m, k, 128, sum(ns)) == 4096 + (m * k * 2 + 255) // 256 * 256
+    assert api.int4_workspace_bytes(m, k, 128, sum(ns)) == 0
     a = _run(x, projs, 128, use_workspace=True)
     b = _run(x, projs, 128, use_workspace=False)
-    _check(x, projs, 128, a, f"fp16 copy m={m}")
+    _check(x, projs, 128, a, f"no split m={m}")
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u.view(np.uint32), v.view(np.uint32))
 
 
-def test_fp16_copy_leaves_counter_area_zero():
-    """A call that writes the fp16 activation copy (128 rows, no K split)
-    followed on the same workspace by calls that count K slices through the
-    counter area (1 and 5 rows): the copy lies behind that area."""
-    print_case("int4 fp16 copy then split-K")
+def test_large_call_then_split_k_calls():
+    """A call without K split (128 rows) followed, on the same workspace, by
+    calls that count K slices through the counter area (1, 5 and 16 rows):
+    every counter is back at zero after each call."""
+    print_case("int4 large call then split-K")
     x5, projs = _qkv_inputs()
     _check(x5[:128], projs, 128, _run(x5[:128], projs, 128), "qkv M=128")
-    for m in (1, 5):
+    for m in (1, 5, 16):
         x, small = synth.int4_awq(m, 512, (136, 24, 24), 32, seed=2000 + m)
-        _check(x, small, 32, _run(x, small, 32), f"after copy m={m}")
+        _check(x, small, 32, _run(x, small, 32), f"after the large call m={m}")
+        _check(x, small, 32, _run(x, small, 32), f"again m={m}")
 
 
 def test_single_is_q_part_of_fused():

@@ -38,7 +38,7 @@ def _both(m, k, ns, gs, seed):
 
 @pytest.mark.parametrize("first,second", [
     ((8, 4096, (4096, 1024, 1024), 128), (1, 2048, (512, 96, 96), 64)),      # fp32 GEMV: exchange through the scratch
-    ((64, 2048, (1024, 256, 256), 128), (16, 1024, (512, 128, 128), 128)),   # matrix-core path: partials, fp16 copy
+    ((64, 2048, (1024, 256, 256), 128), (16, 1024, (512, 128, 128), 128)),   # matrix-core path: partial tiles, then no split
 ])
 def test_noalloc_matches_workspace_call_twice(first, second):
     print_case("int4 noalloc", first, second)
@@ -48,10 +48,11 @@ def test_noalloc_matches_workspace_call_twice(first, second):
 
 def test_noalloc_rejects_shapes_beyond_its_scratch():
     print_case("int4 noalloc too large")
-    # 256 rows x K=16384: the fp16 activation copy alone is 8 MiB > 4 MiB
-    x = torch.zeros((256, 16384), dtype=torch.float32, device="cuda")
-    qw = torch.zeros((16384, 16), dtype=torch.int32, device="cuda")
-    sc = torch.zeros((128, 128), dtype=torch.float32, device="cuda")
+    # 32 rows x K=4096 x 16384 columns: 2 K slices of 128 tiles of 32 x 128
+    # fp32 partials need 4 MiB behind the counter area, > 4 MiB in all
+    x = torch.zeros((32, 4096), dtype=torch.float32, device="cuda")
+    qw = torch.zeros((4096, 2048), dtype=torch.int32, device="cuda")
+    sc = torch.zeros((32, 16384), dtype=torch.float32, device="cuda")
     with pytest.raises(_lib.KvqError) as e:
         api.int4_awq_qkv_noalloc(x, [(qw, sc, sc)], 128)
     assert e.value.status == _lib.KVQ_E_INVALID and "scratch" in str(e.value)
