@@ -22,10 +22,10 @@ ceil(512 MiB / working set) copies of that kernel's own inputs and outputs
 median of 5 replays.  ``us_warm`` repeats one copy.  The dominant kernel's
 roofline comes from its cold time.
 
-``--only NAME`` times one kernel cold and nothing else (after five 256 MiB
-device copies that calibrate the traffic counters): the command the
-rocprofv3 kernel-trace and FETCH_SIZE / WRITE_SIZE summaries under profiles/
-are taken with.
+``--only NAME[,NAME...]`` times the named kernels cold and nothing else
+(after five 256 MiB device copies that calibrate the traffic counters), one
+JSON line each: the command the rocprofv3 kernel-trace and counter summaries
+under profiles/ are taken with.
 
 Prints ONE JSON line.  --gpus N with N > 1 exits: every kernel here runs on
 one GPU.
@@ -529,8 +529,9 @@ def tensors_of(s):
 
 # ------------------------------------------------------------------ main --
 
-def run_only(torch, api, name, reps, stream, log):
-    """Time one kernel cold, nothing else (profiler runs)."""
+def run_only(torch, api, names, reps, stream, log):
+    """Time the named kernels (comma-separated) cold, nothing else (profiler
+    runs); one JSON line per kernel."""
     src = torch.empty(COPY_CALIB_MIB << 20, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     for _ in range(5):
@@ -541,19 +542,21 @@ def run_only(torch, api, name, reps, stream, log):
     bufs = StepBuffers(torch, api, base)
     table = {r[0]: r for r in kernel_table() + extra_table()}
     launch = {n: (f, a) for n, f, a in bufs.launchers(api) + bufs.extra_launchers(api)}
-    if name not in launch:
-        print(f"bench.py: unknown kernel {name!r}; one of: {', '.join(launch)}", file=sys.stderr)
-        sys.exit(2)
-    fn, args = launch[name]
-    with torch.cuda.stream(stream):
-        fn(*args)                      # eager: allocates the workspace
-    torch.cuda.synchronize()
-    log(f"timing {name} cold")
-    sec, copies, launches, ws = time_cold(torch, api, fn, args, stream, reps)
-    _, nbytes, flops, kind = table[name]
-    print(json.dumps({"kernel": name, "us": round(sec * 1e6, 2), "copies": copies, "launches": launches,
-                      "working_set_bytes": ws, "algorithmic_bytes": nbytes,
-                      "roofline": roofline_for(name, nbytes, flops, kind, sec)}), flush=True)
+    for name in names.split(","):
+        if name not in launch:
+            print(f"bench.py: unknown kernel {name!r}; one of: {', '.join(launch)}", file=sys.stderr)
+            sys.exit(2)
+    for name in names.split(","):
+        fn, args = launch[name]
+        with torch.cuda.stream(stream):
+            fn(*args)                      # eager: allocates the workspace
+        torch.cuda.synchronize()
+        log(f"timing {name} cold")
+        sec, copies, launches, ws = time_cold(torch, api, fn, args, stream, reps)
+        _, nbytes, flops, kind = table[name]
+        print(json.dumps({"kernel": name, "us": round(sec * 1e6, 2), "copies": copies, "launches": launches,
+                          "working_set_bytes": ws, "algorithmic_bytes": nbytes,
+                          "roofline": roofline_for(name, nbytes, flops, kind, sec)}), flush=True)
 
 
 def main():
@@ -563,7 +566,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated by the step (0: >= 768 MiB of them)")
     ap.add_argument("--kernel-reps", type=int, default=100, help="least launches per isolated kernel timing")
-    ap.add_argument("--only", default=None, help="time this one kernel cold and nothing else")
+    ap.add_argument("--only", default=None, help="time these kernels (comma-separated) cold and nothing else")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single-core", action="store_true", help="skip the one-thread oracle step")
     ap.add_argument("--no-check", action="store_true", help="skip the graph-vs-eager self-check")

@@ -197,22 +197,32 @@ __global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ 
     const int wc = lane & 15, kg = lane >> 4;
 
     // Tile, row chunk and K slice of this workgroup.  Workgroups go to the
-    // XCDs in turn (index mod kXcds), each XCD with its own L2: with several
-    // row chunks, all workgroups of one tile are placed on the XCD of index
-    // t mod kXcds, so the tile's weights are fetched from HBM once instead of
-    // once per chunk; slots past the last tile exit at once.  With one chunk,
-    // consecutive workgroups take the K slices of a tile.
+    // XCDs in turn (index mod kXcds), each XCD with its own L2.  A tile's rows
+    // of weights are 64-byte runs, so tiles 2p and 2p+1 of a projection share
+    // every 128-byte line: the pair is placed on one XCD (dispatched
+    // together), which fetches each line from HBM once instead of twice.
+    // With several row chunks, all workgroups of a pair sit on the XCD of
+    // index p mod kXcds (the chunks re-read the same weights); with one
+    // chunk, the pair's workgroups of K slice bs go to XCD (p*ks_b + bs) mod
+    // kXcds, so each XCD's L2 holds few K slices of the activations.  Slots
+    // past the last tile exit at once.
     const uint32_t per_tile = nchunks * ks_b;
-    uint32_t t, r;
+    const uint32_t npairs = (P.ntiles + 1) / 2;
+    const uint32_t xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    uint32_t pair, h, r;
     if (nchunks > 1) {
-        const uint32_t j = blockIdx.x / kXcds;
-        t = blockIdx.x % kXcds + kXcds * (j / per_tile);
-        r = j % per_tile;
-        if (t >= P.ntiles) return;
+        pair = xcd + kXcds * (j / (2 * per_tile));
+        const uint32_t rr = j % (2 * per_tile);
+        h = rr % 2;
+        r = rr / 2;
     } else {
-        t = blockIdx.x / per_tile;
-        r = blockIdx.x % per_tile;
+        h = j % 2;
+        const uint32_t g = kXcds * (j / 2) + xcd;
+        pair = g / ks_b;
+        r = g % ks_b;
     }
+    const uint32_t t = 2 * pair + h;
+    if (pair >= npairs || t >= P.ntiles) return;
     const uint32_t c = r / ks_b, bs = r % ks_b;
     const int p = (P.count > 1 && t >= P.tstart[1]) ? ((P.count > 2 && t >= P.tstart[2]) ? 2 : 1) : 0;
     const uint32_t np = pick(p, P.n[0], P.n[1], P.n[2]), wp = np / 8;
@@ -1011,8 +1021,11 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
             partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.counter_bytes);
         }
     }
-    const uint64_t tile_slots = pl.nchunks > 1 ? (uint64_t)kXcds * ((P.ntiles + kXcds - 1) / kXcds) : P.ntiles;
-    const uint64_t blocks = tile_slots * pl.nchunks * pl.ks_b;
+    // the kernel's placement: tile pairs on one XCD (see there)
+    const uint64_t npairs = (P.ntiles + 1) / 2;
+    const uint64_t blocks = pl.nchunks > 1
+                                ? (uint64_t)kXcds * ((npairs + kXcds - 1) / kXcds) * 2 * pl.nchunks * pl.ks_b
+                                : 2 * (uint64_t)kXcds * ((npairs * pl.ks_b + kXcds - 1) / kXcds);
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
     if (pl.mt == 1) {
         if (xt == KVQ_DT_F32) ring_launch<1, 0>(pl, blocks, x, m, k, group_size, P, counters, partials, s);

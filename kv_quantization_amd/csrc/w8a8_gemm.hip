@@ -506,20 +506,25 @@ void fused_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t
 // rows > 32: one workgroup owns all (<= 256) activation rows and 128 output
 // columns over one slice of K (split-K), so the weight tile is read from HBM
 // once per call and the activation tile (re-read by every column tile) comes
-// from L2.  8 waves in a 4 (rows) x 2 (64 columns) grid, two per SIMD, so one
-// wave's scaling arithmetic overlaps the other's matrix instructions.  Each
-// 128-wide K step of both tiles (and the activation block scales) travels
-// global -> LDS with direct DMA loads (lane i's 16 bytes land at LDS base +
-// 16*i) through a two-stage ring: one K step in flight while the other is
-// multiplied.  Rows are stored with their eight 16-byte chunks XOR-swizzled
-// by (row & 7), which keeps both the load pattern and the MFMA operand reads
-// (ds_read_b128) free of bank conflicts.  The loads are buffer loads from
-// wave-uniform bases (the per-lane offsets never change; rows past the end
-// of the activations or of a weight segment read as zero); a 128-column tile
-// that straddles two weight segments (possible only with per-row scales)
-// uses per-lane global addresses instead.  With split-K the fp32 partial
-// tiles go to the workspace and w8a8_reduce adds them in split order
-// (deterministic), applies per-row scales and writes bf16.
+// from L2.  8 multiplying waves in a 4 (rows) x 2 (64 columns) grid, two per
+// SIMD, so one wave's scaling arithmetic overlaps the other's matrix
+// instructions, and 4 loader waves: two stream the activation tile (and its
+// block scales), two the weight tile, each into its own LDS ring with direct
+// DMA loads (lane i's 16 bytes land at LDS base + 16*i).  The activation ring
+// has 3 stages (its tiles come from L2), the weight ring what LDS leaves, up
+// to 8 (its tiles come from HBM with the longer latency).  A loader waits for
+// its own loads of the next K step (vmcnt), then every wave meets at one
+// barrier per K step; a multiplying wave reads the next activation fragment
+// before the matrix instructions of the current one.  Rows are stored with
+// their eight 16-byte chunks XOR-swizzled by (row & 7), which keeps both the
+// load pattern and the MFMA operand reads (ds_read_b128) free of bank
+// conflicts.  The loads are buffer loads from wave-uniform bases (the
+// per-lane offsets never change; rows past the end of the activations or of
+// a weight segment read as zero); a 128-column tile that straddles two weight
+// segments (possible only with per-row scales) uses per-lane global addresses
+// instead.  With split-K the fp32 partial tiles go to the workspace and
+// w8a8_reduce adds them in split order (deterministic), applies per-row
+// scales and writes bf16.
 
 constexpr int kWideN = 128;
 constexpr int kWideWaves = 8;                              // waves that multiply
