@@ -422,9 +422,11 @@ def time_cold(torch, api, fn, args, stream, reps):
 # <kernel>`, each scaled by what the counter reads for a 256 MiB device copy.
 # Reported only while every listed source (comments aside) is the one the
 # counters were taken on.
-TRAFFIC = {"w8a8_gemm_blk128_M256": {"bytes": 136316069,
+TRAFFIC = {"w8a8_gemm_blk128_M256": {"bytes": 132675584,
                                      "sources": {"kv_quantization_amd/csrc/w8a8_gemm.hip":
-                                                 "b726fabd67eb798d13491df72e134473203496b71d443563902c6727647a8d17"}}}
+                                                 "c1135df59efd6f675cb71d927b830d0740e008e6f923bb2561fb4aed01a248c0",
+                                                 "kv_quantization_amd/csrc/kvq_common.h":
+                                                 "b77ff8ec048dd95b28a74a8fac2ed8f89bd33c35a443965ca2a10f3f39a07c55"}}}
 
 
 def code_digest(path):
