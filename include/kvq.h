@@ -49,7 +49,7 @@ int kvq_abi_version(void);
 /* Workspaces (w8a8_gemv, w8a8_proj, int4_awq_qkv_gemm): the first
  * KVQ_WORKSPACE_COUNTER_BYTES bytes hold the counters through which the
  * workgroups of one output tile find the last of them; every call leaves
- * them at zero, and partial sums (and the INT4 call's fp16 activation copy)
+ * them at zero, and partial sums (and the INT4 call's scaled fp16 activations)
  * only ever go behind them, also when a call uses no counters.  One zero-filled
  * buffer can therefore serve calls of all three kinds, in any order, as long
  * as they are ordered on one stream. */
@@ -269,19 +269,26 @@ typedef struct {
  * GEMV on the vector ALUs: codes unpacked to exact floats, x unrounded, s
  * and z applied once per group as s * (sum x q - z * sum x)); 9..15 rows run
  * as two launches of at most 8.
- * m >= 16: the matrix cores take x rounded to fp16 (round to nearest even)
- * and the exact codes, accumulating in fp32; |x| must stay below 65504 (a
- * larger value becomes inf; the error from the rounding is at most 2^-11
- * |x| per term).
+ * m >= 16: the matrix cores take fp16 activations and the exact codes,
+ * accumulating in fp32.  fp32 (and bf16) rows are first scaled by the power
+ * of two 2^E that puts the row's absmax in [2^14, 2^15) and rounded to fp16
+ * (nearest even); each output row is multiplied by 2^-E (exact).  Every term
+ * thus keeps 2^-11 relative precision at any fp32 activation scale (rows of
+ * 1e-6 or 1e5 alike; zero rows and rows holding inf or NaN are left
+ * unscaled).  When a wave's K range fits its LDS ring the wave takes the
+ * absmax over its own K range and scales in registers; otherwise one extra
+ * launch writes the scaled fp16 rows and their 2^-E into the workspace.
+ * Without a workspace, such shapes round x to fp16 unscaled inside the
+ * product kernel: then |x| must stay below 65504 (a larger value becomes
+ * inf) and terms below 2^-14 lose relative precision (fp16 subnormals).
  * workspace: NULL, or at least int4_awq_workspace_bytes(), zero-filled before
  * its first use; the call leaves its counter area at zero and writes partial
- * tiles behind it, and for m > 16 the fp16-rounded activations behind those
- * (one extra launch converts them; every column tile then reads half the
- * bytes).  Without it, one workgroup per tile (less parallelism) and, for
- * m > 16, the rounding happens inside the product kernel: the same fp16
- * operands.  The workspace arguments extend the page's call (which has
- * none): split-K partial sums need device scratch the library does not
- * allocate.  Concurrent calls must not share a workspace. */
+ * tiles behind it, and for m >= 16 the scaled fp16 activations and their
+ * row scales behind those.  Without it, one workgroup per tile (less
+ * parallelism) and the unscaled rounding above.  The workspace arguments
+ * extend the page's call (which has none): split-K partial sums and the
+ * scaled copy need device scratch the library does not allocate.
+ * Concurrent calls must not share a workspace. */
 int int4_awq_qkv_gemm(const float *x, uint32_t m, uint32_t k,
                       uint32_t group_size, const int4_awq_proj_t *q_proj,
                       const int4_awq_proj_t *k_proj,
@@ -294,10 +301,9 @@ int int4_awq_workspace_bytes(uint32_t m, uint32_t k, uint32_t group_size,
 /* The same call with 16-bit activations (kvq_dtype_t: KVQ_DT_F32, KVQ_DT_F16
  * or KVQ_DT_BF16; x holds m*k values of that type).  m < 16: the values are
  * widened exactly to fp32 (the same results as the fp32 call on the widened
- * values).  m >= 16: fp16 values go to the matrix cores unchanged; bf16
- * values are widened exactly and rounded to fp16 like fp32 input (exact for
- * |x| in [2^-14, 65504]).  Outputs stay fp32.  KVQ_DT_F32 is exactly
- * int4_awq_qkv_gemm. */
+ * values).  m >= 16: fp16 values go to the matrix cores unchanged (exact);
+ * bf16 values are widened exactly and then scaled and rounded like fp32
+ * input.  Outputs stay fp32.  KVQ_DT_F32 is exactly int4_awq_qkv_gemm. */
 int int4_awq_qkv_gemm_dt(const void *x, int x_dtype, uint32_t m, uint32_t k,
                          uint32_t group_size, const int4_awq_proj_t *q_proj,
                          const int4_awq_proj_t *k_proj,

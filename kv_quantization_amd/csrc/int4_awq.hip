@@ -122,6 +122,142 @@ __device__ __forceinline__ f16x8 act_f16x8(const u32x4 &lo, const u32x4 &hi) {
     return h;
 }
 
+// The same 8 values as fp32 (fp32 as is, bf16 widened exactly), for the
+// per-row power-of-two scaling (XT 0 and 2).
+template <int XT>
+__device__ __forceinline__ void act_f32x8(const u32x4 &lo, const u32x4 &hi, float v[8]) {
+    if (XT == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = __uint_as_float(lo[j]);
+            v[4 + j] = __uint_as_float(hi[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(lo[j] << 16);
+            v[2 * j + 1] = __uint_as_float(lo[j] & 0xFFFF0000u);
+        }
+    }
+}
+
+// x * 2^e rounded to fp16 (nearest even); the product by a power of two is exact
+template <int XT>
+__device__ __forceinline__ f16x8 act_f16x8_scaled(const u32x4 &lo, const u32x4 &hi, int e) {
+    float v[8];
+    act_f32x8<XT>(lo, hi, v);
+    f16x8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)__builtin_ldexpf(v[j], e);
+    return h;
+}
+
+// The exponent E that puts a row's absmax (as non-negative float bits) into
+// [2^14, 2^15): 0 for zero rows and rows holding inf or NaN, else clamped to
+// +-126 so that 2^-E stays a normal float.
+__device__ __forceinline__ int row_pow2(int amax_bits) {
+    if (amax_bits == 0 || amax_bits >= 0x7F800000) return 0;
+    int ex;
+    (void)__builtin_frexpf(__int_as_float(amax_bits), &ex);   // absmax in [2^(ex-1), 2^ex)
+    const int e = 15 - ex;
+    return e < -126 ? -126 : (e > 126 ? 126 : e);
+}
+
+// ------------------------------------------ activation pre-scaling ---
+//
+// From 16 rows the matrix cores take fp16 activations.  fp16 keeps 11 bits
+// only between 2^-14 and 65504: a row of tiny values (|x| ~ 1e-6) would keep
+// a few bits and a row past 65504 would become inf.  So fp32 (and bf16) rows
+// are scaled by a power of two 2^E_m that puts the row's absmax into
+// [2^14, 2^15) and rounded to fp16 (nearest even) once, into the workspace;
+// the product kernel reads that copy and multiplies each output row by
+// 2^-E_m, which is exact.  The sums are linear in x, so the result is the
+// same as with unscaled activations, except that every term now keeps 2^-11
+// relative precision.  One workgroup per row: an absmax pass, then the scaled
+// conversion (the row is read again from L2).  Rows that are zero or hold inf
+// or NaN keep E = 0 (inf and NaN then reach the outputs as they would).
+template <int XT>
+__global__ __launch_bounds__(256) void x_pow2_f16(const void *__restrict__ x, uint32_t K, f16x8 *__restrict__ y,
+                                                  float *__restrict__ inv_scale) {
+    constexpr uint32_t XB = XT == 0 ? 4 : 2;
+    __shared__ int wmax[4];
+    const uint32_t m = blockIdx.x;
+    const uint32_t n8 = K / 8;
+    const rsrc_t rx = make_rsrc(static_cast<const uint8_t *>(x) + (size_t)m * K * XB, K * XB);
+    auto load8 = [&](uint32_t i, float v[8]) {
+        if (XT == 0) {
+            const f32x4 a = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rx, i * 32, 0, 0));
+            const f32x4 b = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rx, i * 32 + 16, 0, 0));
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rx, i * 16, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = __uint_as_float(h[j] << 16);
+                v[2 * j + 1] = __uint_as_float(h[j] & 0xFFFF0000u);
+            }
+        }
+    };
+    // absmax over the row (non-negative floats, inf and NaN included, order
+    // as their bits); rows up to 8192 values stay in registers for the
+    // conversion, longer ones are read again (from L2)
+    constexpr int NR = 4;   // 8-value chunks per thread kept in registers
+    const bool held = n8 <= NR * 256;
+    float v[NR][8];
+    int amax = 0;
+    if (held) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const uint32_t i = threadIdx.x + 256 * j;
+            if (i < n8) {
+                load8(i, v[j]);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int b = __float_as_int(v[j][q]) & 0x7FFFFFFF;
+                    amax = b > amax ? b : amax;
+                }
+            }
+        }
+    } else {
+        for (uint32_t i = threadIdx.x; i < n8; i += 256) {
+            float u[8];
+            load8(i, u);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int b = __float_as_int(u[q]) & 0x7FFFFFFF;
+                amax = b > amax ? b : amax;
+            }
+        }
+    }
+    amax = team_ext<64, true>(amax);
+    if (lane_id() == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) amax = wmax[w] > amax ? wmax[w] : amax;
+    const int e = row_pow2(amax);
+    if (threadIdx.x == 0) inv_scale[m] = __builtin_ldexpf(1.0f, -e);
+    auto store8 = [&](uint32_t i, const float *u) {
+        f16x8 h;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) h[q] = (_Float16)__builtin_ldexpf(u[q], e);
+        y[(size_t)m * n8 + i] = h;
+    };
+    if (held) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const uint32_t i = threadIdx.x + 256 * j;
+            if (i < n8) store8(i, v[j]);
+        }
+    } else {
+        for (uint32_t i = threadIdx.x; i < n8; i += 256) {
+            float u[8];
+            load8(i, u);
+            store8(i, u);
+        }
+    }
+}
+
 // ------------------------------------------------ matrix-core ring ---
 //
 // 16 rows and more: P_g and X_g on the matrix cores, s and z per group in
@@ -187,7 +323,8 @@ __device__ __forceinline__ void ring_wait(int later) {
 template <int MT, int XT, int KB, int R, int WV>
 __global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ x, uint32_t M, uint32_t K,
                                                       uint32_t gs, Projs P, uint32_t nchunks, uint32_t ks_b,
-                                                      uint32_t *__restrict__ counters, float *__restrict__ partials) {
+                                                      uint32_t *__restrict__ counters, float *__restrict__ partials,
+                                                      const float *__restrict__ rscale, int inscale) {
     using C = RingCfg<MT, XT, KB, R, WV>;
     constexpr int MR = C::MR;
     constexpr int NTH = WV * kWave;
@@ -296,6 +433,60 @@ __global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ 
     for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
 
     for (int b = 0; b < R && b < nst; ++b) issue(b);
+    // Per-row power-of-two scaling inside the wave (fp32 and bf16 input, when
+    // the wave's whole K range fits in its ring, nst <= R): every stage has
+    // been issued, so wait for all of them, take each of the wave's rows'
+    // absmax over its K range, and scale the activations by 2^E into fp16
+    // below; the wave's sums are multiplied by 2^-E per output row at the
+    // end (exact).  Lane (wc, kg) holds row mt*16+wc; its 4 K quarters are
+    // lanes 16 apart.
+    int erow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) erow[mt] = 0;
+    if (XT != 1 && inscale) {
+        wait_vm<0>();
+        asm volatile("" ::: "memory");
+        int amax[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) amax[mt] = 0;
+        for (int b = 0; b < nst; ++b) {
+            const uint8_t *st = ring + wv * C::WAVE_BYTES + (b % R) * C::STAGE;
+#pragma unroll
+            for (int s = 0; s < C::SUB; ++s) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int ml = mt * 16 + wc;
+                    const int swz = (ml / C::RPB) & (C::CPR - 1);
+                    const uint8_t *xr = st + C::W_BYTES + ml * C::X_ROW;
+                    u32x4 lo, hi;
+                    if (XT == 0) {
+                        const int c0 = 8 * s + 2 * kg;
+                        lo = *reinterpret_cast<const u32x4 *>(xr + ((c0 ^ swz) << 4));
+                        hi = *reinterpret_cast<const u32x4 *>(xr + (((c0 + 1) ^ swz) << 4));
+                    } else {
+                        lo = *reinterpret_cast<const u32x4 *>(xr + (((4 * s + kg) ^ swz) << 4));
+                        hi = lo;
+                    }
+                    float v[8];
+                    act_f32x8<XT>(lo, hi, v);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int bits = __float_as_int(v[q]) & 0x7FFFFFFF;
+                        amax[mt] = bits > amax[mt] ? bits : amax[mt];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            int a = amax[mt];
+            auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)a, false, false);
+            a = (int)r32[0] > (int)r32[1] ? (int)r32[0] : (int)r32[1];
+            auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)a, false, false);
+            a = (int)r16[0] > (int)r16[1] ? (int)r16[0] : (int)r16[1];
+            erow[mt] = row_pow2(a);
+        }
+    }
     for (int b = 0; b < nst; ++b) {
         const int later = (nst - b < R ? nst - b : R) - 1;
         ring_wait<C::L, R - 1>(later);
@@ -341,7 +532,8 @@ __global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ 
             awq_operands(w[s], B);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const f16x8 a = act_f16x8<XT>(xv[s][mt][0], xv[s][mt][1]);
+                const f16x8 a = (XT != 1 && inscale) ? act_f16x8_scaled<XT>(xv[s][mt][0], xv[s][mt][1], erow[mt])
+                                                     : act_f16x8<XT>(xv[s][mt][0], xv[s][mt][1]);
                 xg[mt] = mfma16(a, ones, xg[mt]);
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = mfma16(a, B[cc], pg[mt][cc]);
@@ -380,6 +572,29 @@ __global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ 
     float *part = partials + (size_t)tile_id * ks_b * (MR * 128);
     const rsrc_t rp = make_rsrc(part, ks_b * (MR * 128) * 4);
     float *outp = pick(p, P.out[0], P.out[1], P.out[2]);
+    // activations scaled by 2^E per row inside the wave: undo it on the lane's
+    // output rows 4kg..4kg+3, whose exponents lanes 4kg..4kg+3 hold
+    if (XT != 1 && inscale) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 sc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sc[i] = __builtin_ldexpf(1.0f, -__builtin_amdgcn_ds_bpermute((4 * kg + i) * 4, erow[mt]));
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) acc[mt][cc] *= sc;
+        }
+    }
+    // activations pre-scaled by 2^E per row: undo it (exact) on the lane's output rows
+    if (rscale) {
+        const rsrc_t rr = make_rsrc(rscale, M * 4);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 sc = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rr, (c * MR + mt * 16 + 4 * kg) * 4, 0, 0));
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) acc[mt][cc] *= sc;   // rows past M: zero sums times zero
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -771,43 +986,61 @@ constexpr uint32_t kRingTargetWgs = 256;   // one 8-wave workgroup per CU
 
 struct RingPlan {
     uint32_t mt, mr, nchunks, ks_b, kb;
-    size_t counter_bytes, partial_bytes, ws_bytes;
+    bool inscale;                       // rows scaled inside each wave (its K range fits its ring)
+    size_t counter_bytes, partial_bytes;
+    size_t x16_offset, x16_bytes;       // pre-scaled fp16 activations (fp32 and bf16 input), behind the partials
+    size_t scale_offset, scale_bytes;   // their per-row 2^-E
+    size_t ws_bytes;                    // workspace this plan uses in full
 };
+
+uint32_t ring_kb(uint32_t mt, uint32_t gs, int xt) { return (gs >= 64 && !(mt == 2 && xt == KVQ_DT_F32)) ? 64 : 32; }
 
 // 16 rows per wave up to 16 rows, else 32-row chunks; 64-row stages except
 // where the group is 32 rows or two fp32 row tiles would not fit the ring;
-// K slices (a power of two, whole groups per wave) until ~one workgroup per CU
+// K slices (a power of two, whole groups per wave) until ~one workgroup per
+// CU.  fp32 and bf16 rows are scaled by powers of two into fp16: inside
+// each wave when its whole K range fits its ring, else by the pre-pass into
+// the workspace (then the product reads fp16).
 RingPlan ring_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles, int xt) {
     RingPlan pl;
     pl.mt = m <= 16 ? 1 : 2;
     pl.mr = 16 * pl.mt;
     pl.nchunks = (m + pl.mr - 1) / pl.mr;
-    pl.kb = (gs >= 64 && !(pl.mt == 2 && xt == KVQ_DT_F32)) ? 64 : 32;
     const uint64_t units = (uint64_t)ntiles * pl.nchunks;
     const uint32_t ngroups = k / gs;
     pl.ks_b = 1;
     while (units * pl.ks_b * 2 <= kRingTargetWgs && (uint64_t)pl.ks_b * 2 * kRingWaves <= ngroups) pl.ks_b *= 2;
     const size_t tiles = (size_t)ntiles * pl.nchunks;
     if (tiles * 4 > KVQ_WORKSPACE_COUNTER_BYTES) pl.ks_b = 1;   // more tiles than counters: no exchange
+    pl.kb = ring_kb(pl.mt, gs, xt);
+    const uint32_t gpw = (ngroups + pl.ks_b * kRingWaves - 1) / (pl.ks_b * kRingWaves);   // most groups of a wave
+    pl.inscale = xt != KVQ_DT_F16 && gpw * (gs / pl.kb) <= (uint32_t)kRingStages;
+    const bool pre = xt != KVQ_DT_F16 && !pl.inscale;
+    if (pre) pl.kb = ring_kb(pl.mt, gs, KVQ_DT_F16);   // the product then reads the fp16 copy
     pl.counter_bytes = pl.ks_b > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;
     pl.partial_bytes = pl.ks_b > 1 ? tiles * pl.ks_b * pl.mr * 128 * 4 : 0;
-    pl.ws_bytes = pl.counter_bytes + pl.partial_bytes;
+    // the counter area is always kept (zero) in front when the copy is there
+    pl.x16_offset = KVQ_WORKSPACE_COUNTER_BYTES + pl.partial_bytes;
+    pl.x16_bytes = pre ? ((size_t)m * k * 2 + 255) / 256 * 256 : 0;
+    pl.scale_offset = pl.x16_offset + pl.x16_bytes;
+    pl.scale_bytes = pre ? ((size_t)m * 4 + 255) / 256 * 256 : 0;
+    pl.ws_bytes = pre ? pl.scale_offset + pl.scale_bytes : pl.counter_bytes + pl.partial_bytes;
     return pl;
 }
 
 // two fp32 row tiles per wave only fit the ring with 32-row stages
 template <int MT, int XT>
 void ring_launch(const RingPlan &pl, uint64_t blocks, const void *x, uint32_t m, uint32_t k, uint32_t gs,
-                 const Projs &P, uint32_t *counters, float *partials, hipStream_t s) {
+                 const Projs &P, uint32_t *counters, float *partials, const float *rscale, hipStream_t s) {
     if constexpr (!(MT == 2 && XT == 0)) {
         if (pl.kb == 64) {
             awq_ring<MT, XT, 64, kRingStages, kRingWaves><<<(unsigned)blocks, kRingWaves * kWave, 0, s>>>(
-                x, m, k, gs, P, pl.nchunks, pl.ks_b, counters, partials);
+                x, m, k, gs, P, pl.nchunks, pl.ks_b, counters, partials, rscale, pl.inscale ? 1 : 0);
             return;
         }
     }
     awq_ring<MT, XT, 32, kRingStages, kRingWaves><<<(unsigned)blocks, kRingWaves * kWave, 0, s>>>(
-        x, m, k, gs, P, pl.nchunks, pl.ks_b, counters, partials);
+        x, m, k, gs, P, pl.nchunks, pl.ks_b, counters, partials, rscale, pl.inscale ? 1 : 0);
 }
 
 int check_proj(const char *fn, const int4_awq_proj_t *p, const char *which, uint32_t k, uint32_t gs) {
@@ -1013,13 +1246,31 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
     }
     uint32_t *counters = nullptr;
     float *partials = nullptr;
+    const float *rscale = nullptr;
+    const bool have_ws = workspace && aligned16(workspace) && workspace_bytes >= pl.ws_bytes;
     if (pl.ks_b > 1) {
-        if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) {
+        if (!have_ws) {
             pl.ks_b = 1;   // no (or too small) workspace: one workgroup per tile
         } else {
             counters = static_cast<uint32_t *>(workspace);
             partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.counter_bytes);
         }
+    }
+    if (pl.x16_bytes && have_ws) {
+        // fp32 / bf16 activations: per-row power-of-two scaling into fp16
+        f16x8 *x16 = reinterpret_cast<f16x8 *>(static_cast<uint8_t *>(workspace) + pl.x16_offset);
+        float *sc = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.scale_offset);
+        if (xt == KVQ_DT_F32) x_pow2_f16<0><<<m, 256, 0, s>>>(x, k, x16, sc);
+        else x_pow2_f16<2><<<m, 256, 0, s>>>(x, k, x16, sc);
+        int st = launch_status(fn);
+        if (st) return st;
+        x = x16;
+        xt = KVQ_DT_F16;
+        rscale = sc;
+    } else if (pl.x16_bytes) {
+        // without a workspace the product kernel rounds the activations
+        // itself, unscaled
+        pl.kb = ring_kb(pl.mt, group_size, xt);
     }
     // the kernel's placement: tile pairs on one XCD (see there)
     const uint64_t npairs = (P.ntiles + 1) / 2;
@@ -1028,13 +1279,13 @@ int awq_run(const char *fn, const void *x, int xt, uint32_t m, uint32_t k, uint3
                                 : 2 * (uint64_t)kXcds * ((npairs * pl.ks_b + kXcds - 1) / kXcds);
     if (blocks > 0x7FFFFFFFull) return fail(KVQ_E_INVALID, "%s: problem too large", fn);
     if (pl.mt == 1) {
-        if (xt == KVQ_DT_F32) ring_launch<1, 0>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
-        else if (xt == KVQ_DT_F16) ring_launch<1, 1>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
-        else ring_launch<1, 2>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
+        if (xt == KVQ_DT_F32) ring_launch<1, 0>(pl, blocks, x, m, k, group_size, P, counters, partials, rscale, s);
+        else if (xt == KVQ_DT_F16) ring_launch<1, 1>(pl, blocks, x, m, k, group_size, P, counters, partials, rscale, s);
+        else ring_launch<1, 2>(pl, blocks, x, m, k, group_size, P, counters, partials, rscale, s);
     } else {
-        if (xt == KVQ_DT_F32) ring_launch<2, 0>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
-        else if (xt == KVQ_DT_F16) ring_launch<2, 1>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
-        else ring_launch<2, 2>(pl, blocks, x, m, k, group_size, P, counters, partials, s);
+        if (xt == KVQ_DT_F32) ring_launch<2, 0>(pl, blocks, x, m, k, group_size, P, counters, partials, rscale, s);
+        else if (xt == KVQ_DT_F16) ring_launch<2, 1>(pl, blocks, x, m, k, group_size, P, counters, partials, rscale, s);
+        else ring_launch<2, 2>(pl, blocks, x, m, k, group_size, P, counters, partials, rscale, s);
     }
     return launch_status(fn);
 }

@@ -149,17 +149,22 @@ def test_workspace_sizes(lib):
     assert b.value > 0          # small M slices K across workgroups
     assert lib.int4_awq_workspace_bytes(1, 512, 128, 512, ctypes.byref(b)) == 0
     assert b.value == 0         # tiny problem: one workgroup per tile
-    # 16 rows and more (matrix cores): counter area and partial tiles when K
-    # is split, with up to two extra tiles for any split of n into three
-    # projections; 16 rows x 6144 columns: 4 K slices of 16 x 128 fp32 tiles
+    # 16 rows and more (matrix cores): the counter area and partial tiles
+    # when K is split (up to two extra tiles for any split of n into three
+    # projections); when a wave's K range does not fit its ring, also the
+    # per-row power-of-two scaled fp16 copy of the activations and the row
+    # scales, each rounded up to 256 bytes
     counters = 4096
+    r256 = lambda v: (v + 255) // 256 * 256
+    # 16 rows x 6144 columns: 4 K slices of 16 x 128 fp32 tiles; one group
+    # per wave, scaled inside the wave
     assert lib.int4_awq_workspace_bytes(16, 4096, 128, 6144, ctypes.byref(b)) == 0
     assert b.value == counters + (6144 // 128 + 2) * 4 * 16 * 128 * 4
-    # 128 rows x 6144 columns: enough (tile, row chunk) units, K is not split
+    # 128 rows x 6144 columns: K is not split, 4 groups per wave: the copy
     assert lib.int4_awq_workspace_bytes(128, 4096, 128, 6144, ctypes.byref(b)) == 0
-    assert b.value == 0
+    assert b.value == counters + 128 * 4096 * 2 + 512
     assert lib.int4_awq_workspace_bytes(17, 96, 32, 8, ctypes.byref(b)) == 0
-    assert b.value == 0         # one tile, 3 groups: fewer groups than waves, no split
+    assert b.value == 0         # one tile, 3 groups of 32: fits the rings, no split
     assert lib.int4_awq_workspace_bytes(16, 96, 32, 8, ctypes.byref(b)) == 0
     assert b.value == 0
     assert lib.w8a8_gemv_workspace_bytes(0, 8, 4096, 6144, ctypes.byref(b)) == 0

@@ -94,18 +94,37 @@ def test_without_workspace_same_bits_order_independent(m):
 
 @pytest.mark.parametrize("m,k,ns", [(33, 2048, (8192, 1024, 1024)), (128, 4096, (4096, 1024, 1024)),
                                     (256, 1024, (2048, 512, 512))])
-def test_no_k_split_needs_no_workspace(m, k, ns):
+def test_no_k_split_workspace_holds_the_scaled_copy(m, k, ns):
     """These shapes have more than 128 (tile, row chunk) units, so no call
-    splits K across workgroups: the workspace query says 0 bytes, and calls
-    with and without a workspace run the same plan and give the same bits."""
+    splits K across workgroups: the workspace holds the counter area (left
+    zero), the per-row power-of-two scaled fp16 copy of the activations and
+    the row scales.  Without a workspace the product kernel rounds the
+    activations itself, unscaled; both pass."""
     print_case("int4 no split-K", m, k)
     x, projs = synth.int4_awq(m, k, ns, 128, seed=1900 + m)
-    assert api.int4_workspace_bytes(m, k, 128, sum(ns)) == 0
-    a = _run(x, projs, 128, use_workspace=True)
-    b = _run(x, projs, 128, use_workspace=False)
-    _check(x, projs, 128, a, f"no split m={m}")
-    for u, v in zip(a, b):
-        np.testing.assert_array_equal(u.view(np.uint32), v.view(np.uint32))
+    r256 = lambda b: (b + 255) // 256 * 256
+    assert api.int4_workspace_bytes(m, k, 128, sum(ns)) == 4096 + r256(m * k * 2) + r256(m * 4)
+    _check(x, projs, 128, _run(x, projs, 128, use_workspace=True), f"scaled copy m={m}")
+    _check(x, projs, 128, _run(x, projs, 128, use_workspace=False), f"in-kernel rounding m={m}")
+
+
+@pytest.mark.parametrize("m", [16, 40, 128])
+@pytest.mark.parametrize("kind", ["tiny", "huge", "mixed"])
+def test_matrix_core_activation_range(m, kind):
+    """From 16 rows the activations reach the matrix cores as fp16, each row
+    scaled by a power of two that puts its absmax in [2^14, 2^15): rows of
+    1e-6 keep 11 bits per term and rows of 1e5 (past fp16's 65504) do not
+    overflow.  Mixed: rows alternate 1e-6, 1e5, exact zeros and N(0, 1)."""
+    print_case("int4 matrix-core activation range", m, kind)
+    x, projs = synth.int4_awq(m, 1024, (256, 64, 64), 128, seed=2400 + m)
+    if kind == "tiny":
+        x = (x * 1e-6).astype(np.float32)
+    elif kind == "huge":
+        x = (x * 1e5).astype(np.float32)
+    else:
+        f = np.array([1e-6, 1e5, 0.0, 1.0], dtype=np.float64)[np.arange(m) % 4]
+        x = (x * f[:, None]).astype(np.float32)
+    _check(x, projs, 128, _run(x, projs, 128), f"{kind} m={m}")
 
 
 def test_large_call_then_split_k_calls():
