@@ -36,8 +36,6 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBlock = 256;
-
 struct Segs {
     const uint8_t *w[3];
     const float *s[3];
@@ -832,8 +830,20 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
     }
 
 
-    // ---- epilogue: bf16 output (no split) or fp32 partial tile [split][rows][N]
-    float *part = partials + (size_t)split * rows * S.ntotal;
+    // ---- epilogue: bf16 output (no split), or the fp32 partial tile in the
+    // accumulators' own layout: per (tile, split) [wm][mt][wn][nt][lane] of
+    // f32x4 (lane (r16, g) holds column r16 of its 16x16 block and rows
+    // 4g..4g+3), so every wave writes whole 1 KiB blocks with 16-byte stores.
+    // Rows past `rows` and columns past the weights hold zero sums.
+    if (splits > 1) {
+        f32x4 *part = reinterpret_cast<f32x4 *>(partials) + (size_t)blockIdx.x * (4 * MTW * 2 * 4 * kWave);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                __builtin_nontemporal_store(acc[mt][nt], part + (((wm * MTW + mt) * 2 + wn) * 4 + nt) * kWave + lane);
+        return;
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         const uint32_t col = n0 + wn * 64 + nt * 16 + r16;
@@ -841,63 +851,57 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
         const int sg = seg_of(S, col);
         const uint32_t jl = col - S.start[sg];
         if (jl >= S.n[sg]) continue;
-        const float sw = (KIND == 0 && splits == 1) ? S.s[sg][jl] : 1.0f;
+        const float sw = KIND == 0 ? S.s[sg][jl] : 1.0f;
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t m = wm * 16 * MTW + mt * 16 + 4 * g + e;
                 if (m >= rows) continue;
-                if (splits == 1) {
-                    const float y = KIND == 0 ? acc[mt][nt][e] * sa[m] * sw : acc[mt][nt][e];
-                    out[(size_t)m * ldc + col] = bf16_rne(y);
-                } else {
-                    part[(size_t)m * S.ntotal + col] = acc[mt][nt][e];
-                }
+                const float y = KIND == 0 ? acc[mt][nt][e] * sa[m] * sw : acc[mt][nt][e];
+                out[(size_t)m * ldc + col] = bf16_rne(y);
             }
         }
     }
 }
 
-// Sum the split-K partials [splits][rows][N] in split order, scale (per-row
-// kind), round to bf16.  One thread per 4 consecutive output columns of a row
-// (16-byte partial loads; needs N % 4 == 0, so no 4-column group leaves its
-// row, and per-row segments are multiples of 16 columns, so none straddles a
-// segment), or per column otherwise.
-template <int KIND, int V>
-__global__ __launch_bounds__(kBlock) void w8a8_reduce(const float *__restrict__ partials, uint32_t splits,
-                                                      const float *__restrict__ sa, uint32_t rows, Segs S,
-                                                      uint16_t *__restrict__ out, uint32_t ldc) {
-    const uint64_t idx = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * V;
-    const uint64_t total = (uint64_t)rows * S.ntotal;
-    if (idx >= total) return;
-    const uint32_t m = (uint32_t)(idx / S.ntotal), col = (uint32_t)(idx % S.ntotal);
-    // all loads of a batch of 8 splits are issued before the first add, so
-    // the memory latency is paid once per batch, not once per split
-    typedef float fv __attribute__((ext_vector_type(V)));
-    fv acc = {};
+// Sum the split-K partial tiles in split order (deterministic), scale (per-row
+// kind), round to bf16.  One workgroup per (column tile, wave block
+// (wm, mt, wn)): thread (nt, lane) adds the splits' f32x4 at its place of the
+// partial layout (up to 8 loads in flight) and writes rows 4g..4g+3 of column
+// r16 of block nt.
+template <int KIND, int MTW>
+__global__ __launch_bounds__(256) void w8a8_reduce(const f32x4 *__restrict__ partials, uint32_t splits,
+                                                   const float *__restrict__ sa, uint32_t rows, Segs S,
+                                                   uint16_t *__restrict__ out, uint32_t ldc) {
+    constexpr int UNITS = 4 * MTW * 2;
+    const uint32_t tile = blockIdx.x / UNITS, u = blockIdx.x % UNITS;
+    const int wm = u / (MTW * 2), mt = (u / 2) % MTW, wn = u % 2;
+    const int nt = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const size_t per_split = (size_t)UNITS * 4 * kWave;
+    const f32x4 *p = partials + (size_t)tile * splits * per_split + ((size_t)u * 4 + nt) * kWave + lane;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (uint32_t s0 = 0; s0 < splits; s0 += 8) {
-        fv t[8];
+        f32x4 t[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (s0 + u < splits)
-                t[u] = __builtin_nontemporal_load(reinterpret_cast<const fv *>(partials + (size_t)(s0 + u) * total + idx));
+        for (int q = 0; q < 8; ++q)
+            if (s0 + q < splits) t[q] = __builtin_nontemporal_load(p + (size_t)(s0 + q) * per_split);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (s0 + u < splits) acc += t[u];
+        for (int q = 0; q < 8; ++q)
+            if (s0 + q < splits) v += t[q];
     }
-    float v[V];
+    const uint32_t col = tile * kWideN + wn * 64 + nt * 16 + r16;
+    if (col >= S.ntotal) return;
+    const int sg = seg_of(S, col);
+    const uint32_t jl = col - S.start[sg];
+    if (jl >= S.n[sg]) return;
+    const float sw = KIND == 0 ? S.s[sg][jl] : 1.0f;
 #pragma unroll
-    for (int e = 0; e < V; ++e) v[e] = acc[e];
-    if (KIND == 0) {
-        const int sg = seg_of(S, col);
-        const float *sw = S.s[sg] + (col - S.start[sg]);
-#pragma unroll
-        for (int e = 0; e < V; ++e) v[e] = v[e] * sa[m] * sw[e];
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t m = wm * 16 * MTW + mt * 16 + 4 * g + e;
+        if (m < rows) out[(size_t)m * ldc + col] = bf16_rne(KIND == 0 ? v[e] * sa[m] * sw : v[e]);
     }
-    uint16_t *o = out + (size_t)m * ldc + col;
-#pragma unroll
-    for (int e = 0; e < V; ++e) o[e] = bf16_rne(v[e]);
 }
 
 // --------------------------------------------------------------- host ---
@@ -964,7 +968,8 @@ WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
     if (sp < 1) sp = 1;
     p.splits = sp;
     p.counter_bytes = sp > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;   // partials go behind the counters
-    p.ws_bytes = sp > 1 ? p.counter_bytes + (size_t)sp * rows * ntotal * sizeof(float) : 0;
+    // partial tiles: per (column tile, split) 4 x MTW x 2 x 4 blocks of 64 f32x4
+    p.ws_bytes = sp > 1 ? p.counter_bytes + (size_t)p.ntiles * sp * (4 * p.mtw * 2 * 4 * kWave) * 16 : 0;
     return p;
 }
 
@@ -1011,16 +1016,20 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
 #undef KVQ_WIDE
     int st = launch_status("w8a8_gemv");
     if (st || pl.splits == 1) return st;
-    const uint64_t total = (uint64_t)rows * S.ntotal;
-    if (S.ntotal % 4 == 0) {
-        const unsigned rgrid = (unsigned)((total / 4 + kBlock - 1) / kBlock);
-        if (kind == W8A8_ROWSCALE) w8a8_reduce<0, 4><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
-        else w8a8_reduce<1, 4><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
-    } else {
-        const unsigned rgrid = (unsigned)((total + kBlock - 1) / kBlock);
-        if (kind == W8A8_ROWSCALE) w8a8_reduce<0, 1><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
-        else w8a8_reduce<1, 1><<<rgrid, kBlock, 0, s>>>(partials, pl.splits, a_scales, rows, S, out, ldc);
+    const unsigned rgrid = pl.ntiles * (4 * pl.mtw * 2);
+    const f32x4 *pt = reinterpret_cast<const f32x4 *>(partials);
+#define KVQ_RED(MTW)                                                                                          \
+    do {                                                                                                      \
+        if (kind == W8A8_ROWSCALE) w8a8_reduce<0, MTW><<<rgrid, 256, 0, s>>>(pt, pl.splits, a_scales, rows, S, out, ldc); \
+        else w8a8_reduce<1, MTW><<<rgrid, 256, 0, s>>>(pt, pl.splits, a_scales, rows, S, out, ldc);           \
+    } while (0)
+    switch (pl.mtw) {
+        case 1: KVQ_RED(1); break;
+        case 2: KVQ_RED(2); break;
+        case 3: KVQ_RED(3); break;
+        default: KVQ_RED(4); break;
     }
+#undef KVQ_RED
     return launch_status("w8a8_gemv (split-K reduction)");
 }
 
