@@ -61,12 +61,6 @@ struct Projs {
 };
 
 
-// Cache-policy operand of the buffer intrinsics: sc1 makes a load or store
-// coherent at agent scope (the encoding an agent-scope relaxed atomic load or
-// store uses on this family), which the partial tiles exchanged between
-// workgroups on different XCDs (whose L2s are not coherent) need.
-constexpr int kAuxSc1 = 16;
-
 // 8 words (K rows 0..7 of one word column) -> 8 B operands; operand c holds
 // column c's codes (as fp16 subnormals, scaled 2^-24 or 2^-20) for rows 0..7,
 // row 2i in the low half of register i.

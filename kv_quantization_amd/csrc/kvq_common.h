@@ -130,6 +130,12 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 family
 constexpr uint32_t kOffNone = 0x80000000u;     // a lane offset past every resource used here (sizes < 2 GiB)
 
+// Cache-policy operand of the buffer intrinsics: sc1 makes a load or store
+// coherent at agent scope (the encoding an agent-scope relaxed atomic load or
+// store uses on this family), which partial tiles exchanged between
+// workgroups on different XCDs (whose L2s are not coherent) need.
+constexpr int kAuxSc1 = 16;
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
