@@ -525,14 +525,16 @@ void fused_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t
 // scales and writes bf16.
 
 constexpr int kWideN = 128;
-constexpr int kWideWaves = 8;                              // waves that multiply
+constexpr int kWideWM = 4;                                 // multiplying waves along rows (x 2 along columns)
+constexpr int kWideWaves = 2 * kWideWM;                    // waves that multiply
+constexpr int kWideMaxMTW = 256 / (16 * kWideWM);         // 16-row tiles per wave at 256 rows
 constexpr int kWideLoaders = 4;                            // waves that only load (2 per stream)
 constexpr int kWideThreads = (kWideWaves + kWideLoaders) * kWave;
 
 
 template <int MTW, int KIND>
 struct WideCfg {
-    static constexpr int WM = 4;                         // multiplying waves along rows
+    static constexpr int WM = kWideWM;                   // multiplying waves along rows
     static constexpr int BM = 16 * MTW * WM;             // rows per workgroup
     static constexpr int A_BYTES = BM * 128;
     static constexpr int B_BYTES = kWideN * 128;
@@ -555,7 +557,7 @@ struct WideCfg {
     // weight ring takes what LDS is left.  The double-buffered scale chunks
     // are refilled 8 K blocks apart, so SA <= 5.
     static constexpr int SA = 3;
-    static constexpr int LDS_MAX = 160 * 1024 - 2 * ((4 * 16 * WM + 1) * 16) - 1024;
+    static constexpr int LDS_MAX = 160 * 1024 - 2 * SC_BYTES - 1024;
     static constexpr int SB_FIT = (LDS_MAX - SA * A_BYTES) / B_BYTES;
     static constexpr int SB = SB_FIT > 8 ? 8 : SB_FIT;
     static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SA_ROWS % 8 == 0, "tile shape");
@@ -836,12 +838,12 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
     // 4g..4g+3), so every wave writes whole 1 KiB blocks with 16-byte stores.
     // Rows past `rows` and columns past the weights hold zero sums.
     if (splits > 1) {
-        f32x4 *part = reinterpret_cast<f32x4 *>(partials) + (size_t)blockIdx.x * (4 * MTW * 2 * 4 * kWave);
+        f32x4 *part = reinterpret_cast<f32x4 *>(partials) + (size_t)blockIdx.x * (kWideWM * MTW * 2 * 4 * kWave);
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
-                __builtin_nontemporal_store(acc[mt][nt], part + (((wm * MTW + mt) * 2 + wn) * 4 + nt) * kWave + lane);
+                part[(((wm * MTW + mt) * 2 + wn) * 4 + nt) * kWave + lane] = acc[mt][nt];
         return;
     }
 #pragma unroll
@@ -874,7 +876,7 @@ template <int KIND, int MTW>
 __global__ __launch_bounds__(256) void w8a8_reduce(const f32x4 *__restrict__ partials, uint32_t splits,
                                                    const float *__restrict__ sa, uint32_t rows, Segs S,
                                                    uint16_t *__restrict__ out, uint32_t ldc) {
-    constexpr int UNITS = 4 * MTW * 2;
+    constexpr int UNITS = kWideWM * MTW * 2;
     const uint32_t tile = blockIdx.x / UNITS, u = blockIdx.x % UNITS;
     const int wm = u / (MTW * 2), mt = (u / 2) % MTW, wn = u % 2;
     const int nt = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -960,7 +962,7 @@ struct WidePlan {
 // ~256 workgroups.
 WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
     WidePlan p;
-    p.mtw = (rows + 63) / 64;
+    p.mtw = (rows + 16 * kWideWM - 1) / (16 * kWideWM);
     p.ntiles = (ntotal + kWideN - 1) / kWideN;
     const uint32_t nkb = k / 128;
     uint32_t sp = 256 / (p.ntiles ? p.ntiles : 1);
@@ -969,7 +971,7 @@ WidePlan wide_plan(uint32_t rows, uint32_t k, uint32_t ntotal) {
     p.splits = sp;
     p.counter_bytes = sp > 1 ? KVQ_WORKSPACE_COUNTER_BYTES : 0;   // partials go behind the counters
     // partial tiles: per (column tile, split) 4 x MTW x 2 x 4 blocks of 64 f32x4
-    p.ws_bytes = sp > 1 ? p.counter_bytes + (size_t)p.ntiles * sp * (4 * p.mtw * 2 * 4 * kWave) * 16 : 0;
+    p.ws_bytes = sp > 1 ? p.counter_bytes + (size_t)p.ntiles * sp * (kWideWM * p.mtw * 2 * 4 * kWave) * 16 : 0;
     return p;
 }
 
@@ -1010,13 +1012,23 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
         case 1: KVQ_WIDE(1); break;
         case 2: KVQ_WIDE(2); break;
         case 3: KVQ_WIDE(3); break;
-        default: KVQ_WIDE(4); break;
+        case 4: KVQ_WIDE(4); break;
+        default:
+            if constexpr (kWideMaxMTW > 4) {
+                switch (pl.mtw) {
+                    case 5: KVQ_WIDE(5 < kWideMaxMTW ? 5 : kWideMaxMTW); break;
+                    case 6: KVQ_WIDE(6 < kWideMaxMTW ? 6 : kWideMaxMTW); break;
+                    case 7: KVQ_WIDE(7 < kWideMaxMTW ? 7 : kWideMaxMTW); break;
+                    default: KVQ_WIDE(kWideMaxMTW); break;
+                }
+            }
+            break;
     }
 #undef KVQ_WIDE3
 #undef KVQ_WIDE
     int st = launch_status("w8a8_gemv");
     if (st || pl.splits == 1) return st;
-    const unsigned rgrid = pl.ntiles * (4 * pl.mtw * 2);
+    const unsigned rgrid = pl.ntiles * (kWideWM * pl.mtw * 2);
     const f32x4 *pt = reinterpret_cast<const f32x4 *>(partials);
 #define KVQ_RED(MTW)                                                                                          \
     do {                                                                                                      \
@@ -1027,7 +1039,17 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
         case 1: KVQ_RED(1); break;
         case 2: KVQ_RED(2); break;
         case 3: KVQ_RED(3); break;
-        default: KVQ_RED(4); break;
+        case 4: KVQ_RED(4); break;
+        default:
+            if constexpr (kWideMaxMTW > 4) {
+                switch (pl.mtw) {
+                    case 5: KVQ_RED(5 < kWideMaxMTW ? 5 : kWideMaxMTW); break;
+                    case 6: KVQ_RED(6 < kWideMaxMTW ? 6 : kWideMaxMTW); break;
+                    case 7: KVQ_RED(7 < kWideMaxMTW ? 7 : kWideMaxMTW); break;
+                    default: KVQ_RED(kWideMaxMTW); break;
+                }
+            }
+            break;
     }
 #undef KVQ_RED
     return launch_status("w8a8_gemv (split-K reduction)");
