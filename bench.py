@@ -422,11 +422,11 @@ def time_cold(torch, api, fn, args, stream, reps):
 # <kernel>`, each scaled by what the counter reads for a 256 MiB device copy.
 # Reported only while every listed source (comments aside) is the one the
 # counters were taken on.
-TRAFFIC = {"w8a8_gemm_blk128_M256": {"bytes": 132675584,
+TRAFFIC = {"w8a8_gemm_blk128_M256": {"bytes": 132179968,
                                      "sources": {"kv_quantization_amd/csrc/w8a8_gemm.hip":
-                                                 "c1135df59efd6f675cb71d927b830d0740e008e6f923bb2561fb4aed01a248c0",
+                                                 "dce8b89fd9858ac181629c32581b575c8b46704cb14ae70b6328be24ca8c876c",
                                                  "kv_quantization_amd/csrc/kvq_common.h":
-                                                 "b77ff8ec048dd95b28a74a8fac2ed8f89bd33c35a443965ca2a10f3f39a07c55"}}}
+                                                 "4ad11bdaedb2d5c50e052267b1590dd88196791033af9859d0d0771553b9b7e7"}}}
 
 
 def code_digest(path):
