@@ -178,38 +178,53 @@ __global__ __launch_bounds__(256) void x_pow2_f16(const void *__restrict__ x, ui
     const uint32_t m = blockIdx.x;
     const uint32_t n8 = K / 8;
     const rsrc_t rx = make_rsrc(static_cast<const uint8_t *>(x) + (size_t)m * K * XB, K * XB);
-    auto load8 = [&](uint32_t i, float v[8]) {
+    // 8 values from the 16 or 32 bytes at 8-value chunk i (an offset past the
+    // row reads zeros)
+    auto raw8 = [&](uint32_t i, u32x4 r[2]) {
+        const uint32_t off = i < n8 ? i * 8 * XB : kOffNone;
+        r[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+        r[1] = XT == 0 ? __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0) : r[0];
+    };
+    auto unpack8 = [&](const u32x4 r[2], float v[8]) {
         if (XT == 0) {
-            const f32x4 a = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rx, i * 32, 0, 0));
-            const f32x4 b = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rx, i * 32 + 16, 0, 0));
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        } else {
-            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rx, i * 16, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[2 * j] = __uint_as_float(h[j] << 16);
-                v[2 * j + 1] = __uint_as_float(h[j] & 0xFFFF0000u);
+            for (int q = 0; q < 4; ++q) {
+                v[q] = __uint_as_float(r[0][q]);
+                v[4 + q] = __uint_as_float(r[1][q]);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[2 * q] = __uint_as_float(r[0][q] << 16);
+                v[2 * q + 1] = __uint_as_float(r[0][q] & 0xFFFF0000u);
             }
         }
     };
+    auto load8 = [&](uint32_t i, float v[8]) {
+        u32x4 r[2];
+        raw8(i, r);
+        unpack8(r, v);
+    };
     // absmax over the row (non-negative floats, inf and NaN included, order
     // as their bits); rows up to 8192 values stay in registers for the
-    // conversion, longer ones are read again (from L2)
+    // conversion (every load issued before the first use, no branch around
+    // them), longer ones are read again (from L2)
     constexpr int NR = 4;   // 8-value chunks per thread kept in registers
     const bool held = n8 <= NR * 256;
     float v[NR][8];
     int amax = 0;
     if (held) {
+        u32x4 r[NR][2];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) raw8(threadIdx.x + 256 * j, r[j]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            const uint32_t i = threadIdx.x + 256 * j;
-            if (i < n8) {
-                load8(i, v[j]);
+            unpack8(r[j], v[j]);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int b = __float_as_int(v[j][q]) & 0x7FFFFFFF;
-                    amax = b > amax ? b : amax;
-                }
+            for (int q = 0; q < 8; ++q) {
+                const int b = __float_as_int(v[j][q]) & 0x7FFFFFFF;
+                amax = b > amax ? b : amax;
             }
         }
     } else {

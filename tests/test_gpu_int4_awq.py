@@ -108,6 +108,35 @@ def test_no_k_split_workspace_holds_the_scaled_copy(m, k, ns):
     _check(x, projs, 128, _run(x, projs, 128, use_workspace=False), f"in-kernel rounding m={m}")
 
 
+@pytest.mark.parametrize("m,k,ns,gs", [
+    (64, 4096, (512,), 128),              # 4 tiles x 2 row chunks: K slices over the waves and workgroups
+    (100, 2048, (1152, 128, 128), 64),    # 11 tiles (a pair across projections), 4 ragged row chunks
+    (300, 1024, (512, 256, 256), 32),     # 10 row chunks, 32-row groups
+    (129, 1536, (2048, 512, 512), 256),   # 5 row chunks (the last one row), 6 groups
+    (64, 512, (16384,), 128),             # 128 tiles
+    (96, 1088, (256, 64, 64), 32),        # 34 groups of 32 (odd)
+    (80, 544, (256, 64, 64), 32),         # 17 groups of 32
+])
+def test_matrix_core_more_shapes(m, k, ns, gs):
+    """The matrix-core ring on ragged shapes: parity with and without a
+    workspace, the same bits on a second call, and fp16 / bf16 activations
+    bit-identical to the fp32 call on their values."""
+    print_case("int4 matrix-core shapes", m, k, ns, gs)
+    x, projs = synth.int4_awq(m, k, ns, gs, seed=3100 + m + gs)
+    a = _run(x, projs, gs)
+    _check(x, projs, gs, a, f"m={m} k={k} gs={gs}")
+    for u, v in zip(a, _run(x, projs, gs)):
+        np.testing.assert_array_equal(u.view(np.uint32), v.view(np.uint32))
+    _check(x, projs, gs, _run(x, projs, gs, use_workspace=False), f"nows m={m} k={k} gs={gs}")
+    for dt in (1, 2):
+        xb = _oracle.narrow16(x, dt)
+        xw = _oracle.widen16(xb, dt)
+        got16 = _run16(xb, dt, projs, gs)
+        _check(xw, projs, gs, got16, f"dt={dt} m={m}")
+        for u, v in zip(got16, _run(xw, projs, gs)):
+            np.testing.assert_array_equal(u.view(np.uint32), v.view(np.uint32))
+
+
 @pytest.mark.parametrize("m", [16, 40, 128])
 @pytest.mark.parametrize("kind", ["tiny", "huge", "mixed"])
 def test_matrix_core_activation_range(m, kind):
