@@ -256,7 +256,7 @@ void skinny_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, u
 // loads, so the in-order load counter lets the encoding run while the weights
 // are still in flight.  Per-row scales need the whole row's absmax, i.e. a
 // workgroup barrier after every wave has its part; the host keeps per-row
-// calls to one chunk per wave (K <= 4 * U * 128), where that barrier sits
+// calls to one chunk per wave (K <= W * U * 128), where that barrier sits
 // between the first loads and the first MFMAs.  Block scales are local to
 // one 128-column group (a 16-lane team) and any K works.
 constexpr uint32_t kFusedRows = 8;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
     __shared__ __attribute__((aligned(16))) uint8_t lq[W][R][RS];
     __shared__ float lgs[W][R][U];
     __shared__ float lamax[W][R];
-    __shared__ float ls[R];
+    __shared__ float ls[R], ly[R];
     __shared__ f32x4 red[W][NT][kWave];
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
@@ -371,6 +371,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
             for (int w = 1; w < W; ++w) am = fmaxf(am, lamax[w][threadIdx.x]);
             const float s = act_scale(am);
             ls[threadIdx.x] = s;
+            ly[threadIdx.x] = 1.0f / s;
             if (writer && threadIdx.x < rows) saout[threadIdx.x] = s;
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -384,6 +385,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
         for (int m = 0; m < R; ++m) {
             if ((uint32_t)m >= rows) break;
             const float srow = KIND == 0 ? ls[m] : 0.0f;
+            const float yrow = KIND == 0 ? ly[m] : 0.0f;
 #pragma unroll
             for (int j = 0; j < XJ; ++j) {
                 const uint32_t blk = 4 * j + g;
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
                 float v[8];
                 act8<SILU, UP>(xw[m][j], xu[m][j], v);
                 const float s = KIND == 0 ? srow : act_scale(team_absmax<16>(absmax8(v)));
-                const float y = 1.0f / s;
+                const float y = KIND == 0 ? yrow : 1.0f / s;
                 const u32x2 c = encode8(v, s, y);
                 if (ok) {
                     *reinterpret_cast<u32x2 *>(&lq[wv][m][blk * 128 + r16 * 8]) = c;
