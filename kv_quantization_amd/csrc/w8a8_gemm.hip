@@ -125,7 +125,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_skinny(const uint8_t *__restri
                                                           Segs S, uint16_t *__restrict__ out, uint32_t ldc) {
     __shared__ f32x4 red[W][MT * NT][kWave];
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, g = lane >> 4;
     const uint32_t nkb = K / 128;
     const uint32_t kb0 = wv * nkb / W, kb1 = (wv + 1) * nkb / W;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(W * kWave) void w8a8_fused(
     __shared__ float ls[R], ly[R];
     __shared__ f32x4 red[W][NT][kWave];
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, g = lane >> 4;
     const uint32_t nkb = K / 128;
     const uint32_t kb0 = wv * nkb / W, kb1 = (wv + 1) * nkb / W;
