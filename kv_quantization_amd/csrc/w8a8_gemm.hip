@@ -511,8 +511,9 @@ void fused_launch(w8a8_scale_t kind, int silu, const uint16_t *x, const uint16_t
 // instructions, and 4 loader waves: two stream the activation tile (and its
 // block scales), two the weight tile, each into its own LDS ring with direct
 // DMA loads (lane i's 16 bytes land at LDS base + 16*i).  The activation ring
-// has 3 stages (its tiles come from L2), the weight ring what LDS leaves, up
-// to 8 (its tiles come from HBM with the longer latency).  A loader waits for
+// has 3-4 stages (its tiles come from L2), the weight ring what LDS leaves,
+// up to a cap of 4-8 by tile size (its tiles come from HBM with the longer
+// latency, but more weight loads in flight slow the CU's L2 hits).  A loader waits for
 // its own loads of the next K step (vmcnt), then every wave meets at one
 // barrier per K step; a multiplying wave reads the next activation fragment
 // before the matrix instructions of the current one.  Rows are stored with
@@ -556,12 +557,17 @@ struct WideCfg {
     static constexpr int SC_BYTES = (BM + 1) * 16;                // one chunk: [BM rows + sw][4 K blocks]
     // Ring depths: the activation tiles come from L2 (every column tile
     // reads them), the weight tiles from HBM with its longer latency; the
-    // weight ring takes what LDS is left.  The double-buffered scale chunks
-    // are refilled 8 K blocks apart, so SA <= 5.
-    static constexpr int SA = 3;
+    // weight ring takes what LDS is left, up to a cap.  Weight loads in
+    // flight beyond what keeps the CU's share of HBM busy only slow the
+    // activation loads (L2 hits) of the same CU, so the small tiles keep
+    // fewer weight stages and more activation stages (measured per tile
+    // size).  The double-buffered scale chunks are refilled 8 K blocks
+    // apart, so SA <= 5.
+    static constexpr int SA = MTW <= 2 ? 4 : 3;
+    static constexpr int SB_CAP = MTW == 1 ? 4 : (MTW == 2 ? 6 : 8);
     static constexpr int LDS_MAX = 160 * 1024 - 2 * SC_BYTES - 1024;
     static constexpr int SB_FIT = (LDS_MAX - SA * A_BYTES) / B_BYTES;
-    static constexpr int SB = SB_FIT > 8 ? 8 : SB_FIT;
+    static constexpr int SB = SB_FIT > SB_CAP ? SB_CAP : SB_FIT;
     static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SA_ROWS % 8 == 0, "tile shape");
     static_assert(SB >= 3 && SA <= 5, "ring depths");
     static_assert((SB - 2) * B_INSTR + 15 < 64 && (SA - 2) * (A_INSTR + SC_INSTR + 1) + 15 < 64, "vmcnt range");
