@@ -1006,8 +1006,8 @@ uint32_t ring_kb(uint32_t mt, uint32_t gs, int xt) { return (gs >= 64 && !(mt ==
 
 // 16 rows per wave up to 16 rows, else 32-row chunks; 64-row stages except
 // where the group is 32 rows or two fp32 row tiles would not fit the ring;
-// K slices (a power of two, whole groups per wave) until ~one workgroup per
-// CU.  fp32 and bf16 rows are scaled by powers of two into fp16: inside
+// K slices (a power of two, whole groups per wave, then one more if K is
+// split and it fits) until ~one workgroup per CU.  fp32 and bf16 rows are scaled by powers of two into fp16: inside
 // each wave when its whole K range fits its ring, else by the pre-pass into
 // the workspace (then the product reads fp16).
 RingPlan ring_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles, int xt) {
@@ -1019,6 +1019,10 @@ RingPlan ring_plan(uint32_t m, uint32_t k, uint32_t gs, uint32_t ntiles, int xt)
     const uint32_t ngroups = k / gs;
     pl.ks_b = 1;
     while (units * pl.ks_b * 2 <= kRingTargetWgs && (uint64_t)pl.ks_b * 2 * kRingWaves <= ngroups) pl.ks_b *= 2;
+    // when K is split already, one more slice if it still fits one workgroup
+    // per CU: a CU streams only its share of HBM, so more busy CUs move the
+    // weights sooner (some waves may then hold no group and add zeros)
+    if (pl.ks_b > 1 && units * (pl.ks_b + 1) <= kRingTargetWgs && pl.ks_b + 1 <= ngroups) pl.ks_b += 1;
     const size_t tiles = (size_t)ntiles * pl.nchunks;
     if (tiles * 4 > KVQ_WORKSPACE_COUNTER_BYTES) pl.ks_b = 1;   // more tiles than counters: no exchange
     pl.kb = ring_kb(pl.mt, gs, xt);

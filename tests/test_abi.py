@@ -156,10 +156,11 @@ def test_workspace_sizes(lib):
     # scales, each rounded up to 256 bytes
     counters = 4096
     r256 = lambda v: (v + 255) // 256 * 256
-    # 16 rows x 6144 columns: 4 K slices of 16 x 128 fp32 tiles; one group
-    # per wave, scaled inside the wave
+    # 16 rows x 6144 columns: 5 K slices (4, then one more while 48-50 tiles
+    # x 5 stay within 256 workgroups) of 16 x 128 fp32 tiles; at most one
+    # group per wave, scaled inside the wave
     assert lib.int4_awq_workspace_bytes(16, 4096, 128, 6144, ctypes.byref(b)) == 0
-    assert b.value == counters + (6144 // 128 + 2) * 4 * 16 * 128 * 4
+    assert b.value == counters + (6144 // 128 + 2) * 5 * 16 * 128 * 4
     # 128 rows x 6144 columns: K is not split, 4 groups per wave: the copy
     assert lib.int4_awq_workspace_bytes(128, 4096, 128, 6144, ctypes.byref(b)) == 0
     assert b.value == counters + 128 * 4096 * 2 + 512
