@@ -41,6 +41,7 @@
 #include "kvq_common.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace kvq {
 namespace {
@@ -535,19 +536,31 @@ __global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ 
         // the slot's reads are done: refill it while this stage is multiplied
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (b + R < nst) issue(b + R);
+        // A group's first K step starts its sums from a zero accumulator, so
+        // its epilogue need not clear them (~70 vector instructions per group
+        // at 32 rows).  bf16 input keeps the clearing: its extra widening
+        // leaves no registers for the second copy of this step.
+        constexpr bool kZeroStart = XT != 2;
+        auto multiply = [&](auto fresh) {
 #pragma unroll
-        for (int s = 0; s < C::SUB; ++s) {
-            f16x8 B[8];
-            awq_operands(w[s], B);
+            for (int s = 0; s < C::SUB; ++s) {
+                f16x8 B[8];
+                awq_operands(w[s], B);
+                const bool z = decltype(fresh)::value && s == 0;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const f16x8 a = (XT != 1 && inscale) ? act_f16x8_scaled<XT>(xv[s][mt][0], xv[s][mt][1], erow[mt])
-                                                     : act_f16x8<XT>(xv[s][mt][0], xv[s][mt][1]);
-                xg[mt] = mfma16(a, ones, xg[mt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const f16x8 a = (XT != 1 && inscale)
+                                        ? act_f16x8_scaled<XT>(xv[s][mt][0], xv[s][mt][1], erow[mt])
+                                        : act_f16x8<XT>(xv[s][mt][0], xv[s][mt][1]);
+                    xg[mt] = mfma16(a, ones, z ? f32x4{0.f, 0.f, 0.f, 0.f} : xg[mt]);
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) pg[mt][cc] = mfma16(a, B[cc], pg[mt][cc]);
+                    for (int cc = 0; cc < 8; ++cc)
+                        pg[mt][cc] = mfma16(a, B[cc], z ? f32x4{0.f, 0.f, 0.f, 0.f} : pg[mt][cc]);
+                }
             }
-        }
+        };
+        if (kZeroStart && (uint32_t)b % spg == 0) multiply(std::true_type{});
+        else multiply(std::false_type{});
         if (gend) {
             // columns 0,1,4,5 were unpacked as q*2^-24, columns 2,3,6,7 as q*2^-20
             const float f[8] = {0x1p24f, 0x1p24f, 0x1p20f, 0x1p20f, 0x1p24f, 0x1p24f, 0x1p20f, 0x1p20f};
@@ -563,9 +576,9 @@ __global__ __launch_bounds__(WV * kWave) void awq_ring(const void *__restrict__ 
                     for (int i = 0; i < 4; ++i)
                         acc[mt][cc][i] = __builtin_fmaf(sv[cc], __builtin_fmaf(-zv[cc], xg[mt][i], pg[mt][cc][i]),
                                                         acc[mt][cc][i]);
-                    pg[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (!kZeroStart) pg[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                xg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (!kZeroStart) xg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
     }
