@@ -535,7 +535,7 @@ constexpr int kWideLoaders = 4;                            // waves that only lo
 constexpr int kWideThreads = (kWideWaves + kWideLoaders) * kWave;
 
 
-template <int MTW, int KIND>
+template <int MTW, int KIND, bool SX4>
 struct WideCfg {
     static constexpr int WM = kWideWM;                   // multiplying waves along rows
     static constexpr int BM = 16 * MTW * WM;             // rows per workgroup
@@ -553,7 +553,11 @@ struct WideCfg {
     static constexpr int A_INSTR = A_BYTES / 1024 / LW;           // 1 KiB loads per A loader per stage
     static constexpr int B_INSTR = B_BYTES / 1024 / LW;           // per B loader per stage
     static constexpr int SA_ROWS = BM / LW;                       // activation-scale rows per A loader
-    static constexpr int SC_INSTR = (SA_ROWS * 4 + 63) / 64;      // dword loads per A loader per chunk
+    // scale loads per A loader per chunk: SX4 one 16-byte load per row (a
+    // row's 4 scales), else one 4-byte load per scale.  The vector L1 takes
+    // a direct-to-LDS instruction at a time per wave whatever its width, so
+    // the 16-byte form issues a quarter of the instructions.
+    static constexpr int SC_INSTR = SX4 ? (SA_ROWS + 63) / 64 : (SA_ROWS * 4 + 63) / 64;
     static constexpr int SC_BYTES = (BM + 1) * 16;                // one chunk: [BM rows + sw][4 K blocks]
     // Ring depths: the activation tiles come from L2 (every column tile
     // reads them), the weight tiles from HBM with its longer latency; the
@@ -621,12 +625,12 @@ __device__ __forceinline__ void wait_stages(int later, uint32_t extra) {
 }
 
 
-template <int MTW, int KIND, bool UNI>
+template <int MTW, int KIND, bool UNI, bool SX4>
 __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restrict__ q, const float *__restrict__ sa,
                                                           uint32_t rows, uint32_t K, Segs S,
                                                           uint16_t *__restrict__ out, uint32_t ldc, uint32_t splits,
                                                           uint32_t ntiles, float *__restrict__ partials) {
-    using C = WideCfg<MTW, KIND>;
+    using C = WideCfg<MTW, KIND, SX4>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a[C::SA * C::A_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b[C::SB * C::B_BYTES];
     // block scales (KIND 1), double-buffered in chunks of 4 K blocks
@@ -691,7 +695,8 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
             uint32_t scoff[C::SC_INSTR];
 #pragma unroll
             for (int j = 0; j < C::SC_INSTR; ++j)
-                scoff[j] = ((lw * C::SA_ROWS + 16 * j + (lane >> 2)) * nkb + (lane & 3)) * 4;
+                scoff[j] = SX4 ? (lw * C::SA_ROWS + 64 * j + lane) * nkb * 4
+                               : ((lw * C::SA_ROWS + 16 * j + (lane >> 2)) * nkb + (lane & 3)) * 4;
             auto issue_a = [&](int it) {
                 const uint32_t kb = kb0 + it;
                 const uint32_t abase = a0 + (uint32_t)(it % C::SA) * C::A_BYTES;
@@ -706,8 +711,15 @@ __global__ __launch_bounds__(kWideThreads) void w8a8_wide(const uint8_t *__restr
                     const uint32_t slot = sc0 + ((kb >> 2) & 1) * C::SC_BYTES;
 #pragma unroll
                     for (int j = 0; j < C::SC_INSTR; ++j) {
-                        const uint32_t dst = slot + (lw * C::SA_ROWS + 16 * j) * 16;
-                        if (16 * j + (lane >> 2) < C::SA_ROWS) lds_buf4(rsa, scoff[j] + c4, 0, dst);
+                        if (SX4) {
+                            // lane i: row lw*SA_ROWS + 64j + i, its 4 scales
+                            // (16-byte aligned: nkb is a multiple of 4)
+                            const uint32_t dst = slot + (lw * C::SA_ROWS + 64 * j) * 16;
+                            if (64 * j + lane < C::SA_ROWS) lds_buf16(rsa, scoff[j] + c4, 0, dst);
+                        } else {
+                            const uint32_t dst = slot + (lw * C::SA_ROWS + 16 * j) * 16;
+                            if (16 * j + (lane >> 2) < C::SA_ROWS) lds_buf4(rsa, scoff[j] + c4, 0, dst);
+                        }
                     }
                     if (lw == 0 && lane < 4) lds_buf4(rsw, lane * 4 + c4, 0, slot + C::BM * 16);
                 }
@@ -1007,14 +1019,17 @@ int gemv_launch(w8a8_scale_t kind, const uint8_t *q, const float *a_scales, uint
     // tiles never straddle segments when every non-last segment is a multiple of 128 rows
     bool uni = true;
     for (uint32_t i = 0; i + 1 < S.count; ++i) uni = uni && (S.n[i] % kWideN == 0);
-#define KVQ_WIDE3(MTW, KIND, UNI) \
-    w8a8_wide<MTW, KIND, UNI><<<grid, kWideThreads, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, pl.ntiles, \
-                                                             partials)
-#define KVQ_WIDE(MTW)                                        \
-    do {                                                     \
-        if (kind == W8A8_BLK128) KVQ_WIDE3(MTW, 1, true);    \
-        else if (uni) KVQ_WIDE3(MTW, 0, true);               \
-        else KVQ_WIDE3(MTW, 0, false);                       \
+    // block-scale rows start 16-byte aligned when K is a multiple of 512
+    const bool sx4 = (k / 128) % 4 == 0;
+#define KVQ_WIDE3(MTW, KIND, UNI, SX4) \
+    w8a8_wide<MTW, KIND, UNI, SX4><<<grid, kWideThreads, 0, s>>>(q, a_scales, rows, k, S, out, ldc, pl.splits, \
+                                                                  pl.ntiles, partials)
+#define KVQ_WIDE(MTW)                                                  \
+    do {                                                               \
+        if (kind == W8A8_BLK128 && sx4) KVQ_WIDE3(MTW, 1, true, true); \
+        else if (kind == W8A8_BLK128) KVQ_WIDE3(MTW, 1, true, false);  \
+        else if (uni) KVQ_WIDE3(MTW, 0, true, false);                  \
+        else KVQ_WIDE3(MTW, 0, false, false);                          \
     } while (0)
     switch (pl.mtw) {
         case 1: KVQ_WIDE(1); break;
