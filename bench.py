@@ -422,9 +422,9 @@ def time_cold(torch, api, fn, args, stream, reps):
 # <kernel>`, each scaled by what the counter reads for a 256 MiB device copy.
 # Reported only while every listed source (comments aside) is the one the
 # counters were taken on.
-TRAFFIC = {"w8a8_gemm_blk128_M256": {"bytes": 132171776,
+TRAFFIC = {"w8a8_gemm_blk128_M256": {"bytes": 132180992,
                                      "sources": {"kv_quantization_amd/csrc/w8a8_gemm.hip":
-                                                 "f36c6e94b1038d89f611e5e869b6e20255862e54afe21da9885d4ebeb0d0a2f2",
+                                                 "0a0fb83138f1e11b3b03832563bb86a9ca57b485cb0647bc9bbc85b38a780405",
                                                  "kv_quantization_amd/csrc/kvq_common.h":
                                                  "4ad11bdaedb2d5c50e052267b1590dd88196791033af9859d0d0771553b9b7e7"}}}
 
