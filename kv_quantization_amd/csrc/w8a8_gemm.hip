@@ -8,14 +8,18 @@
 // threads over <=128-row chunks, re-streaming the weights per chunk.  Here
 // every call is one launch over all (<=256) rows:
 //
-//   * rows <= 32  "skinny": a workgroup owns 16 output columns; its 4 waves
-//     split K, each streaming 16 weight rows with 16-byte loads straight into
-//     MFMA operands (v_mfma_scale_f32_16x16x128_f8f6f4, unit E8M0 scales, so
-//     one instruction is one 128-wide scale block) and the activation rows
-//     as the other operand; partial sums meet in LDS.
+//   * rows <= 32  "skinny": a workgroup owns a few 16-column tiles (a pair of
+//     workgroups shares three, so 6144 columns make 256 equal workgroups);
+//     its waves split K, each streaming 16 weight rows per tile with 16-byte
+//     loads straight into MFMA operands (v_mfma_scale_f32_16x16x128_f8f6f4,
+//     unit E8M0 scales, so one instruction is one 128-wide scale block) and
+//     the activation rows as the other operand; partial sums meet in LDS.
+//     Up to 8 rows the same kernel can quantize the bf16 activations itself
+//     (the single-launch projection).
 //   * rows > 32   "wide": all rows x 128 columns per workgroup over a slice
-//     of K, both tiles staged through a double-buffered LDS ring with direct
-//     global->LDS loads; split-K partials are added by a second kernel.
+//     of K; 4 loader waves fill LDS rings (3 to 6 stages of the activation
+//     and weight tiles) with direct global->LDS loads while 8 waves multiply,
+//     one barrier per K step; split-K partials are added by a second kernel.
 //
 // Operand layout: for a 16x16x128 fp8 MFMA, lane l supplies row (l % 16) of
 // A (or column (l % 16) of B) and 32 bytes of K.  Lane l carries K bytes
